@@ -1,0 +1,177 @@
+/*
+ * tfb.h — C ABI of libtfb.so: the forward pass of a pre-norm, Llama-style
+ * transformer decoder block on AMD Instinct MI355X (gfx950), in full-sequence
+ * prefill and in single-token decode against a KV cache, plus a thin model
+ * (embedding, L blocks, final norm, untied LM head, greedy next token).
+ *
+ * The operation is the one described on the page "Transformer block"
+ * (tirogla.com/ml-training/transformer-architecture), section "How it works":
+ *   h = RMSNorm(x; g_attn); q = h Wq, k = h Wk, v = h Wv; RoPE on q and k;
+ *   per head softmax(q k^T / sqrt(dh) + causal mask) v with fp32 softmax,
+ *   heads concatenated, r = x + O Wo;
+ *   out = r + W2-projection of (SiLU(RMSNorm(r; g_mlp) W1) * RMSNorm(r; g_mlp) W3).
+ * Shapes and names follow that page's notation: B batch, T sequence, d width,
+ * H query heads, Hkv KV heads (GQA shares each KV head among H/Hkv consecutive
+ * query heads), dh = d/H head width, f MLP width, L layers, V vocabulary.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device pointers unless their name starts with h_ or the
+ *    comment says "host".  Arrays are row-major and densely packed.
+ *  - Storage is fp32 (TFB_F32) or bf16 (TFB_BF16) as the config says, for
+ *    x, out, weights, gains, embedding and the KV cache.  Accumulation, the
+ *    softmax and the norms are fp32; logits are always fp32.
+ *  - Weights are [in, out] so that y = x W (the page's Code section: "weight W
+ *    is [in, out], y = x.W").
+ *  - The caller owns all memory.  The library never allocates or frees device
+ *    memory, never synchronises and never reads device memory back, so every
+ *    call can be captured into a HIP graph.  Scratch space is the caller's
+ *    workspace of at least tfb_workspace_bytes() bytes.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream).  Host-visible arguments are validated before anything is
+ *    launched: on an error nothing is launched and no caller buffer changes.
+ *    A launch failure returns TFB_ERR_HIP.  Faults that happen on the device
+ *    surface at the caller's next synchronisation.
+ *  - Pointers must be 16-byte aligned.  For TFB_BF16, d, f must be multiples
+ *    of 64, dh must be 64 or 128 and the vocabulary a multiple of 64; for
+ *    TFB_F32, dh must be even and at most 256.  Always H*dh == d, H % Hkv == 0.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef TFB_H
+#define TFB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TFB_OK = 0,
+    TFB_ERR_NULL = -1,           /* a required pointer is NULL */
+    TFB_ERR_SHAPE = -2,          /* sizes violate the constraints above */
+    TFB_ERR_DTYPE = -3,          /* unknown storage type */
+    TFB_ERR_ALIGN = -4,          /* a pointer is not 16-byte aligned */
+    TFB_ERR_WORKSPACE = -5,      /* workspace NULL or smaller than required */
+    TFB_ERR_CACHE_OVERFLOW = -6, /* a position bound is not below the cache (or RoPE table) length */
+    TFB_ERR_HIP = -7,            /* a kernel launch failed */
+    TFB_ERR_UNSUPPORTED = -8     /* valid request this build does not implement */
+} tfb_status;
+
+typedef enum { TFB_F32 = 0, TFB_BF16 = 1 } tfb_dtype;
+
+/* Block hyper-parameters (the page's notation).  rope_base is the RoPE
+ * frequency base (10000 or 500000 in the workloads); rms_eps is the RMSNorm
+ * epsilon inside the square root. */
+typedef struct {
+    int32_t d, n_heads, n_kv_heads, head_dim, d_ff;
+    float rope_base, rms_eps;
+    int32_t dtype; /* tfb_dtype */
+} tfb_block_config;
+
+/* One block's weights, all in the config's storage type, [in, out] layout:
+ * g_attn, g_mlp [d]; wq [d, H*dh]; wk, wv [d, Hkv*dh]; wo [H*dh, d];
+ * w1 (gate, the SiLU branch) and w3 (up) [d, f]; w2 (down) [f, d].
+ * No biases (the page: "Parameter count (no biases, SwiGLU, untied head)"). */
+typedef struct {
+    const void *g_attn, *g_mlp;
+    const void *wq, *wk, *wv, *wo;
+    const void *w1, *w3, *w2;
+} tfb_block_weights;
+
+/* KV cache of one layer: k and v are each [batch, Hkv, t_max, dh] in the
+ * config's storage type and hold post-RoPE keys and values (the page's
+ * "KV cache" paragraph: "store post-RoPE k and v of every past token").
+ * Row t of sequence b is the token at absolute position t. */
+typedef struct {
+    void *k, *v;
+    int32_t batch, t_max;
+} tfb_kv_cache;
+
+/* The thin model: embedding [V, d], L blocks, final RMSNorm gain [d] and an
+ * untied LM head w_unembed [d, V].  `layers` is a HOST array of L weight sets
+ * whose members are device pointers. */
+typedef struct {
+    tfb_block_config blk;
+    int32_t n_layers, vocab;
+    const void *embed;
+    const tfb_block_weights *layers;
+    const void *g_final;
+    const void *w_unembed;
+} tfb_model;
+
+/* Bytes of workspace the calls below need for batch B, sequence T (T = 1 for
+ * decode) and, for tfb_model_forward, vocabulary `vocab` (0 = block calls
+ * only).  Returns 0 for an invalid config. */
+size_t tfb_workspace_bytes(const tfb_block_config *cfg, int32_t B, int32_t T, int32_t vocab);
+
+/* Fill the RoPE table: table[t][i] = (cos, sin) of t * base^(-2i/dh) for
+ * t < t_max, i < dh/2, angle computed in fp64 and stored as fp32
+ * ([t_max, dh/2, 2] fp32, device).  The page's Implementation notes:
+ * "Precompute RoPE cos/sin as a [T_max, dh/2] table"; pairs are interleaved
+ * (2i, 2i+1), "Meta's reference code" layout. */
+tfb_status tfb_rope_table_init(const tfb_block_config *cfg, int32_t t_max, float *table, void *stream);
+
+/* Full-sequence (or chunked) prefill of one block, the page's How it works
+ * steps 2-3.  x, out: [B, T, d]; out may alias x.  Token t of sequence b is
+ * at absolute position start_pos + t (0 for a fresh prompt; a positive value
+ * continues a sequence whose rows 0..start_pos-1 are already in the cache:
+ * chunked prefill).  When cache is non-NULL, rows start_pos..start_pos+T-1 of
+ * every sequence are written and attention reads rows 0..start_pos+t; cache
+ * batch must equal B and start_pos+T <= t_max.  With cache NULL, start_pos
+ * must be 0 and the keys and values stay in the workspace.
+ * rope_table: from tfb_rope_table_init with t_max_table >= start_pos + T. */
+tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                             int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T, int32_t start_pos,
+                             tfb_kv_cache *cache, void *ws, size_t ws_bytes, void *stream);
+
+/* One decode step of one block for B sequences (the page's KV cache
+ * paragraph: "a decode step computes q [B, H, 1, dh] and attends over the
+ * cache").  x, out: [B, 1, d], out may alias x.  pos: [B] int32 (device,
+ * read-only): the position of each new token, which is also the number of
+ * valid cache rows before the step.  Row pos[b] of the cache is written with
+ * the new post-RoPE k and v and attention reads rows 0..pos[b].  h_max_pos is
+ * a host upper bound of max(pos) and must be < t_max and < t_max_table;
+ * device code additionally never touches rows >= t_max.  Positions are not
+ * advanced (the caller, or tfb_model_forward, does that). */
+tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                            int32_t t_max_table, const void *x, void *out, int32_t B, tfb_kv_cache *cache,
+                            const int32_t *pos, int32_t h_max_pos, void *ws, size_t ws_bytes, void *stream);
+
+/* Append n_new rows per sequence: k_new, v_new [B, n_new, Hkv, dh] (already
+ * rotated) are written to cache rows start[b] .. start[b]+n_new-1.
+ * start: [B] int32 device; h_max_start is a host upper bound of max(start)
+ * with h_max_start + n_new <= t_max.  Rows outside that range are never
+ * touched. */
+tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const void *k_new, const void *v_new,
+                         const int32_t *start, int32_t n_new, int32_t h_max_start, void *stream);
+
+/* Model forward (the pidoku page "The Transformer", section 5 "The full
+ * model": embed, L blocks, final norm, LM head; the tirogla page, How it
+ * works steps 1 and 4).  ids: [B, T] int32 device, each in [0, V).
+ * caches: HOST array of n_layers caches.  lens: [B] int32 device, in/out:
+ *   T > 1  prefill of a fresh prompt: lens must be 0 on entry (every
+ *          sequence starts at position 0) and becomes T;
+ *   T == 1 decode: the new token sits at position lens[b]; lens[b] += 1.
+ * h_max_len: host upper bound of max(lens) on entry (0 for prefill); must
+ * satisfy h_max_len + T <= t_max.
+ * logits (nullable): fp32 [B, T, V], or [B, 1, V] when last_only != 0 (the
+ * last row of each sequence only).
+ * next_ids (nullable): [B] int32, argmax of each sequence's last row, lowest
+ * index on ties (greedy decoding). */
+tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, int32_t t_max_table, const int32_t *ids,
+                             int32_t B, int32_t T, tfb_kv_cache *caches, int32_t *lens, int32_t h_max_len,
+                             float *logits, int32_t last_only, int32_t *next_ids, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Static description of a status code. */
+const char *tfb_status_string(tfb_status s);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t tfb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TFB_H */

@@ -1,0 +1,172 @@
+"""Host-side checks of libtfb.so that need no GPU: it loads, exports every
+function include/tfb.h declares, sizes workspaces, and rejects invalid
+arguments before any launch (so these calls never reach the device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_decoder_block_rmsnorm_amd as tfb
+
+FAKE = 0x10000  # an aligned address; never dereferenced because validation fails first
+
+
+def _declared():
+    text = open(tfb.HEADER).read()
+    return sorted(set(re.findall(r"\b(tfb_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tfb.lib()
+    names = _declared()
+    assert set(names) == set(tfb.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", tfb.LIB_PATH], capture_output=True, text=True, check=True)
+    syms = set(re.findall(r"\bT (tfb_[a-z_]+)\b", out.stdout))
+    assert set(names) <= syms
+
+
+def test_status_strings_and_version():
+    lib = tfb.lib()
+    for code in tfb.STATUS:
+        assert lib.tfb_status_string(code)
+    assert lib.tfb_version() >= 100
+
+
+def _cfg(**kw):
+    base = dict(d=4096, n_heads=32, n_kv_heads=8, d_ff=14336, rope_base=5e5, rms_eps=1e-6, dtype="bf16")
+    base.update(kw)
+    return tfb.Config(**base)
+
+
+def test_workspace_bytes():
+    lib = tfb.lib()
+    c = _cfg()
+    n1 = tfb.workspace_bytes(c, 2, 128)
+    n2 = tfb.workspace_bytes(c, 2, 256)
+    assert 0 < n1 < n2
+    assert tfb.workspace_bytes(c, 4, 8, 32000) > tfb.workspace_bytes(c, 4, 8)
+    # each region holds at least the activations of the block
+    M = 2 * 256
+    assert n2 >= M * (4 * 4096 + 14336) * 2
+    for bad in (dict(n_heads=30), dict(d_ff=100), dict(dtype="f16"), dict(n_kv_heads=5)):
+        cc = _cfg(**bad) if bad.get("dtype") != "f16" else None
+        if cc is None:
+            c2 = _cfg().c()
+            c2.dtype = 7
+            assert lib.tfb_workspace_bytes(ctypes.byref(c2), 1, 1, 0) == 0
+        else:
+            assert tfb.workspace_bytes(cc, 1, 1) == 0
+    assert tfb.workspace_bytes(c, 0, 1) == 0 and tfb.workspace_bytes(c, 1, 0) == 0
+
+
+def _weights(addr=FAKE):
+    return tfb.BlockWeights(*[ctypes.c_void_p(addr + 256 * i) for i in range(9)])
+
+
+def _prefill(cfg, w=None, rope=FAKE, t_tab=64, x=FAKE, out=FAKE, B=1, T=8, start=0, cache=None, ws=FAKE,
+             ws_n=1 << 40):
+    lib = tfb.lib()
+    w = w or _weights()
+    return lib.tfb_block_prefill(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(rope), t_tab,
+                                 ctypes.c_void_p(x), ctypes.c_void_p(out), B, T, start,
+                                 None if cache is None else ctypes.byref(cache), ctypes.c_void_p(ws), ws_n, None)
+
+
+def test_prefill_rejects_invalid_arguments():
+    good = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()
+    bad_heads = _cfg(d=512, n_heads=4, n_kv_heads=3, d_ff=1024).c()
+    assert _prefill(bad_heads) == -2
+    bad_dh = _cfg(d=512, n_heads=16, n_kv_heads=2, d_ff=1024).c()  # dh = 32 not supported for bf16
+    assert _prefill(bad_dh) == -2
+    c = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()
+    c.dtype = 9
+    assert _prefill(c) == -3
+    w = _weights()
+    w.wo = None
+    assert _prefill(good, w=w) == -1
+    w = _weights()
+    w.w2 = ctypes.c_void_p(FAKE + 2)
+    assert _prefill(good, w=w) == -4
+    assert _prefill(good, x=0) == -1
+    assert _prefill(good, out=FAKE + 8) == -4
+    assert _prefill(good, B=0) == -2
+    assert _prefill(good, T=-1) == -2
+    assert _prefill(good, start=3) == -2            # start needs a cache
+    assert _prefill(good, T=65) == -6               # beyond the RoPE table
+    cache = tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 1, 16)
+    assert _prefill(good, cache=cache, T=17) == -6  # beyond the cache
+    assert _prefill(good, cache=cache, T=8, start=9) == -6
+    cache2 = tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 2, 16)
+    assert _prefill(good, cache=cache2) == -2       # cache batch != B
+    need = tfb.workspace_bytes(tfb.Config(512, 4, 2, 1024), 1, 8)
+    assert _prefill(good, ws_n=need - 1) == -5
+    assert _prefill(good, ws=0) == -5
+    f32 = _cfg(d=64, n_heads=4, n_kv_heads=2, d_ff=192, dtype="f32").c()
+    f32.head_dim = 15
+    assert _prefill(f32) == -2
+
+
+def test_decode_and_append_reject_invalid_arguments():
+    lib = tfb.lib()
+    cfg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()
+    w = _weights()
+    cache = tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 2, 32)
+
+    def dec(h_max=5, t_tab=64, pos=FAKE, B=2, ws_n=1 << 40):
+        return lib.tfb_block_decode(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(FAKE), t_tab,
+                                    ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), B, ctypes.byref(cache),
+                                    ctypes.c_void_p(pos), h_max, ctypes.c_void_p(FAKE), ws_n, None)
+    assert dec(h_max=32) == -6
+    assert dec(h_max=10, t_tab=10) == -6
+    assert dec(pos=0) == -1
+    assert dec(B=3) == -2
+    assert dec(h_max=-1) == -2
+    assert dec(ws_n=16) == -5
+
+    def app(n_new=4, h_max=2, start=FAKE):
+        return lib.tfb_kv_append(ctypes.byref(cfg), ctypes.byref(cache), ctypes.c_void_p(FAKE),
+                                 ctypes.c_void_p(FAKE), ctypes.c_void_p(start), n_new, h_max, None)
+    assert app(n_new=4, h_max=29) == -6
+    assert app(n_new=0) == -2
+    assert app(start=0) == -1
+
+
+def test_model_rejects_invalid_arguments():
+    lib = tfb.lib()
+    cfg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024)
+    layers = (tfb.BlockWeights * 2)(_weights(), _weights())
+    m = tfb.Model(cfg.c(), 2, 1000, ctypes.c_void_p(FAKE), layers, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE))
+    caches = (tfb.KVCache * 2)(*[tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 2, 32)] * 2)
+
+    def fwd(B=2, T=4, h_max=0, t_tab=64, model=m, ws_n=1 << 40):
+        return lib.tfb_model_forward(ctypes.byref(model), ctypes.c_void_p(FAKE), t_tab, ctypes.c_void_p(FAKE), B, T,
+                                     caches, ctypes.c_void_p(FAKE), h_max, None, 1, None, ctypes.c_void_p(FAKE), ws_n,
+                                     None)
+    assert fwd() == -2                      # vocab 1000 is not a multiple of 64 for bf16
+    m.vocab = 1024
+    assert fwd(h_max=3) == -2               # prefill must start at 0
+    assert fwd(T=1, h_max=32) == -6         # decode beyond the cache
+    assert fwd(T=40) == -6
+    assert fwd(B=3) == -2                   # caches hold 2 sequences
+    assert fwd(ws_n=100) == -5
+    m.n_layers = 0
+    assert fwd() == -2
+
+
+def test_product_path_has_no_cpu_fallback():
+    """The binding must refuse to run when the library is absent."""
+    import importlib
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import transformer_decoder_block_rmsnorm_amd as t\n"
+            "t.LIB_PATH = '/nonexistent/libtfb.so'\n"
+            "try:\n    t.lib()\nexcept RuntimeError as e:\n    print('raised', e)\n") % os.path.dirname(
+        os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert "raised" in res.stdout
+    src = open(os.path.join(os.path.dirname(tfb.__file__), "__init__.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src

@@ -1,0 +1,254 @@
+"""GPU parity of the decoder block against the CPU oracle (same seeded inputs).
+
+Tolerances: max |err| <= 1e-4 rms(oracle) for fp32 storage and 2e-2 rms for
+bf16 storage with fp32 accumulation; cache placement and untouched rows are
+checked bit for bit.
+"""
+import numpy as np
+import pytest
+
+from tests.conftest import gpu_available
+from tests.gpu_util import dev_weights, dev_x, new_cache, to_np, tol, widen_cache
+from tests.inputs import rel_err, small_cfg
+from synth.configs import C1
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import transformer_decoder_block_rmsnorm_amd as tfb  # noqa: E402
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def run_prefill_decode(cfg, B, T0, steps, t_max, gains="ones"):
+    """Prefill T0 tokens then `steps` decode steps on the GPU; returns outputs
+    [B, T0+steps, d], the caches, and the inputs."""
+    torch = _torch()
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg, gains=gains)
+    x32, x = dev_x(cfg, B, T0 + steps)
+    rope = tfb.rope_table_init(tc, t_max)
+    kc, vc = new_cache(cfg, B, t_max)
+    out = torch.empty((B, T0, cfg.d), dtype=x.dtype, device="cuda")
+    tfb.block_prefill(tc, w, rope, x[:, :T0].contiguous(), out, cache=(kc, vc))
+    outs = [to_np(out)]
+    for s in range(steps):
+        pos = torch.full((B,), T0 + s, dtype=torch.int32, device="cuda")
+        o1 = torch.empty((B, 1, cfg.d), dtype=x.dtype, device="cuda")
+        tfb.block_decode(tc, w, rope, x[:, T0 + s:T0 + s + 1].contiguous(), o1, (kc, vc), pos, T0 + s)
+        outs.append(to_np(o1))
+    torch.cuda.synchronize()
+    return np.concatenate(outs, axis=1), kc, vc, w32, x32
+
+
+def check_against_oracle(oracle, cfg, B, T0, steps, t_max, gains="ones"):
+    got, kc, vc, w32, x32 = run_prefill_decode(cfg, B, T0, steps, t_max, gains)
+    dh = cfg.d // cfg.n_heads
+    okc = np.full((B, cfg.n_kv_heads, t_max, dh), np.nan, np.float32)
+    ovc = okc.copy()
+    ref = oracle.block_forward(cfg, w32, x32, kc=okc, vc=ovc)
+    n = T0 + steps
+    assert rel_err(got, ref) <= tol(cfg), rel_err(got, ref)
+    gk, gv = widen_cache(kc), widen_cache(vc)
+    assert rel_err(gk[:, :, :n], okc[:, :, :n]) <= tol(cfg)
+    assert rel_err(gv[:, :, :n], ovc[:, :, :n]) <= tol(cfg)
+    # rows never written keep their NaN sentinel, bit for bit
+    assert np.isnan(gk[:, :, n:]).all() and np.isnan(gv[:, :, n:]).all()
+    assert np.isfinite(gk[:, :, :n]).all() and np.isfinite(got).all()
+    return got, ref
+
+
+def test_tiny_fp32_block_prefill_then_decode(oracle):
+    """The tiny fp32 workload: d=64, H=4, Hkv=2, f=192, T=16 then 4 decode steps."""
+    print("case: tiny fp32 prefill 16 + 4 decode", flush=True)
+    check_against_oracle(oracle, C1, 1, 16, 4, 32)
+
+
+def test_fp32_random_gains_and_batch(oracle):
+    cfg = small_cfg(d=128, H=4, Hkv=1, f=256, number=81)
+    print("case: fp32 d=128 MQA B=3 T=37+3 random gains", flush=True)
+    check_against_oracle(oracle, cfg, 3, 37, 3, 48, gains="random")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(d=512, H=4, Hkv=2, f=1024, B=2, T0=300, steps=2),   # GQA, ragged rows (300 = 2*128 + 44)
+    dict(d=256, H=2, Hkv=2, f=768, B=1, T0=129, steps=2),    # MHA, one row past a tile
+    dict(d=512, H=8, Hkv=1, f=512, B=2, T0=70, steps=3),     # MQA, dh = 64
+    dict(d=1024, H=8, Hkv=2, f=2048, B=1, T0=256, steps=1),  # full tiles
+])
+def test_bf16_block_prefill_then_decode(oracle, shape):
+    cfg = small_cfg(d=shape["d"], H=shape["H"], Hkv=shape["Hkv"], f=shape["f"], dtype="bf16", number=82)
+    print("case: bf16", shape, flush=True)
+    check_against_oracle(oracle, cfg, shape["B"], shape["T0"], shape["steps"], shape["T0"] + shape["steps"] + 5)
+
+
+def test_bf16_random_gains_rope_base_500k(oracle):
+    cfg = small_cfg(d=512, H=4, Hkv=1, f=1536, dtype="bf16", base=500000.0, number=83)
+    print("case: bf16 random gains base 5e5", flush=True)
+    check_against_oracle(oracle, cfg, 2, 200, 2, 210, gains="random")
+
+
+def test_prefill_without_cache_matches(oracle):
+    torch = _torch()
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=84)
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg)
+    x32, x = dev_x(cfg, 2, 150)
+    rope = tfb.rope_table_init(tc, 150)
+    out = torch.empty_like(x)
+    tfb.block_prefill(tc, w, rope, x, out)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(out), oracle.block_forward(cfg, w32, x32)) <= 2e-2
+
+
+def test_out_may_alias_x(oracle):
+    torch = _torch()
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=85)
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg)
+    x32, x = dev_x(cfg, 1, 64)
+    rope = tfb.rope_table_init(tc, 64)
+    tfb.block_prefill(tc, w, rope, x, x)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(x), oracle.block_forward(cfg, w32, x32)) <= 2e-2
+
+
+def test_causal_mask_placement_bitwise():
+    """Rows <= i must not change, bit for bit, when rows > i change."""
+    torch = _torch()
+    for cfg in (C1, small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=86)):
+        tc = tfb.Config.of(cfg)
+        _, w = dev_weights(cfg)
+        _, x = dev_x(cfg, 2, 200 if cfg.dtype == "bf16" else 16)
+        T = x.shape[1]
+        rope = tfb.rope_table_init(tc, T)
+        o1 = torch.empty_like(x)
+        tfb.block_prefill(tc, w, rope, x, o1)
+        for i in (0, T // 3, T - 2):
+            x2 = x.clone()
+            x2[:, i + 1:] = 37.0
+            o2 = torch.empty_like(x)
+            tfb.block_prefill(tc, w, rope, x2, o2)
+            torch.cuda.synchronize()
+            assert torch.equal(o1[:, :i + 1], o2[:, :i + 1]), (cfg.dtype, i)
+            assert not torch.equal(o1[:, i + 1:], o2[:, i + 1:])
+
+
+def test_deterministic_repeat_bitwise():
+    torch = _torch()
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=87)
+    tc = tfb.Config.of(cfg)
+    _, w = dev_weights(cfg)
+    _, x = dev_x(cfg, 2, 333)
+    rope = tfb.rope_table_init(tc, 333)
+    outs = []
+    for _ in range(2):
+        kc, vc = new_cache(cfg, 2, 333, 0.0)
+        o = torch.empty_like(x)
+        tfb.block_prefill(tc, w, rope, x, o, cache=(kc, vc))
+        outs.append((o, kc, vc))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    torch = _torch()
+    for dtype in ("f32", "bf16"):
+        d, f = (64, 192) if dtype == "f32" else (512, 1024)
+        cfg = small_cfg(d=d, H=4, Hkv=2, f=f, dtype=dtype, number=88)
+        cfg_m = small_cfg(d=d, H=4, Hkv=4, f=f, dtype=dtype, number=88)
+        _, w = dev_weights(cfg)
+        _, x = dev_x(cfg, 1, 40)
+        dh = d // 4
+        cols = torch.cat([torch.arange(g * dh, (g + 1) * dh) for g in range(2) for _ in range(2)]).cuda()
+        wm = dict(w, wk=w["wk"][:, cols].contiguous(), wv=w["wv"][:, cols].contiguous())
+        outs = []
+        for c, ww in ((cfg, w), (cfg_m, wm)):
+            tc = tfb.Config.of(c)
+            rope = tfb.rope_table_init(tc, 40)
+            o = torch.empty_like(x)
+            tfb.block_prefill(tc, ww, rope, x, o)
+            outs.append(o)
+        torch.cuda.synchronize()
+        err = (outs[0].float() - outs[1].float()).abs().max().item()
+        assert err <= 1e-6 * outs[1].float().abs().max().item() + (0 if dtype == "f32" else 1e-2), (dtype, err)
+
+
+def test_decode_over_nan_tail_and_ragged_positions(oracle):
+    """Sequences at different positions decode together; cache rows beyond
+    pos[b] hold NaN and must never influence the result."""
+    torch = _torch()
+    for cfg in (C1, small_cfg(d=512, H=4, Hkv=1, f=1024, dtype="bf16", number=89)):
+        tc = tfb.Config.of(cfg)
+        B, t_max = 3, 80
+        w32, w = dev_weights(cfg)
+        x32, x = dev_x(cfg, B, t_max)
+        lens = [5, 33, 71]
+        rope = tfb.rope_table_init(tc, t_max)
+        kc, vc = new_cache(cfg, B, t_max)
+        dh = cfg.d // cfg.n_heads
+        okc = np.full((B, cfg.n_kv_heads, t_max, dh), np.nan, np.float32)
+        ovc = okc.copy()
+        for b in range(B):  # prefill each sequence to its own length
+            kb, vb = new_cache(cfg, 1, t_max)
+            ob = torch.empty((1, lens[b], cfg.d), dtype=x.dtype, device="cuda")
+            tfb.block_prefill(tc, w, rope, x[b:b + 1, :lens[b]].contiguous(), ob, cache=(kb, vb))
+            kc[b].copy_(kb[0])
+            vc[b].copy_(vb[0])
+            k1, v1 = okc[b:b + 1].copy(), ovc[b:b + 1].copy()
+            oracle.block_forward(cfg, w32, x32[b:b + 1, :lens[b]], kc=k1, vc=v1)
+            okc[b], ovc[b] = k1[0], v1[0]
+        pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        xd = torch.stack([x[b, lens[b]] for b in range(B)])[:, None].contiguous()
+        o = torch.empty_like(xd)
+        tfb.block_decode(tc, w, rope, xd, o, (kc, vc), pos, max(lens))
+        torch.cuda.synchronize()
+        xd32 = np.stack([x32[b, lens[b]] for b in range(B)])[:, None]
+        ref = oracle.block_forward(cfg, w32, xd32, start=np.array(lens, np.int32), kc=okc, vc=ovc)
+        got = to_np(o)
+        assert np.isfinite(got).all()
+        assert rel_err(got, ref) <= tol(cfg)
+        gk = widen_cache(kc)
+        for b in range(B):
+            assert np.isnan(gk[b, :, lens[b] + 1:]).all()
+            assert rel_err(gk[b, :, lens[b]], okc[b, :, lens[b]]) <= tol(cfg)
+
+
+def test_kv_append_bit_exact(oracle):
+    torch = _torch()
+    for cfg in (C1, small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=90)):
+        tc = tfb.Config.of(cfg)
+        B, t_max, n = 3, 40, 5
+        dh = cfg.d // cfg.n_heads
+        import synth
+        kf, kb = synth.normal(cfg.seed, 11, (B, n, cfg.n_kv_heads, dh), 1.0, cfg.dtype == "bf16")
+        vf, vb = synth.normal(cfg.seed, 12, (B, n, cfg.n_kv_heads, dh), 1.0, cfg.dtype == "bf16")
+        from tests.gpu_util import to_dev
+        k_new, v_new = to_dev(kf, kb), to_dev(vf, vb)
+        start = np.array([0, 17, 35], np.int32)
+        kc, vc = new_cache(cfg, B, t_max)
+        tfb.kv_append(tc, (kc, vc), k_new, v_new, torch.from_numpy(start).cuda(), int(start.max()))
+        torch.cuda.synchronize()
+        okc = np.full((B, cfg.n_kv_heads, t_max, dh), np.nan, np.float32)
+        ovc = okc.copy()
+        oracle.kv_append(okc, ovc, kf, vf, start)
+        g = widen_cache(kc)
+        same = (g == okc) | (np.isnan(g) & np.isnan(okc))
+        assert same.all()
+        g = widen_cache(vc)
+        assert ((g == ovc) | (np.isnan(g) & np.isnan(ovc))).all()
+
+
+def test_rope_table_matches_oracle(oracle):
+    torch = _torch()
+    for base, dh in ((10000.0, 16), (500000.0, 128), (10000.0, 64)):
+        cfg = small_cfg(d=dh * 4, H=4, Hkv=2, f=64, base=base)
+        tab = tfb.rope_table_init(tfb.Config.of(cfg), 4096)
+        torch.cuda.synchronize()
+        c, s = oracle.rope_table(4096, dh, base)
+        g = tab.cpu().numpy()
+        # fp64 angle rounded to fp32 on both sides: at most one ulp apart
+        assert np.max(np.abs(g[..., 0] - c)) <= 6e-8 and np.max(np.abs(g[..., 1] - s)) <= 6e-8

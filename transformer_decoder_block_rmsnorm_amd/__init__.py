@@ -1,0 +1,210 @@
+"""Python binding of libtfb.so (include/tfb.h): argument marshalling only.
+
+Every step of the decoder block runs in the library's HIP kernels; torch is
+used here for device memory and the current stream.  Importing works without
+a GPU, but calling into the library requires the built ``libtfb.so`` and
+raises ``RuntimeError`` when it is missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtfb.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "tfb.h")
+
+TFB_F32, TFB_BF16 = 0, 1
+STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTYPE", -4: "TFB_ERR_ALIGN",
+          -5: "TFB_ERR_WORKSPACE", -6: "TFB_ERR_CACHE_OVERFLOW", -7: "TFB_ERR_HIP", -8: "TFB_ERR_UNSUPPORTED"}
+EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
+           "tfb_model_forward", "tfb_status_string", "tfb_version")
+
+_VP = ctypes.c_void_p
+
+
+class BlockConfig(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rope_base", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in ("g_attn", "g_mlp", "wq", "wk", "wv", "wo", "w1", "w3", "w2")]
+
+
+class KVCache(ctypes.Structure):
+    _fields_ = [("k", _VP), ("v", _VP), ("batch", ctypes.c_int32), ("t_max", ctypes.c_int32)]
+
+
+class Model(ctypes.Structure):
+    _fields_ = [("blk", BlockConfig), ("n_layers", ctypes.c_int32), ("vocab", ctypes.c_int32), ("embed", _VP),
+                ("layers", ctypes.POINTER(BlockWeights)), ("g_final", _VP), ("w_unembed", _VP)]
+
+
+WEIGHT_NAMES = ("g_attn", "g_mlp", "wq", "wk", "wv", "wo", "w1", "w3", "w2")
+
+
+class TfbError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, STATUS.get(code, "?"), code))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtfb.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtfb.so is not built (run __graft_entry__.build()); there is no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tfb_workspace_bytes.argtypes = [ctypes.POINTER(BlockConfig), ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32]
+        L.tfb_workspace_bytes.restype = ctypes.c_size_t
+        L.tfb_rope_table_init.argtypes = [ctypes.POINTER(BlockConfig), ctypes.c_int32, _VP, _VP]
+        L.tfb_block_prefill.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
+                                        ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(KVCache), _VP, ctypes.c_size_t, _VP]
+        L.tfb_block_decode.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
+                                       ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.POINTER(KVCache), _VP,
+                                       ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
+        L.tfb_kv_append.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(KVCache), _VP, _VP, _VP,
+                                    ctypes.c_int32, ctypes.c_int32, _VP]
+        L.tfb_model_forward.argtypes = [ctypes.POINTER(Model), _VP, ctypes.c_int32, _VP, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.POINTER(KVCache), _VP, ctypes.c_int32, _VP,
+                                        ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
+        for f in ("tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
+                  "tfb_model_forward"):
+            getattr(L, f).restype = ctypes.c_int
+        L.tfb_status_string.argtypes = [ctypes.c_int]
+        L.tfb_status_string.restype = ctypes.c_char_p
+        L.tfb_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# torch-side helpers (device memory and streams only)
+# ---------------------------------------------------------------------------
+def _ptr(t):
+    return None if t is None else _VP(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return _VP(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise TfbError(rc, where)
+
+
+@dataclass
+class Config:
+    d: int
+    n_heads: int
+    n_kv_heads: int
+    d_ff: int
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-6
+    dtype: str = "bf16"
+
+    @property
+    def head_dim(self) -> int:
+        return self.d // self.n_heads
+
+    def c(self) -> BlockConfig:
+        return BlockConfig(self.d, self.n_heads, self.n_kv_heads, self.head_dim, self.d_ff, self.rope_base,
+                           self.rms_eps, TFB_BF16 if self.dtype == "bf16" else TFB_F32)
+
+    @staticmethod
+    def of(obj) -> "Config":
+        return Config(obj.d, obj.n_heads, obj.n_kv_heads, obj.d_ff, obj.rope_base, obj.rms_eps, obj.dtype)
+
+
+def weights_struct(w: dict) -> BlockWeights:
+    return BlockWeights(*[_VP(w[n].data_ptr()) for n in WEIGHT_NAMES])
+
+
+def cache_struct(k, v) -> KVCache:
+    return KVCache(_VP(k.data_ptr()), _VP(v.data_ptr()), k.shape[0], k.shape[2])
+
+
+def workspace_bytes(cfg: Config, B: int, T: int, vocab: int = 0) -> int:
+    return int(lib().tfb_workspace_bytes(ctypes.byref(cfg.c()), B, T, vocab))
+
+
+def workspace(cfg: Config, B: int, T: int, vocab: int = 0, device="cuda"):
+    import torch
+    n = workspace_bytes(cfg, B, T, vocab)
+    if n == 0:
+        raise TfbError(-2, "tfb_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def rope_table_init(cfg: Config, t_max: int, table=None):
+    import torch
+    if table is None:
+        table = torch.empty((t_max, cfg.head_dim // 2, 2), dtype=torch.float32, device="cuda")
+    _check(lib().tfb_rope_table_init(ctypes.byref(cfg.c()), t_max, _ptr(table), _stream()), "tfb_rope_table_init")
+    return table
+
+
+def block_prefill(cfg: Config, w: dict, rope, x, out, start_pos: int = 0, cache=None, ws=None):
+    """x, out: [B, T, d] device tensors; cache: (k, v) tensors [B, Hkv, t_max, dh] or None."""
+    B, T, _ = x.shape
+    if ws is None:
+        ws = workspace(cfg, B, T)
+    kv = None if cache is None else ctypes.byref(cache_struct(*cache))
+    ws_n = ws.numel() * ws.element_size()
+    _check(lib().tfb_block_prefill(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
+                                   rope.shape[0], _ptr(x), _ptr(out), B, T, start_pos, kv, _ptr(ws), ws_n,
+                                   _stream()), "tfb_block_prefill")
+    return out
+
+
+def block_decode(cfg: Config, w: dict, rope, x, out, cache, pos, h_max_pos: int, ws=None):
+    """x, out: [B, 1, d]; cache: (k, v); pos: int32 [B] device tensor."""
+    B = x.shape[0]
+    if ws is None:
+        ws = workspace(cfg, B, 1)
+    ws_n = ws.numel() * ws.element_size()
+    _check(lib().tfb_block_decode(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
+                                  rope.shape[0], _ptr(x), _ptr(out), B, ctypes.byref(cache_struct(*cache)),
+                                  _ptr(pos), h_max_pos, _ptr(ws), ws_n, _stream()), "tfb_block_decode")
+    return out
+
+
+def kv_append(cfg: Config, cache, k_new, v_new, start, h_max_start: int):
+    n_new = k_new.shape[1]
+    _check(lib().tfb_kv_append(ctypes.byref(cfg.c()), ctypes.byref(cache_struct(*cache)), _ptr(k_new),
+                               _ptr(v_new), _ptr(start), n_new, h_max_start, _stream()), "tfb_kv_append")
+
+
+class ModelHandle:
+    """Keeps the ctypes structs of a model alive across calls."""
+
+    def __init__(self, cfg: Config, layers: list, embed, g_final, w_unembed):
+        self.cfg = cfg
+        self.vocab = embed.shape[0]
+        self._layers = (BlockWeights * len(layers))(*[weights_struct(w) for w in layers])
+        self._tensors = (layers, embed, g_final, w_unembed)
+        self.m = Model(cfg.c(), len(layers), self.vocab, _VP(embed.data_ptr()), self._layers,
+                       _VP(g_final.data_ptr()), _VP(w_unembed.data_ptr()))
+
+
+def model_forward(h: ModelHandle, rope, ids, caches: list, lens, h_max_len: int, logits=None, last_only=False,
+                  next_ids=None, ws=None):
+    B, T = ids.shape
+    if ws is None:
+        ws = workspace(h.cfg, B, T, h.vocab)
+    kv = (KVCache * len(caches))(*[cache_struct(k, v) for k, v in caches])
+    ws_n = ws.numel() * ws.element_size()
+    _check(lib().tfb_model_forward(ctypes.byref(h.m), _ptr(rope), rope.shape[0], _ptr(ids), B, T, kv, _ptr(lens),
+                                   h_max_len, _ptr(logits), 1 if last_only else 0, _ptr(next_ids), _ptr(ws), ws_n,
+                                   _stream()), "tfb_model_forward")

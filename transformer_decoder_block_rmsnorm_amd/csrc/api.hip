@@ -1,0 +1,339 @@
+// C ABI of libtfb (include/tfb.h): argument validation, workspace layout and
+// the launch sequence of each call.  Page short names: [TIR] tirogla
+// "Transformer block", [PID] pidoku "The Transformer".
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+using namespace tfb;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t esize(int dtype) { return dtype == TFB_BF16 ? 2 : 4; }
+
+// Decode attention splits each (sequence, KV head) key range into at most
+// this many chunks; their partial results live in the workspace.
+constexpr int kMaxSplits = 64;
+
+struct WsLayout {
+    size_t h, q, att, r, act, kv_k, kv_v, part, x0, x1, last, logits, total;
+};
+
+WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
+    WsLayout L{};
+    const size_t es = esize(c.dtype), M = (size_t)B * T;
+    const size_t qd = (size_t)c.n_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+    L.h = take(M * c.d * es);
+    L.q = take(M * qd * es);
+    L.att = take(M * qd * es);
+    L.r = take(M * c.d * sizeof(float));  // block-internal residual, fp32
+    L.act = take(M * (size_t)c.d_ff * es);
+    L.kv_k = take(M * kvd * es);  // keys and values when no cache is given
+    L.kv_v = take(M * kvd * es);
+    L.part = take(attention_decode_scratch_bytes(B, c.n_heads, c.head_dim, kMaxSplits));
+    if (vocab > 0) {
+        L.x0 = take(M * c.d * es);
+        L.x1 = take(M * c.d * es);
+        L.last = take((size_t)B * c.d * es);
+        L.logits = take((size_t)B * vocab * sizeof(float));
+    }
+    L.total = off;
+    return L;
+}
+
+tfb_status check_cfg(const tfb_block_config *c) {
+    if (!c) return TFB_ERR_NULL;
+    if (c->dtype != TFB_F32 && c->dtype != TFB_BF16) return TFB_ERR_DTYPE;
+    if (c->d <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->d_ff <= 0) return TFB_ERR_SHAPE;
+    if (c->n_heads % c->n_kv_heads != 0 || c->n_heads * c->head_dim != c->d || (c->head_dim & 1)) return TFB_ERR_SHAPE;
+    if (!(c->rope_base > 0.0f) || !(c->rms_eps >= 0.0f) || !isfinite(c->rope_base) || !isfinite(c->rms_eps))
+        return TFB_ERR_SHAPE;
+    if (c->dtype == TFB_BF16) {
+        if (c->d % 64 || c->d_ff % 64 || (c->head_dim != 64 && c->head_dim != 128)) return TFB_ERR_SHAPE;
+    } else {
+        if (c->head_dim > 256 || c->d % 4 || c->d_ff % 4) return TFB_ERR_SHAPE;
+    }
+    return TFB_OK;
+}
+
+tfb_status check_weights(const tfb_block_weights *w) {
+    if (!w) return TFB_ERR_NULL;
+    const void *p[] = {w->g_attn, w->g_mlp, w->wq, w->wk, w->wv, w->wo, w->w1, w->w3, w->w2};
+    for (const void *x : p)
+        if (!x) return TFB_ERR_NULL;
+    for (const void *x : p)
+        if (!aligned(x)) return TFB_ERR_ALIGN;
+    return TFB_OK;
+}
+
+tfb_status check_cache(const tfb_kv_cache *kv, int B) {
+    if (!kv->k || !kv->v) return TFB_ERR_NULL;
+    if (!aligned(kv->k) || !aligned(kv->v)) return TFB_ERR_ALIGN;
+    if (kv->batch != B || kv->t_max <= 0) return TFB_ERR_SHAPE;
+    return TFB_OK;
+}
+
+#define TRY_HIP(expr)                                  \
+    do {                                               \
+        if ((expr) != hipSuccess) return TFB_ERR_HIP;  \
+    } while (0)
+
+// The launches of one block for M = B*T rows ([TIR] How it works steps 2-3):
+//   RMSNorm_1 -> fused QKV GEMM (+RoPE, q to workspace, k and v to the cache)
+//   -> causal GQA attention -> Wo GEMM + residual -> RMSNorm_2
+//   -> fused gate-up GEMM (+SiLU * up) -> W2 GEMM + residual.
+tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
+                     const void *x,
+                     void *out, int B, int T, int start, const int32_t *pos, void *kc, void *vc, int t_max,
+                     uint8_t *ws, const WsLayout &L, hipStream_t s) {
+    const int M = B * T, d = c.d, H = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, f = c.d_ff;
+    const int qd = H * dh, kvd = Hkv * dh;
+    void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
+
+    TRY_HIP(rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s));
+
+    GemmCall g{};
+    g.dtype = c.dtype;
+    g.epi = EPI_QKV;
+    g.A = h;
+    g.lda = d;
+    g.M = M;
+    g.K = d;
+    g.w[0] = w.wq; g.w[1] = w.wk; g.w[2] = w.wv;
+    g.w_cols[0] = qd; g.w_cols[1] = kvd; g.w_cols[2] = kvd;
+    g.ep.M = M;
+    g.ep.N = qd + 2 * kvd;
+    g.ep.q = q;
+    g.ep.kc = kc;
+    g.ep.vc = vc;
+    g.ep.rope = rope;
+    g.ep.rope_rows = rope_rows;
+    g.ep.pos = pos;
+    g.ep.T = T; g.ep.H = H; g.ep.Hkv = Hkv; g.ep.dh = dh; g.ep.t_max = t_max; g.ep.start = start;
+    TRY_HIP(gemm_launch(g, s));
+
+    AttnCall a{};
+    a.dtype = c.dtype;
+    a.q = q; a.kc = kc; a.vc = vc; a.o = att; a.pos = pos;
+    a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.dh = dh; a.t_max = t_max; a.start = start;
+    a.scale = 1.0f / sqrtf((float)dh);
+    a.partials = ws + L.part;
+    a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
+    a.max_keys = pos ? t_max : start + T;
+    TRY_HIP(pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s));
+
+    GemmCall o{};
+    o.dtype = c.dtype;
+    o.epi = EPI_RESID;
+    o.A = att; o.lda = qd; o.M = M; o.K = qd;
+    o.w[0] = w.wo; o.w_cols[0] = d;
+    o.ep.M = M; o.ep.N = d; o.ep.out = r; o.ep.ldo = d; o.ep.res = x; o.ep.ldr = d; o.ep.out_f32 = 1;
+    TRY_HIP(gemm_launch(o, s));
+
+    TRY_HIP(rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true));
+
+    GemmCall gu{};
+    gu.dtype = c.dtype;
+    gu.epi = EPI_SWIGLU;
+    gu.A = h; gu.lda = d; gu.M = M; gu.K = d;
+    gu.w[0] = w.w1; gu.w[1] = w.w3; gu.w_cols[0] = f; gu.w_cols[1] = f;
+    gu.ep.M = M; gu.ep.N = f; gu.ep.out = act; gu.ep.ldo = f;
+    TRY_HIP(gemm_launch(gu, s));
+
+    GemmCall dn{};
+    dn.dtype = c.dtype;
+    dn.epi = EPI_RESID;
+    dn.A = act; dn.lda = f; dn.M = M; dn.K = f;
+    dn.w[0] = w.w2; dn.w_cols[0] = d;
+    dn.ep.M = M; dn.ep.N = d; dn.ep.out = out; dn.ep.ldo = d; dn.ep.res = r; dn.ep.ldr = d; dn.ep.res_f32 = 1;
+    TRY_HIP(gemm_launch(dn, s));
+    return TFB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t tfb_version(void) { return 100; }
+
+const char *tfb_status_string(tfb_status st) {
+    switch (st) {
+        case TFB_OK: return "ok";
+        case TFB_ERR_NULL: return "a required pointer is NULL";
+        case TFB_ERR_SHAPE: return "invalid sizes";
+        case TFB_ERR_DTYPE: return "unknown storage type";
+        case TFB_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case TFB_ERR_WORKSPACE: return "workspace missing or too small";
+        case TFB_ERR_CACHE_OVERFLOW: return "position bound not below cache or RoPE table length";
+        case TFB_ERR_HIP: return "HIP launch failed";
+        case TFB_ERR_UNSUPPORTED: return "unsupported request";
+    }
+    return "unknown status";
+}
+
+size_t tfb_workspace_bytes(const tfb_block_config *cfg, int32_t B, int32_t T, int32_t vocab) {
+    if (check_cfg(cfg) != TFB_OK || B <= 0 || T <= 0 || vocab < 0) return 0;
+    return ws_layout(*cfg, B, T, vocab).total;
+}
+
+tfb_status tfb_rope_table_init(const tfb_block_config *cfg, int32_t t_max, float *table, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if (!table) return TFB_ERR_NULL;
+    if (!aligned(table)) return TFB_ERR_ALIGN;
+    if (t_max <= 0) return TFB_ERR_SHAPE;
+    TRY_HIP(rope_table_launch(t_max, cfg->head_dim, (double)cfg->rope_base, table, (hipStream_t)stream));
+    return TFB_OK;
+}
+
+tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                             int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T, int32_t start_pos,
+                             tfb_kv_cache *cache, void *ws, size_t ws_bytes, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if ((st = check_weights(w)) != TFB_OK) return st;
+    if (!rope_table || !x || !out) return TFB_ERR_NULL;
+    if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
+    if (B <= 0 || T <= 0 || start_pos < 0) return TFB_ERR_SHAPE;
+    if (cache) {
+        if ((st = check_cache(cache, B)) != TFB_OK) return st;
+        if ((int64_t)start_pos + T > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
+    } else if (start_pos != 0) {
+        return TFB_ERR_SHAPE;
+    }
+    if ((int64_t)start_pos + T > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    const WsLayout L = ws_layout(*cfg, B, T, 0);
+    if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
+    if (!aligned(ws)) return TFB_ERR_ALIGN;
+    uint8_t *wsb = (uint8_t *)ws;
+    void *kc = cache ? cache->k : (void *)(wsb + L.kv_k);
+    void *vc = cache ? cache->v : (void *)(wsb + L.kv_v);
+    const int t_max = cache ? cache->t_max : T;
+    return run_block(*cfg, *w, rope_table, t_max_table, x, out, B, T, start_pos, nullptr, kc, vc, t_max, wsb, L,
+                     (hipStream_t)stream);
+}
+
+tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                            int32_t t_max_table, const void *x, void *out, int32_t B, tfb_kv_cache *cache,
+                            const int32_t *pos, int32_t h_max_pos, void *ws, size_t ws_bytes, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if ((st = check_weights(w)) != TFB_OK) return st;
+    if (!rope_table || !x || !out || !cache || !pos) return TFB_ERR_NULL;
+    if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
+    if (B <= 0 || h_max_pos < 0) return TFB_ERR_SHAPE;
+    if ((st = check_cache(cache, B)) != TFB_OK) return st;
+    if (h_max_pos >= cache->t_max || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    const WsLayout L = ws_layout(*cfg, B, 1, 0);
+    if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
+    if (!aligned(ws)) return TFB_ERR_ALIGN;
+    return run_block(*cfg, *w, rope_table, t_max_table, x, out, B, 1, 0, pos, cache->k, cache->v, cache->t_max, (uint8_t *)ws,
+                     L, (hipStream_t)stream);
+}
+
+tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const void *k_new, const void *v_new,
+                         const int32_t *start, int32_t n_new, int32_t h_max_start, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if (!cache || !k_new || !v_new || !start) return TFB_ERR_NULL;
+    if (!aligned(k_new) || !aligned(v_new)) return TFB_ERR_ALIGN;
+    if (cache->batch <= 0) return TFB_ERR_SHAPE;
+    if ((st = check_cache(cache, cache->batch)) != TFB_OK) return st;
+    if (n_new <= 0 || h_max_start < 0) return TFB_ERR_SHAPE;
+    if ((int64_t)h_max_start + n_new > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
+    TRY_HIP(kv_append_launch(cfg->dtype, cache->k, cache->v, k_new, v_new, start, cache->batch, n_new,
+                             cfg->n_kv_heads, cfg->head_dim, cache->t_max, (hipStream_t)stream));
+    return TFB_OK;
+}
+
+tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, int32_t t_max_table, const int32_t *ids,
+                             int32_t B, int32_t T, tfb_kv_cache *caches, int32_t *lens, int32_t h_max_len,
+                             float *logits, int32_t last_only, int32_t *next_ids, void *ws, size_t ws_bytes,
+                             void *stream) {
+    if (!model) return TFB_ERR_NULL;
+    const tfb_block_config &c = model->blk;
+    tfb_status st = check_cfg(&c);
+    if (st != TFB_OK) return st;
+    if (!model->embed || !model->layers || !model->g_final || !model->w_unembed || !rope_table || !ids ||
+        !caches || !lens)
+        return TFB_ERR_NULL;
+    if (!aligned(model->embed) || !aligned(model->g_final) || !aligned(model->w_unembed) || !aligned(rope_table) ||
+        (logits && !aligned(logits)))
+        return TFB_ERR_ALIGN;
+    if (model->n_layers <= 0 || model->vocab <= 0 || B <= 0 || T <= 0 || h_max_len < 0) return TFB_ERR_SHAPE;
+    if (c.dtype == TFB_BF16 && model->vocab % 64) return TFB_ERR_SHAPE;
+    if (c.dtype == TFB_F32 && model->vocab % 4) return TFB_ERR_SHAPE;
+    if (T > 1 && h_max_len != 0) return TFB_ERR_SHAPE;  // prefill starts every sequence at 0
+    for (int l = 0; l < model->n_layers; ++l) {
+        if ((st = check_weights(&model->layers[l])) != TFB_OK) return st;
+        if ((st = check_cache(&caches[l], B)) != TFB_OK) return st;
+        if ((int64_t)h_max_len + T > caches[l].t_max) return TFB_ERR_CACHE_OVERFLOW;
+    }
+    if ((int64_t)h_max_len + T > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    const WsLayout L = ws_layout(c, B, T, model->vocab);
+    if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
+    if (!aligned(ws)) return TFB_ERR_ALIGN;
+
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *wsb = (uint8_t *)ws;
+    const int M = B * T, d = c.d, V = model->vocab;
+    // Embed ([PID] Tiny example, forward), then the L blocks.
+    TRY_HIP(embed_launch(c.dtype, ids, model->embed, wsb + L.x0, M, d, V, s));
+    void *cur = wsb + L.x0, *nxt = wsb + L.x1;
+    for (int l = 0; l < model->n_layers; ++l) {
+        if (T > 1)
+            st = run_block(c, model->layers[l], rope_table, t_max_table, cur, nxt, B, T, 0, nullptr, caches[l].k, caches[l].v,
+                           caches[l].t_max, wsb, L, s);
+        else
+            st = run_block(c, model->layers[l], rope_table, t_max_table, cur, nxt, B, 1, 0, lens, caches[l].k, caches[l].v,
+                           caches[l].t_max, wsb, L, s);
+        if (st != TFB_OK) return st;
+        void *tmp = cur; cur = nxt; nxt = tmp;
+    }
+    // Final norm and untied LM head ([TIR] How it works step 4), fp32 logits.
+    const void *fin = cur;
+    int rows = M;
+    if (last_only && T > 1) {
+        TRY_HIP(gather_last_launch(c.dtype, cur, wsb + L.last, B, T, d, s));
+        fin = wsb + L.last;
+        rows = B;
+    }
+    if (logits || next_ids) {
+        void *hn = wsb + L.h;
+        TRY_HIP(rmsnorm_launch(c.dtype, fin, d, model->g_final, hn, d, rows, d, c.rms_eps, s));
+        float *lg = logits;
+        if (!lg) {
+            if (rows != B) {  // next ids only: the head runs on the last rows
+                TRY_HIP(gather_last_launch(c.dtype, cur, wsb + L.last, B, T, d, s));
+                TRY_HIP(rmsnorm_launch(c.dtype, wsb + L.last, d, model->g_final, hn, d, B, d, c.rms_eps, s));
+                rows = B;
+            }
+            lg = (float *)(wsb + L.logits);
+        }
+        GemmCall hd{};
+        hd.dtype = c.dtype;
+        hd.epi = EPI_F32;
+        hd.A = hn; hd.lda = d; hd.M = rows; hd.K = d;
+        hd.w[0] = model->w_unembed; hd.w_cols[0] = V;
+        hd.ep.M = rows; hd.ep.N = V; hd.ep.out = lg; hd.ep.ldo = V;
+        TRY_HIP(gemm_launch(hd, s));
+        if (next_ids) {
+            // Greedy next token from each sequence's last row ([PID] Under the hood, step 6).
+            if (rows == B) {
+                TRY_HIP(argmax_launch(lg, V, B, V, next_ids, s));
+            } else {
+                TRY_HIP(argmax_launch(lg + (int64_t)(T - 1) * V, (int64_t)T * V, B, V, next_ids, s));
+            }
+        }
+    }
+    TRY_HIP(add_scalar_launch(lens, B, T, s));
+    return TFB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Fused GEMM epilogues of the decoder block (shared by the bf16 MFMA GEMM and
+// the fp32 GEMM).  Page short names: [TIR] tirogla "Transformer block".
+#pragma once
+#include "common.h"
+
+namespace tfb {
+
+enum EpiKind {
+    EPI_QKV = 0,    // RoPE on q and k, q -> [B,H,T,dh] workspace, k and v -> KV cache rows
+    EPI_RESID = 1,  // out = residual + acc            ([TIR] How it works: "Add to the residual")
+    EPI_SWIGLU = 2, // act = SiLU(gate) * up           ([TIR] How it works step 3)
+    EPI_F32 = 3,    // fp32 store (logits)
+};
+
+struct EpiParams {
+    int M, N;                // logical output rows / columns
+    void *out;               // RESID, SWIGLU: storage type T; F32: float
+    int64_t ldo;
+    const void *res;         // RESID residual input (may alias out)
+    int64_t ldr;
+    int res_f32, out_f32;    // RESID: residual / output held in fp32 instead of the storage type
+    // QKV
+    void *q, *kc, *vc;       // q [B,H,T,dh]; caches [B,Hkv,t_max,dh]
+    const float *rope;       // [t_max_table][dh/2][2] (cos, sin)
+    const int32_t *pos;      // decode: [B] positions (T == 1); NULL: start + t
+    int T, H, Hkv, dh, t_max, start;
+    int rope_rows;           // rows of the RoPE table (device positions are clamped to it)
+};
+
+// Position of output row m (token t of sequence b).
+__device__ __forceinline__ void qkv_row(const EpiParams &p, int m, int &b, int &t, int &ps) {
+    b = m / p.T;
+    t = m - b * p.T;
+    ps = p.pos ? p.pos[b] : p.start + t;
+}
+
+// Store the pair of output columns (c, c+1), c even, of row m.
+template <int KIND, typename T>
+__device__ __forceinline__ void epi_store_pair(const EpiParams &p, int m, int c, float v0, float v1) {
+    if (m >= p.M || c >= p.N) return;
+    if constexpr (KIND == EPI_RESID) {
+        // The block-internal residual r stays fp32 so that only the block
+        // output is rounded to the storage type.
+        int64_t ir = (int64_t)m * p.ldr + c, io = (int64_t)m * p.ldo + c;
+        float r0, r1;
+        if (p.res_f32) {
+            float2 rr = *(const float2 *)((const float *)p.res + ir);
+            r0 = rr.x; r1 = rr.y;
+        } else {
+            r0 = Elem<T>::load((const T *)p.res, ir);
+            r1 = Elem<T>::load((const T *)p.res, ir + 1);
+        }
+        if (p.out_f32) {
+            *(float2 *)((float *)p.out + io) = make_float2(r0 + v0, r1 + v1);
+        } else {
+            Elem<T>::store((T *)p.out, io, r0 + v0);
+            Elem<T>::store((T *)p.out, io + 1, r1 + v1);
+        }
+    } else if constexpr (KIND == EPI_F32) {
+        float *out = (float *)p.out;
+        int64_t io = (int64_t)m * p.ldo + c;
+        out[io] = v0;
+        out[io + 1] = v1;
+    } else if constexpr (KIND == EPI_QKV) {
+        int b, t, ps;
+        qkv_row(p, m, b, t, ps);
+        const int qd = p.H * p.dh, kvd = p.Hkv * p.dh;
+        // RoPE on q and k only, pairs (2i, 2i+1) rotated by ps * theta_i
+        // ([TIR] Code, rope; never on v: [TIR] Pitfalls).
+        if (c < qd + kvd) {
+            int e = c % p.dh;
+            const int pr = min(max(ps, 0), p.rope_rows - 1);
+            float2 cs = ((const float2 *)p.rope)[(int64_t)pr * (p.dh >> 1) + (e >> 1)];
+            float a = v0, bb = v1;
+            v0 = a * cs.x - bb * cs.y;
+            v1 = a * cs.y + bb * cs.x;
+        }
+        if (c < qd) {
+            int h = c / p.dh, e = c - h * p.dh;
+            T *q = (T *)p.q;
+            int64_t iq = (((int64_t)b * p.H + h) * p.T + t) * p.dh + e;
+            Elem<T>::store(q, iq, v0);
+            Elem<T>::store(q, iq + 1, v1);
+        } else {
+            if (ps < 0 || ps >= p.t_max) return;  // never write outside the cache
+            int cc = c - qd;
+            T *dst = (T *)p.kc;
+            if (cc >= kvd) { cc -= kvd; dst = (T *)p.vc; }
+            int g = cc / p.dh, e = cc - g * p.dh;
+            int64_t ic = (((int64_t)b * p.Hkv + g) * p.t_max + ps) * p.dh + e;
+            Elem<T>::store(dst, ic, v0);
+            Elem<T>::store(dst, ic + 1, v1);
+        }
+    }
+}
+
+// SwiGLU epilogue: one logical column c of act.
+template <typename T>
+__device__ __forceinline__ void epi_store_swiglu(const EpiParams &p, int m, int c, float gate, float up) {
+    if (m >= p.M || c >= p.N) return;
+    Elem<T>::store((T *)p.out, (int64_t)m * p.ldo + c, silu_f(gate) * up);
+}
+
+}  // namespace tfb

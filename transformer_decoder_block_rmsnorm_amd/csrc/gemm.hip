@@ -1,0 +1,334 @@
+// Weight GEMMs of the decoder block: y = x W with W stored [in, out]
+// (tirogla "Transformer block", Code: "weight W is [in, out], y = x.W").
+//
+// bf16: MFMA 32x32x16 tiles, fp32 accumulation.  Both operands are staged in
+// LDS as [rows][64 k] with k contiguous and the eight 16-byte chunks of a row
+// XOR-swizzled by (row & 7), so fragment reads of 32 consecutive rows are
+// bank-conflict free.  The weight tile arrives N-contiguous; each thread
+// loads an 8x8 block and transposes it in registers (byte permutes) before
+// writing it k-contiguous.  One barrier per 64-wide k step, LDS double
+// buffered, next tile's global loads in flight during the current MFMAs.
+//
+// Fused epilogues (epilogue.h): RoPE + KV-cache scatter for the fused QKV
+// projection, residual add for Wo and W2, SiLU(gate) * up for the fused
+// gate-up projection (W1 and W3 tiles interleaved in 32-column blocks), fp32
+// store for the LM head.
+//
+// fp32: a plain LDS-tiled VALU GEMM with the same epilogues (the fp32 storage
+// path serves small shapes; it is launch-latency bound).
+#include "epilogue.h"
+#include "kernels.h"
+
+namespace tfb {
+
+// Where the columns of the B operand come from.
+//  SRC_ONE:    a single [K, N] matrix.
+//  SRC_CONCAT: up to three matrices side by side (Wq | Wk | Wv); a column
+//              tile never straddles two of them.
+//  SRC_DUAL:   W1 and W3 interleaved in 32-column blocks (gate-up); the
+//              logical output has N/2 columns.
+enum SrcKind { SRC_ONE = 0, SRC_CONCAT = 1, SRC_DUAL = 2 };
+
+struct GemmArgs {
+    const void *A;
+    int64_t lda;
+    int M, K;
+    int N;              // B columns in this launch (DUAL: 2 * logical width)
+    const void *w[3];
+    int w_cols[3];      // columns (= leading dimension) of each matrix
+    int tiles_m, tiles_n, group_m;
+};
+
+constexpr int BK = 64;
+
+// Logical tile (tm, tn) of workgroup `bid`.  Workgroups are dealt to the 8
+// XCDs round robin; the remap gives each XCD a contiguous run of logical
+// tiles, and the run is ordered in groups of `group_m` row panels so that the
+// tiles resident on one XCD share A and B panels in that XCD's L2.
+__device__ __forceinline__ void tile_of(const GemmArgs &g, int bid, int &tm, int &tn) {
+    const int total = g.tiles_m * g.tiles_n;
+    int L = bid;
+    if ((total & 7) == 0) L = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int per_group = g.group_m * g.tiles_n;
+    const int grp = L / per_group;
+    const int first_m = grp * g.group_m;
+    const int gm = min(g.tiles_m - first_m, g.group_m);
+    const int r = L - grp * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g, EpiParams ep) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+    constexpr int TM = WTM / 32, TN = WTN / 32;  // MFMA tiles per wave
+    constexpr int A_CH = BM * BK / 8 / NT;       // 16-byte A chunks per thread
+    constexpr int B_BLK = (BK / 8) * (BN / 8);   // 8x8 weight blocks per tile
+    constexpr int B_PER = (B_BLK + NT - 1) / NT;
+    static_assert(BM * BK / 8 % NT == 0, "A tile must split evenly");
+    static_assert(SRC != SRC_DUAL || TN % 2 == 0, "dual source needs gate/up tile pairs");
+
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * BK];
+    // buffer b: A tile at lds + b*(BM+BN)*BK, B tile right after it
+    auto As = [&](int b) { return lds + b * (BM + BN) * BK; };
+    auto Bs = [&](int b) { return lds + b * (BM + BN) * BK + BM * BK; };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(g, blockIdx.x, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- A source rows (clamped: rows >= M compute garbage that is never stored)
+    const bf16_t *A = (const bf16_t *)g.A;
+    const bf16_t *a_ptr[A_CH];
+    int a_lds[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        int id = tid + i * NT;
+        int row = id >> 3, ch = id & 7;
+        int gr = min(m0 + row, g.M - 1);
+        a_ptr[i] = A + (int64_t)gr * g.lda + ch * 8;
+        a_lds[i] = row * BK + ((ch ^ (row & 7)) * 8);
+    }
+    // ---- B source columns: each thread owns B_PER 8(k) x 8(n) blocks
+    const bf16_t *b_ptr[B_PER];
+    int b_ld[B_PER], b_nb[B_PER], b_kb[B_PER];
+    bool b_ok[B_PER];
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+        int id = tid + i * NT;
+        b_ok[i] = id < B_BLK;
+        int nb = id % (BN / 8), kb = id / (BN / 8);
+        b_nb[i] = nb;
+        b_kb[i] = kb;
+        int c = n0 + nb * 8;  // column within this launch's B
+        const bf16_t *base;
+        int ld, col;
+        if constexpr (SRC == SRC_ONE) {
+            base = (const bf16_t *)g.w[0]; ld = g.w_cols[0]; col = c;
+        } else if constexpr (SRC == SRC_CONCAT) {
+            int s = 0, cc = c;
+            if (cc >= g.w_cols[0]) { cc -= g.w_cols[0]; s = 1; if (cc >= g.w_cols[1]) { cc -= g.w_cols[1]; s = 2; } }
+            base = (const bf16_t *)g.w[s]; ld = g.w_cols[s]; col = cc;
+        } else {
+            int s = (c >> 5) & 1;
+            base = (const bf16_t *)g.w[s]; ld = g.w_cols[s]; col = 32 * (c >> 6) + (c & 31);
+        }
+        if (col >= ld) b_ok[i] = false;  // ragged last tile: zero fill
+        b_ld[i] = ld;
+        b_ptr[i] = base + (int64_t)(kb * 8) * ld + (b_ok[i] ? col : 0);
+    }
+
+    u32x4 ra[A_CH], rb[B_PER][8];
+    auto load_global = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) ra[i] = *(const u32x4 *)(a_ptr[i] + kt * BK);
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            if (b_ok[i]) {
+                const bf16_t *p = b_ptr[i] + (int64_t)kt * BK * b_ld[i];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) rb[i][r] = *(const u32x4 *)(p + (int64_t)r * b_ld[i]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) rb[i][r] = u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_lds = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) *(u32x4 *)(As(buf) + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) {
+            if (tid + i * NT < B_BLK) {
+                u32x4 t[8];
+                transpose8x8_bf16(rb[i], t);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    int n = b_nb[i] * 8 + j;
+                    *(u32x4 *)(Bs(buf) + n * BK + ((b_kb[i] ^ (n & 7)) * 8)) = t[j];
+                }
+            }
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int KT = g.K / BK;
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    const int lr = lane & 31, lh = lane >> 5;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load_global(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int ch = ks * 2 + lh;
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                int row = wm * WTM + i * 32 + lr;
+                af[i] = as_bf16x8(*(const u32x4 *)(As(buf) + row * BK + ((ch ^ (row & 7)) * 8)));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                int n = wn * WTN + j * 32 + lr;
+                bfr[j] = as_bf16x8(*(const u32x4 *)(Bs(buf) + n * BK + ((ch ^ (n & 7)) * 8)));
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+        if (kt + 1 < KT) store_lds(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue straight from the accumulator layout
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (EPI == EPI_SWIGLU) {
+                if (j & 1) continue;
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                if constexpr (EPI == EPI_SWIGLU) {
+                    const int col = tn * (BN / 2) + wn * (WTN / 2) + 16 * j + lr;
+                    epi_store_swiglu<bf16_t>(ep, row, col, acc[i][j][v], acc[i][j + 1][v]);
+                } else {
+                    const int col = n0 + wn * WTN + j * 32 + lr;
+                    float mine = acc[i][j][v];
+                    float other = swap_lane_pair(mine);
+                    if ((lr & 1) == 0) epi_store_pair<EPI, bf16_t>(ep, row, col, mine, other);
+                }
+            }
+        }
+    }
+}
+
+// fp32 storage: 64x64 output tile per 256 threads, 16-wide k steps in LDS,
+// each thread computes a 4 (rows) x 4 (columns) patch.  SWIGLU computes the
+// gate and up dot products of each logical column side by side.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams ep) {
+    constexpr int TMt = 64, TNt = 64, TK = 16;
+    __shared__ float As[TK][TMt + 4];
+    __shared__ float Bs[2][TK][TNt + 4];
+    const int tid = threadIdx.x;
+    const int m0 = blockIdx.y * TMt, n0 = blockIdx.x * TNt;  // logical columns
+    const int tr = tid / 16, tc = tid % 16;
+    const float *A = (const float *)g.A;
+    constexpr int NSRC = (EPI == EPI_SWIGLU) ? 2 : 1;
+    float acc[NSRC][4][4] = {};
+    for (int k0 = 0; k0 < g.K; k0 += TK) {
+        for (int e = tid; e < TMt * TK; e += 256) {
+            int r = e / TK, kk = e % TK;
+            int gr = m0 + r, gk = k0 + kk;
+            As[kk][r] = (gr < g.M && gk < g.K) ? A[(int64_t)gr * g.lda + gk] : 0.0f;
+        }
+        for (int s = 0; s < NSRC; ++s)
+            for (int e = tid; e < TK * TNt; e += 256) {
+                int kk = e / TNt, c = e % TNt;
+                int gc = n0 + c, gk = k0 + kk;
+                float v = 0.0f;
+                if (gk < g.K) {
+                    if (EPI == EPI_SWIGLU) {
+                        if (gc < g.w_cols[s]) v = ((const float *)g.w[s])[(int64_t)gk * g.w_cols[s] + gc];
+                    } else {
+                        int src = 0, cc = gc;
+                        while (src < 2 && g.w[src + 1] && cc >= g.w_cols[src]) { cc -= g.w_cols[src]; ++src; }
+                        if (cc < g.w_cols[src]) v = ((const float *)g.w[src])[(int64_t)gk * g.w_cols[src] + cc];
+                    }
+                }
+                Bs[s][kk][c] = v;
+            }
+        __syncthreads();
+        for (int kk = 0; kk < TK; ++kk) {
+            float a[4];
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][tr * 4 + i];
+            for (int s = 0; s < NSRC; ++s)
+                for (int j = 0; j < 4; ++j) {
+                    float b = Bs[s][kk][tc * 4 + j];
+                    for (int i = 0; i < 4; ++i) acc[s][i][j] += a[i] * b;
+                }
+        }
+        __syncthreads();
+    }
+    for (int i = 0; i < 4; ++i) {
+        int row = m0 + tr * 4 + i;
+        for (int j = 0; j < 4; j += 2) {
+            int col = n0 + tc * 4 + j;
+            if constexpr (EPI == EPI_SWIGLU) {
+                epi_store_swiglu<float>(ep, row, col, acc[0][i][j], acc[1][i][j]);
+                epi_store_swiglu<float>(ep, row, col + 1, acc[0][i][j + 1], acc[1][i][j + 1]);
+            } else {
+                epi_store_pair<EPI, float>(ep, row, col, acc[0][i][j], acc[0][i][j + 1]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+static hipError_t launch_bf16(GemmArgs g, const EpiParams &ep, hipStream_t s) {
+    g.tiles_m = (g.M + BM - 1) / BM;
+    g.tiles_n = (g.N + BN - 1) / BN;
+    g.group_m = 8;
+    const int blocks = g.tiles_m * g.tiles_n;
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s, g,
+                       ep);
+    return hipGetLastError();
+}
+
+hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
+    GemmArgs g{};
+    g.A = c.A;
+    g.lda = c.lda;
+    g.M = c.M;
+    g.K = c.K;
+    for (int i = 0; i < 3; ++i) { g.w[i] = c.w[i]; g.w_cols[i] = c.w_cols[i]; }
+    const EpiParams &ep = c.ep;
+    if (c.dtype == TFB_F32) {
+        g.N = c.ep.N;
+        dim3 grid((c.ep.N + 63) / 64, (c.M + 63) / 64);
+        switch (c.epi) {
+            case EPI_QKV: hipLaunchKernelGGL(gemm_f32_kernel<EPI_QKV>, grid, dim3(256), 0, s, g, ep); break;
+            case EPI_RESID: hipLaunchKernelGGL(gemm_f32_kernel<EPI_RESID>, grid, dim3(256), 0, s, g, ep); break;
+            case EPI_SWIGLU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, g, ep); break;
+            case EPI_F32: hipLaunchKernelGGL(gemm_f32_kernel<EPI_F32>, grid, dim3(256), 0, s, g, ep); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    switch (c.epi) {
+        case EPI_QKV:
+            g.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2];
+            return launch_bf16<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, s);
+        case EPI_RESID:
+            g.N = c.w_cols[0];
+            return launch_bf16<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, s);
+        case EPI_SWIGLU:
+            g.N = 2 * c.w_cols[0];
+            return launch_bf16<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, s);
+        case EPI_F32:
+            g.N = c.w_cols[0];
+            return launch_bf16<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tfb

@@ -1,0 +1,59 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tfb.h"
+#include "epilogue.h"
+
+namespace tfb {
+
+struct GemmCall {
+    int dtype;             // TFB_F32 / TFB_BF16
+    int epi;               // EpiKind
+    const void *A;         // [M, K] activations
+    int64_t lda;
+    int M, K;
+    const void *w[3];      // QKV: wq, wk, wv; SWIGLU: w1, w3; else w[0]
+    int w_cols[3];
+    EpiParams ep;
+};
+hipError_t gemm_launch(const GemmCall &c, hipStream_t s);
+
+// y[m] = x[m] * rsqrt(mean(x[m]^2) + eps) * g, rows of width d.
+// x_f32: the input rows are fp32 (the block-internal residual) whatever the storage type.
+hipError_t rmsnorm_launch(int dtype, const void *x, int64_t ldx, const void *g, void *y, int64_t ldy, int rows, int d,
+                          float eps, hipStream_t s, bool x_f32 = false);
+
+// RoPE table [t_max][dh/2] of (cos, sin) from an fp64 angle.
+hipError_t rope_table_launch(int t_max, int dh, double base, float *table, hipStream_t s);
+
+// Attention over the KV cache: query row t of sequence b sits at position
+// pos[b] (decode, T == 1) or start + t (prefill) and reads cache rows 0..pos.
+struct AttnCall {
+    int dtype;
+    const void *q;        // [B, H, T, dh]
+    const void *kc, *vc;  // [B, Hkv, t_max, dh]
+    void *o;              // [B, T, H*dh]
+    const int32_t *pos;   // decode positions or NULL
+    int B, T, H, Hkv, dh, t_max, start;
+    float scale;
+    void *partials;       // split-KV scratch (decode), may be NULL
+    size_t partial_bytes;
+    int max_keys;         // host bound on keys per query (for work sizing)
+};
+hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
+hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
+size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_keys);
+
+hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
+                            int B, int n_new, int Hkv, int dh, int t_max, hipStream_t s);
+hipError_t embed_launch(int dtype, const int32_t *ids, const void *table, void *x, int64_t rows, int d, int vocab,
+                        hipStream_t s);
+// Copy row (T-1) of each sequence of x [B, T, d] into y [B, d].
+hipError_t gather_last_launch(int dtype, const void *x, void *y, int B, int T, int d, hipStream_t s);
+hipError_t argmax_launch(const float *logits, int64_t ld, int rows, int n, int32_t *out, hipStream_t s);
+hipError_t add_scalar_launch(int32_t *v, int n, int32_t add, hipStream_t s);
+hipError_t fill_i32_launch(int32_t *v, int n, int32_t value, hipStream_t s);
+
+}  // namespace tfb

@@ -1,0 +1,223 @@
+// Small kernels of the decoder-block path: RMSNorm, RoPE table, KV append,
+// embedding gather, last-row gather, greedy argmax, position updates.
+// Page short names: [TIR] tirogla "Transformer block", [PID] pidoku "The
+// Transformer".
+#include "kernels.h"
+
+namespace tfb {
+
+// RMSNorm ([TIR] Code, rms_norm; [PID] Tiny example, rmsnorm): one wave per
+// row, fp32 sum of squares reduced across the wave, y = x * r * g.
+template <typename Tin, typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const Tin *x, int64_t ldx, const T *g, T *y, int64_t ldy,
+                                                      int rows, int d, float eps) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const Tin *xr = x + (int64_t)row * ldx;
+    T *yr = y + (int64_t)row * ldy;
+    float ss = 0.0f;
+    if constexpr (sizeof(Tin) == 2) {
+        for (int c = lane * 8; c < d; c += 512) {
+            u32x4 v = *(const u32x4 *)(xr + c);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float a = bf16_lo(v[w]), b = bf16_hi(v[w]);
+                ss += a * a + b * b;
+            }
+        }
+    } else {
+        for (int c = lane; c < d; c += 64) ss += xr[c] * xr[c];
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+    if constexpr (sizeof(T) == 2 && sizeof(Tin) == 2) {
+        for (int c = lane * 8; c < d; c += 512) {
+            u32x4 v = *(const u32x4 *)(xr + c), gv = *(const u32x4 *)(g + c), o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                o[w] = pack_bf16x2(bf16_lo(v[w]) * r * bf16_lo(gv[w]), bf16_hi(v[w]) * r * bf16_hi(gv[w]));
+            *(u32x4 *)(yr + c) = o;
+        }
+    } else if constexpr (sizeof(T) == 2) {
+        for (int c = lane * 8; c < d; c += 512) {
+            f32x4 v0 = *(const f32x4 *)(xr + c), v1 = *(const f32x4 *)(xr + c + 4);
+            u32x4 gv = *(const u32x4 *)(g + c), o;
+            o[0] = pack_bf16x2(v0[0] * r * bf16_lo(gv[0]), v0[1] * r * bf16_hi(gv[0]));
+            o[1] = pack_bf16x2(v0[2] * r * bf16_lo(gv[1]), v0[3] * r * bf16_hi(gv[1]));
+            o[2] = pack_bf16x2(v1[0] * r * bf16_lo(gv[2]), v1[1] * r * bf16_hi(gv[2]));
+            o[3] = pack_bf16x2(v1[2] * r * bf16_lo(gv[3]), v1[3] * r * bf16_hi(gv[3]));
+            *(u32x4 *)(yr + c) = o;
+        }
+    } else {
+        for (int c = lane; c < d; c += 64) yr[c] = xr[c] * r * g[c];
+    }
+}
+
+hipError_t rmsnorm_launch(int dtype, const void *x, int64_t ldx, const void *g, void *y, int64_t ldy, int rows, int d,
+                          float eps, hipStream_t s, bool x_f32) {
+    dim3 grid((rows + 3) / 4);
+    if (dtype == TFB_BF16 && !x_f32)
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, (const bf16_t *)x, ldx,
+                           (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps);
+    else if (dtype == TFB_BF16)
+        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t>), grid, dim3(256), 0, s, (const float *)x, ldx,
+                           (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<float, float>), grid, dim3(256), 0, s, (const float *)x, ldx,
+                           (const float *)g, (float *)y, ldy, rows, d, eps);
+    return hipGetLastError();
+}
+
+// RoPE table ([TIR] Implementation notes: a [T_max, dh/2] cos/sin table;
+// frequencies base^(-2i/dh) over interleaved pairs).  fp64 angle, fp32 values.
+__global__ void rope_table_kernel(int t_max, int dh, double base, float *table) {
+    const int half = dh / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)t_max * half) return;
+    const int t = (int)(idx / half), i = (int)(idx % half);
+    const double theta = pow(base, -2.0 * (double)i / (double)dh);
+    const double a = (double)t * theta;
+    table[2 * idx] = (float)cos(a);
+    table[2 * idx + 1] = (float)sin(a);
+}
+
+hipError_t rope_table_launch(int t_max, int dh, double base, float *table, hipStream_t s) {
+    const int64_t n = (int64_t)t_max * (dh / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, t_max, dh, base, table);
+    return hipGetLastError();
+}
+
+// KV append ([TIR] How it works, KV cache): [B, n, Hkv, dh] -> cache rows
+// start[b] + t.  One thread per 4 elements; rows outside [0, t_max) are skipped.
+template <typename T>
+__global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const int32_t *start, int B, int n_new,
+                                 int Hkv, int dh, int t_max) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per_row = dh / 4;
+    const int64_t total = (int64_t)B * n_new * Hkv * per_row;
+    if (idx >= total) return;
+    const int e4 = (int)(idx % per_row);
+    int64_t r = idx / per_row;
+    const int g = (int)(r % Hkv);
+    r /= Hkv;
+    const int t = (int)(r % n_new);
+    const int b = (int)(r / n_new);
+    const int p = start[b] + t;
+    if (p < 0 || p >= t_max) return;
+    const int64_t src = (((int64_t)b * n_new + t) * Hkv + g) * dh + e4 * 4;
+    const int64_t dst = (((int64_t)b * Hkv + g) * t_max + p) * dh + e4 * 4;
+    if constexpr (sizeof(T) == 2) {
+        *(u32x2 *)(kc + dst) = *(const u32x2 *)(kn + src);
+        *(u32x2 *)(vc + dst) = *(const u32x2 *)(vn + src);
+    } else {
+        *(u32x4 *)(kc + dst) = *(const u32x4 *)(kn + src);
+        *(u32x4 *)(vc + dst) = *(const u32x4 *)(vn + src);
+    }
+}
+
+hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
+                            int B, int n_new, int Hkv, int dh, int t_max, hipStream_t s) {
+    const int64_t total = (int64_t)B * n_new * Hkv * (dh / 4);
+    dim3 grid((unsigned)((total + 255) / 256));
+    if (dtype == TFB_BF16)
+        hipLaunchKernelGGL(kv_append_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)kc, (bf16_t *)vc,
+                           (const bf16_t *)k_new, (const bf16_t *)v_new, start, B, n_new, Hkv, dh, t_max);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, (float *)kc, (float *)vc,
+                           (const float *)k_new, (const float *)v_new, start, B, n_new, Hkv, dh, t_max);
+    return hipGetLastError();
+}
+
+// Embedding gather ([PID] Tiny example, forward: x[s] = Embed[id]); 16-byte
+// chunks; an id outside [0, vocab) yields a zero row.
+__global__ void embed_kernel(const int32_t *ids, const uint8_t *table, uint8_t *x, int64_t rows, int row_bytes,
+                             int vocab) {
+    const int chunks = row_bytes / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * chunks) return;
+    const int64_t r = idx / chunks;
+    const int c = (int)(idx % chunks);
+    const int id = ids[r];
+    u32x4 v = {0, 0, 0, 0};
+    if (id >= 0 && id < vocab) v = *(const u32x4 *)(table + (int64_t)id * row_bytes + c * 16);
+    *(u32x4 *)(x + r * row_bytes + c * 16) = v;
+}
+
+hipError_t embed_launch(int dtype, const int32_t *ids, const void *table, void *x, int64_t rows, int d, int vocab,
+                        hipStream_t s) {
+    const int row_bytes = d * (dtype == TFB_BF16 ? 2 : 4);
+    const int64_t n = rows * (row_bytes / 16);
+    hipLaunchKernelGGL(embed_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids,
+                       (const uint8_t *)table, (uint8_t *)x, rows, row_bytes, vocab);
+    return hipGetLastError();
+}
+
+__global__ void gather_last_kernel(const uint8_t *x, uint8_t *y, int B, int T, int row_bytes) {
+    const int chunks = row_bytes / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)B * chunks) return;
+    const int b = (int)(idx / chunks), c = (int)(idx % chunks);
+    *(u32x4 *)(y + (int64_t)b * row_bytes + c * 16) =
+        *(const u32x4 *)(x + ((int64_t)b * T + T - 1) * row_bytes + c * 16);
+}
+
+hipError_t gather_last_launch(int dtype, const void *x, void *y, int B, int T, int d, hipStream_t s) {
+    const int row_bytes = d * (dtype == TFB_BF16 ? 2 : 4);
+    const int64_t n = (int64_t)B * (row_bytes / 16);
+    hipLaunchKernelGGL(gather_last_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const uint8_t *)x, (uint8_t *)y, B, T, row_bytes);
+    return hipGetLastError();
+}
+
+// Greedy next token: argmax of each row, lowest index among equal maxima.
+__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int64_t ld, int n, int32_t *out) {
+    const float *row = logits + (int64_t)blockIdx.x * ld;
+    float best = -INFINITY;
+    int idx = 0x7FFFFFFF;
+    for (int j = threadIdx.x; j < n; j += 256) {
+        float v = row[j];
+        if (v > best || (v == best && j < idx)) { best = v; idx = j; }
+    }
+    __shared__ float sv[256];
+    __shared__ int si[256];
+    sv[threadIdx.x] = best;
+    si[threadIdx.x] = idx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            float ov = sv[threadIdx.x + w];
+            int oi = si[threadIdx.x + w];
+            if (ov > sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
+                sv[threadIdx.x] = ov;
+                si[threadIdx.x] = oi;
+            }
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[blockIdx.x] = si[0] == 0x7FFFFFFF ? 0 : si[0];
+}
+
+hipError_t argmax_launch(const float *logits, int64_t ld, int rows, int n, int32_t *out, hipStream_t s) {
+    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, logits, ld, n, out);
+    return hipGetLastError();
+}
+
+__global__ void add_scalar_kernel(int32_t *v, int n, int32_t add) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) v[i] += add;
+}
+__global__ void fill_i32_kernel(int32_t *v, int n, int32_t value) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) v[i] = value;
+}
+
+hipError_t add_scalar_launch(int32_t *v, int n, int32_t add, hipStream_t s) {
+    hipLaunchKernelGGL(add_scalar_kernel, dim3((n + 255) / 256), dim3(256), 0, s, v, n, add);
+    return hipGetLastError();
+}
+hipError_t fill_i32_launch(int32_t *v, int n, int32_t value, hipStream_t s) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, v, n, value);
+    return hipGetLastError();
+}
+
+}  // namespace tfb
