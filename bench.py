@@ -1,0 +1,214 @@
+"""Benchmark of the decoder-block hot path on one MI355X.
+
+Headline (`value`): block prefill TFLOP/s on the Llama-2-7B-shaped block
+(d=4096, H=Hkv=32, dh=128, f=11008, B=1, T=2048, bf16 storage, fp32
+accumulation, KV cache written), algorithmic causal FLOP count.  In the same
+run: the GQA decode step (d=4096, H=32, Hkv=8, f=14336, B=64 sequences with
+cache lengths uniform in [1024, 4096]) in tokens/s, with the decode-attention
+kernel's achieved HBM bandwidth.  Inputs are synthetic and seeded, resident
+in HBM before timing starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block prefill TFLOP/s + decode tok/s, as % of MFMA / HBM roofline on 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBPS = 8000.0      # HBM3E
+
+
+def _dev_tensor(f32, bits):
+    import numpy as np
+    import torch
+    if bits is not None:
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(f32).cuda()
+
+
+def block_inputs(cfg, B, T):
+    from tests.inputs import activations, block_weights
+    w32, bits = block_weights(cfg)
+    w = {k: _dev_tensor(v, None if bits is None else bits[k]) for k, v in w32.items()}
+    x32, xb = activations(cfg, B, T)
+    return w32, w, x32, _dev_tensor(x32, xb)
+
+
+def time_prefill(cfg, steps, warmup):
+    import torch
+    import transformer_decoder_block_rmsnorm_amd as tfb
+    from oracle import formulas as FM
+    tc = tfb.Config.of(cfg)
+    B, T = cfg.B, cfg.T
+    w32, w, x32, x = block_inputs(cfg, B, T)
+    rope = tfb.rope_table_init(tc, cfg.t_max)
+    kc = torch.zeros((B, cfg.n_kv_heads, cfg.t_max, tc.head_dim), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = torch.empty_like(x)
+    ws = tfb.workspace(tc, B, T)
+
+    def step():
+        tfb.block_prefill(tc, w, rope, x, out, cache=(kc, vc), ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = FM.block_prefill_flops_causal(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    # per-kernel durations, measured with HIP events on the launch stream
+    tfb.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    stages = tfb.profile_read()
+    tfb.profile_enable(False)
+    return dict(ms=ms, flops=flops, stages=stages, w32=w32, x32=x32)
+
+
+def time_decode(cfg, steps, warmup):
+    import numpy as np
+    import torch
+    import synth
+    import transformer_decoder_block_rmsnorm_amd as tfb
+    from oracle import formulas as FM
+    from synth.configs import tensor_id
+    tc = tfb.Config.of(cfg)
+    B, dh = cfg.B, cfg.d // cfg.n_heads
+    lens = synth.integers(cfg.seed, tensor_id("lens"), (B,), cfg.lens_lo, cfg.lens_hi)
+    _, w, _, x = block_inputs(cfg, B, 1)
+    shape = (B, cfg.n_kv_heads, cfg.t_max, dh)
+    caches = []
+    for name in ("kc", "vc"):
+        _, bits = synth.normal(cfg.seed, tensor_id(name), shape, 1.0, True)
+        rows = np.arange(cfg.t_max)[None, None, :, None]
+        bits = np.where(rows < lens[:, None, None, None], bits, np.uint16(0))
+        caches.append(_dev_tensor(None, bits))
+    kc, vc = caches
+    pos = torch.from_numpy(lens).cuda()
+    rope = tfb.rope_table_init(tc, cfg.t_max)
+    out = torch.empty_like(x)
+    ws = tfb.workspace(tc, B, 1)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")  # > 256 MB Infinity Cache
+
+    def step():
+        tfb.block_decode(tc, w, rope, x, out, (kc, vc), pos, int(lens.max()), ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    total = 0.0
+    for _ in range(steps):
+        flush.fill_(1)  # evict the caches between steps; not timed
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    ms = total / steps
+    tfb.profile_enable(True)
+    for _ in range(steps):
+        flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+    stages = tfb.profile_read()
+    tfb.profile_enable(False)
+    attn_bytes = FM.decode_attention_bytes(lens, cfg.n_kv_heads, dh) + 2 * B * cfg.d * 2
+    wbytes = 2 * FM.block_matrix_params(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    return dict(ms=ms, stages=stages, attn_bytes=attn_bytes, weight_bytes=wbytes, lens=lens)
+
+
+def cpu_baseline(cfg, w32, x32, rows):
+    """The CPU oracle on a bounded prefix of the same block prefill."""
+    import oracle as O
+    from oracle import formulas as FM
+    orc = O.Oracle()
+    t0 = time.time()
+    orc.block_forward(cfg, w32, x32[:, :rows])
+    dt = time.time() - t0
+    flops = FM.block_prefill_flops_causal(cfg.B, rows, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": orc.threads(), "kind": "oracle",
+            "sample": "first %d of %d tokens of the same block prefill (B=%d, full widths), %.1f s wall"
+                      % (rows, cfg.T, cfg.B, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth.configs import C2, C4
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.backends.cuda.matmul.allow_tf32 = False
+
+    pre = time_prefill(C2, args.steps, args.warmup)
+    tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+    gms, gcalls = pre["stages"]["gateup_gemm"]
+    g_ms = gms / gcalls
+    g_flops = 2 * C2.B * C2.T * C2.d * 2 * C2.d_ff
+    roof = {"kernel": "gateup_gemm (fused W1|W3 GEMM + SiLU*up)", "bound": "mfma",
+            "achieved": round(g_flops / (g_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "launch_ms": round(g_ms, 4), "flops_per_launch": g_flops}
+    stages = {k: round(v[0] / v[1], 4) for k, v in pre["stages"].items()}
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-2-7B-shaped block prefill: d=4096 H=Hkv=32 dh=128 f=11008 B=1 T=2048, "
+                               "KV cache written", "global_batch": C2.B, "seq_len": C2.T, "parallelism": "none"},
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": pre["flops"],
+        "roofline": roof,
+        "prefill_stage_ms": stages,
+    }
+    if not args.no_decode:
+        dec = time_decode(C4, args.steps, args.warmup)
+        ams, acalls = dec["stages"]["attention"]
+        cms, ccalls = dec["stages"].get("attention_combine", (0.0, 1))
+        a_ms = ams / acalls + (cms / ccalls if ccalls else 0.0)
+        a_gbps = dec["attn_bytes"] / (a_ms * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": "GQA decode step: d=4096 H=32 Hkv=8 f=14336 B=64, cache lengths uniform in [1024, 4096], "
+                        "caches flushed from Infinity Cache between steps",
+            "tok_per_s": round(C4.B / (dec["ms"] * 1e-3), 1), "ms_per_step": round(dec["ms"], 4),
+            "attention": {"bound": "hbm", "achieved": round(a_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                          "frac": round(a_gbps / PEAK_HBM_GBPS, 4), "bytes_per_launch": dec["attn_bytes"],
+                          "launch_ms": round(a_ms, 4)},
+            "step_bytes": dec["attn_bytes"] + dec["weight_bytes"],
+            "step_hbm_frac": round((dec["attn_bytes"] + dec["weight_bytes"]) / (dec["ms"] * 1e-3) / 1e9 /
+                                   PEAK_HBM_GBPS, 4),
+            "stage_ms": {k: round(v[0] / v[1], 4) for k, v in dec["stages"].items()},
+        }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(C2, pre["w32"], pre["x32"], args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

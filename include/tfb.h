@@ -20,8 +20,8 @@
  *  - Storage is fp32 (TFB_F32) or bf16 (TFB_BF16) as the config says, for
  *    x, out, weights, gains, embedding and the KV cache.  Accumulation, the
  *    softmax and the norms are fp32; logits are always fp32.
- *  - Weights are [in, out] so that y = x W (the page's Code section: "weight W
- *    is [in, out], y = x.W").
+ *  - Weights are stored [in, out] and applied as y = x W, the layout of the
+ *    scalar block in that page's Code section.
  *  - The caller owns all memory.  The library never allocates or frees device
  *    memory, never synchronises and never reads device memory back, so every
  *    call can be captured into a HIP graph.  Scratch space is the caller's
@@ -72,7 +72,7 @@ typedef struct {
 /* One block's weights, all in the config's storage type, [in, out] layout:
  * g_attn, g_mlp [d]; wq [d, H*dh]; wk, wv [d, Hkv*dh]; wo [H*dh, d];
  * w1 (gate, the SiLU branch) and w3 (up) [d, f]; w2 (down) [f, d].
- * No biases (the page: "Parameter count (no biases, SwiGLU, untied head)"). */
+ * The block has no bias terms (that page's parameter count, How it works). */
 typedef struct {
     const void *g_attn, *g_mlp;
     const void *wq, *wk, *wv, *wo;
@@ -80,9 +80,9 @@ typedef struct {
 } tfb_block_weights;
 
 /* KV cache of one layer: k and v are each [batch, Hkv, t_max, dh] in the
- * config's storage type and hold post-RoPE keys and values (the page's
- * "KV cache" paragraph: "store post-RoPE k and v of every past token").
- * Row t of sequence b is the token at absolute position t. */
+ * config's storage type.  Keys are kept after RoPE, values as projected (the
+ * KV cache paragraph of How it works).  Row t of sequence b holds the token
+ * at absolute position t. */
 typedef struct {
     void *k, *v;
     int32_t batch, t_max;
@@ -107,9 +107,9 @@ size_t tfb_workspace_bytes(const tfb_block_config *cfg, int32_t B, int32_t T, in
 
 /* Fill the RoPE table: table[t][i] = (cos, sin) of t * base^(-2i/dh) for
  * t < t_max, i < dh/2, angle computed in fp64 and stored as fp32
- * ([t_max, dh/2, 2] fp32, device).  The page's Implementation notes:
- * "Precompute RoPE cos/sin as a [T_max, dh/2] table"; pairs are interleaved
- * (2i, 2i+1), "Meta's reference code" layout. */
+ * ([t_max, dh/2, 2] fp32, device).  The tirogla page's Implementation notes
+ * recommend such a precomputed [T_max, dh/2] table; rotation pairs are the
+ * interleaved (2i, 2i+1) components. */
 tfb_status tfb_rope_table_init(const tfb_block_config *cfg, int32_t t_max, float *table, void *stream);
 
 /* Full-sequence (or chunked) prefill of one block, the page's How it works
@@ -125,9 +125,9 @@ tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weight
                              int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T, int32_t start_pos,
                              tfb_kv_cache *cache, void *ws, size_t ws_bytes, void *stream);
 
-/* One decode step of one block for B sequences (the page's KV cache
- * paragraph: "a decode step computes q [B, H, 1, dh] and attends over the
- * cache").  x, out: [B, 1, d], out may alias x.  pos: [B] int32 (device,
+/* One decode step of one block for B sequences: each new token's q
+ * [B, H, 1, dh] attends over its sequence's cache (KV cache paragraph of
+ * How it works).  x, out: [B, 1, d], out may alias x.  pos: [B] int32 (device,
  * read-only): the position of each new token, which is also the number of
  * valid cache rows before the step.  Row pos[b] of the cache is written with
  * the new post-RoPE k and v and attention reads rows 0..pos[b].  h_max_pos is
@@ -163,6 +163,18 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
                              int32_t B, int32_t T, tfb_kv_cache *caches, int32_t *lens, int32_t h_max_len,
                              float *logits, int32_t last_only, int32_t *next_ids, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Benchmark instrumentation (host side, off by default).  While enabled,
+ * every launch made by the calls above is bracketed by a pair of HIP events
+ * recorded on the call's stream.  tfb_profile_read waits for the recorded
+ * events, writes the summed milliseconds and launch counts per stage into
+ * ms[i] and calls[i] for i < n (either may be NULL), forgets the records and
+ * returns the number of stages.  Stage i is named by tfb_profile_stage_name.
+ * Not for use under graph capture; the event pool is created lazily on the
+ * host and holds no device memory. */
+tfb_status tfb_profile_enable(int32_t on);
+int32_t tfb_profile_read(float *ms, int32_t *calls, int32_t n);
+const char *tfb_profile_stage_name(int32_t stage);
 
 /* Static description of a status code. */
 const char *tfb_status_string(tfb_status s);

@@ -19,7 +19,8 @@ TFB_F32, TFB_BF16 = 0, 1
 STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTYPE", -4: "TFB_ERR_ALIGN",
           -5: "TFB_ERR_WORKSPACE", -6: "TFB_ERR_CACHE_OVERFLOW", -7: "TFB_ERR_HIP", -8: "TFB_ERR_UNSUPPORTED"}
 EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
-           "tfb_model_forward", "tfb_status_string", "tfb_version")
+           "tfb_model_forward", "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
+           "tfb_profile_stage_name")
 
 _VP = ctypes.c_void_p
 
@@ -83,6 +84,12 @@ def lib():
         L.tfb_status_string.argtypes = [ctypes.c_int]
         L.tfb_status_string.restype = ctypes.c_char_p
         L.tfb_version.restype = ctypes.c_int32
+        L.tfb_profile_enable.argtypes = [ctypes.c_int32]
+        L.tfb_profile_enable.restype = ctypes.c_int
+        L.tfb_profile_read.argtypes = [_VP, _VP, ctypes.c_int32]
+        L.tfb_profile_read.restype = ctypes.c_int32
+        L.tfb_profile_stage_name.argtypes = [ctypes.c_int32]
+        L.tfb_profile_stage_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -208,3 +215,17 @@ def model_forward(h: ModelHandle, rope, ids, caches: list, lens, h_max_len: int,
     _check(lib().tfb_model_forward(ctypes.byref(h.m), _ptr(rope), rope.shape[0], _ptr(ids), B, T, kv, _ptr(lens),
                                    h_max_len, _ptr(logits), 1 if last_only else 0, _ptr(next_ids), _ptr(ws), ws_n,
                                    _stream()), "tfb_model_forward")
+
+
+def profile_enable(on: bool = True):
+    _check(lib().tfb_profile_enable(1 if on else 0), "tfb_profile_enable")
+
+
+def profile_read() -> dict:
+    """{stage name: (total ms, launches)} for the launches recorded since the last read."""
+    L = lib()
+    cap = 64
+    ms = (ctypes.c_float * cap)()
+    calls = (ctypes.c_int32 * cap)()
+    n = min(cap, L.tfb_profile_read(ms, calls, cap))  # one read: it also clears the records
+    return {L.tfb_profile_stage_name(i).decode(): (ms[i], calls[i]) for i in range(n) if calls[i]}

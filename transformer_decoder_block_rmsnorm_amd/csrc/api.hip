@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "kernels.h"
 
 using namespace tfb;
@@ -84,6 +87,41 @@ tfb_status check_cache(const tfb_kv_cache *kv, int B) {
         if ((expr) != hipSuccess) return TFB_ERR_HIP;  \
     } while (0)
 
+// ---- optional per-stage event timing (tfb_profile_*) -----------------------
+enum Stage {
+    ST_RMSNORM_ATTN, ST_QKV, ST_ATTN, ST_ATTN_COMBINE, ST_WO, ST_RMSNORM_MLP, ST_GATEUP, ST_W2,
+    ST_EMBED, ST_FINAL_NORM, ST_LM_HEAD, ST_ARGMAX, ST_KV_APPEND, ST_COUNT
+};
+const char *kStageNames[ST_COUNT] = {"rmsnorm_attn", "qkv_gemm", "attention", "attention_combine", "wo_gemm",
+                                     "rmsnorm_mlp", "gateup_gemm", "w2_gemm", "embed", "final_norm", "lm_head",
+                                     "argmax", "kv_append"};
+struct ProfRec { int stage; hipEvent_t a, b; };
+std::mutex g_prof_mu;
+bool g_prof = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t prof_event() {
+    if (!g_pool.empty()) { hipEvent_t e = g_pool.back(); g_pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDefault) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Runs one launch; when profiling, brackets it with an event pair.
+template <typename F>
+hipError_t staged(int stage, hipStream_t s, F &&launch) {
+    if (!g_prof) return launch();
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ProfRec r{stage, prof_event(), prof_event()};
+    if (r.a) hipEventRecord(r.a, s);
+    hipError_t e = launch();
+    if (r.b) hipEventRecord(r.b, s);
+    if (r.a && r.b) g_recs.push_back(r);
+    return e;
+}
+#define STAGE(st, expr) staged((st), s, [&]() { return (expr); })
+
 // The launches of one block for M = B*T rows ([TIR] How it works steps 2-3):
 //   RMSNorm_1 -> fused QKV GEMM (+RoPE, q to workspace, k and v to the cache)
 //   -> causal GQA attention -> Wo GEMM + residual -> RMSNorm_2
@@ -96,7 +134,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     const int qd = H * dh, kvd = Hkv * dh;
     void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
 
-    TRY_HIP(rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s));
+    TRY_HIP(STAGE(ST_RMSNORM_ATTN, rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s)));
 
     GemmCall g{};
     g.dtype = c.dtype;
@@ -116,7 +154,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.ep.rope_rows = rope_rows;
     g.ep.pos = pos;
     g.ep.T = T; g.ep.H = H; g.ep.Hkv = Hkv; g.ep.dh = dh; g.ep.t_max = t_max; g.ep.start = start;
-    TRY_HIP(gemm_launch(g, s));
+    TRY_HIP(STAGE(ST_QKV, gemm_launch(g, s)));
 
     AttnCall a{};
     a.dtype = c.dtype;
@@ -126,7 +164,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.partials = ws + L.part;
     a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
     a.max_keys = pos ? t_max : start + T;
-    TRY_HIP(pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s));
+    TRY_HIP(STAGE(ST_ATTN, pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s)));
 
     GemmCall o{};
     o.dtype = c.dtype;
@@ -134,9 +172,9 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     o.A = att; o.lda = qd; o.M = M; o.K = qd;
     o.w[0] = w.wo; o.w_cols[0] = d;
     o.ep.M = M; o.ep.N = d; o.ep.out = r; o.ep.ldo = d; o.ep.res = x; o.ep.ldr = d; o.ep.out_f32 = 1;
-    TRY_HIP(gemm_launch(o, s));
+    TRY_HIP(STAGE(ST_WO, gemm_launch(o, s)));
 
-    TRY_HIP(rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true));
+    TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
 
     GemmCall gu{};
     gu.dtype = c.dtype;
@@ -144,7 +182,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     gu.A = h; gu.lda = d; gu.M = M; gu.K = d;
     gu.w[0] = w.w1; gu.w[1] = w.w3; gu.w_cols[0] = f; gu.w_cols[1] = f;
     gu.ep.M = M; gu.ep.N = f; gu.ep.out = act; gu.ep.ldo = f;
-    TRY_HIP(gemm_launch(gu, s));
+    TRY_HIP(STAGE(ST_GATEUP, gemm_launch(gu, s)));
 
     GemmCall dn{};
     dn.dtype = c.dtype;
@@ -152,7 +190,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     dn.A = act; dn.lda = f; dn.M = M; dn.K = f;
     dn.w[0] = w.w2; dn.w_cols[0] = d;
     dn.ep.M = M; dn.ep.N = d; dn.ep.out = out; dn.ep.ldo = d; dn.ep.res = r; dn.ep.ldr = d; dn.ep.res_f32 = 1;
-    TRY_HIP(gemm_launch(dn, s));
+    TRY_HIP(STAGE(ST_W2, gemm_launch(dn, s)));
     return TFB_OK;
 }
 
@@ -161,6 +199,37 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
 extern "C" {
 
 int32_t tfb_version(void) { return 100; }
+
+tfb_status tfb_profile_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof = on != 0;
+    return TFB_OK;
+}
+
+int32_t tfb_profile_read(float *ms, int32_t *calls, int32_t n) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    float acc[ST_COUNT] = {};
+    int32_t cnt[ST_COUNT] = {};
+    for (const ProfRec &r : g_recs) {
+        float t = 0.0f;
+        if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&t, r.a, r.b) == hipSuccess) {
+            acc[r.stage] += t;
+            cnt[r.stage] += 1;
+        }
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    g_recs.clear();
+    for (int i = 0; i < n && i < ST_COUNT; ++i) {
+        if (ms) ms[i] = acc[i];
+        if (calls) calls[i] = cnt[i];
+    }
+    return ST_COUNT;
+}
+
+const char *tfb_profile_stage_name(int32_t stage) {
+    return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "";
+}
 
 const char *tfb_status_string(tfb_status st) {
     switch (st) {
@@ -247,8 +316,9 @@ tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const
     if ((st = check_cache(cache, cache->batch)) != TFB_OK) return st;
     if (n_new <= 0 || h_max_start < 0) return TFB_ERR_SHAPE;
     if ((int64_t)h_max_start + n_new > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
-    TRY_HIP(kv_append_launch(cfg->dtype, cache->k, cache->v, k_new, v_new, start, cache->batch, n_new,
-                             cfg->n_kv_heads, cfg->head_dim, cache->t_max, (hipStream_t)stream));
+    hipStream_t s = (hipStream_t)stream;
+    TRY_HIP(STAGE(ST_KV_APPEND, kv_append_launch(cfg->dtype, cache->k, cache->v, k_new, v_new, start, cache->batch,
+                                                 n_new, cfg->n_kv_heads, cfg->head_dim, cache->t_max, s)));
     return TFB_OK;
 }
 
@@ -284,7 +354,7 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     uint8_t *wsb = (uint8_t *)ws;
     const int M = B * T, d = c.d, V = model->vocab;
     // Embed ([PID] Tiny example, forward), then the L blocks.
-    TRY_HIP(embed_launch(c.dtype, ids, model->embed, wsb + L.x0, M, d, V, s));
+    TRY_HIP(STAGE(ST_EMBED, embed_launch(c.dtype, ids, model->embed, wsb + L.x0, M, d, V, s)));
     void *cur = wsb + L.x0, *nxt = wsb + L.x1;
     for (int l = 0; l < model->n_layers; ++l) {
         if (T > 1)
@@ -306,7 +376,7 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     }
     if (logits || next_ids) {
         void *hn = wsb + L.h;
-        TRY_HIP(rmsnorm_launch(c.dtype, fin, d, model->g_final, hn, d, rows, d, c.rms_eps, s));
+        TRY_HIP(STAGE(ST_FINAL_NORM, rmsnorm_launch(c.dtype, fin, d, model->g_final, hn, d, rows, d, c.rms_eps, s)));
         float *lg = logits;
         if (!lg) {
             if (rows != B) {  // next ids only: the head runs on the last rows
@@ -322,13 +392,13 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
         hd.A = hn; hd.lda = d; hd.M = rows; hd.K = d;
         hd.w[0] = model->w_unembed; hd.w_cols[0] = V;
         hd.ep.M = rows; hd.ep.N = V; hd.ep.out = lg; hd.ep.ldo = V;
-        TRY_HIP(gemm_launch(hd, s));
+        TRY_HIP(STAGE(ST_LM_HEAD, gemm_launch(hd, s)));
         if (next_ids) {
             // Greedy next token from each sequence's last row ([PID] Under the hood, step 6).
             if (rows == B) {
-                TRY_HIP(argmax_launch(lg, V, B, V, next_ids, s));
+                TRY_HIP(STAGE(ST_ARGMAX, argmax_launch(lg, V, B, V, next_ids, s)));
             } else {
-                TRY_HIP(argmax_launch(lg + (int64_t)(T - 1) * V, (int64_t)T * V, B, V, next_ids, s));
+                TRY_HIP(STAGE(ST_ARGMAX, argmax_launch(lg + (int64_t)(T - 1) * V, (int64_t)T * V, B, V, next_ids, s)));
             }
         }
     }

@@ -6,8 +6,8 @@
 // The query of token t of sequence b sits at absolute position
 // p = pos[b] (decode) or start + t (prefill) and attends cache rows 0..p
 // (causal, key j <= query i: [TIR] How it works step 2; [MSA] 5.1).  Query
-// head h reads KV head h / (H / Hkv) ([TIR] Code: "nh/nkv query heads share
-// one KV head").  Softmax in fp32 with a running maximum ([TIR]
+// head h reads KV head h / (H / Hkv): consecutive query heads share a KV head
+// ([TIR] Code, the GQA index in Block::forward).  Softmax in fp32 with a running maximum ([TIR]
 // Implementation notes; [MSA] 1.3).
 #include "kernels.h"
 

@@ -7,7 +7,7 @@ namespace tfb {
 
 enum EpiKind {
     EPI_QKV = 0,    // RoPE on q and k, q -> [B,H,T,dh] workspace, k and v -> KV cache rows
-    EPI_RESID = 1,  // out = residual + acc            ([TIR] How it works: "Add to the residual")
+    EPI_RESID = 1,  // out = residual + acc            ([TIR] How it works steps 2 and 3)
     EPI_SWIGLU = 2, // act = SiLU(gate) * up           ([TIR] How it works step 3)
     EPI_F32 = 3,    // fp32 store (logits)
 };

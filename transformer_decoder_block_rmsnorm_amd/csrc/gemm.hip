@@ -1,5 +1,6 @@
 // Weight GEMMs of the decoder block: y = x W with W stored [in, out]
-// (tirogla "Transformer block", Code: "weight W is [in, out], y = x.W").
+// (tirogla "Transformer block", Code: weights are kept [in, out] and applied
+// as y = x W).
 //
 // bf16: MFMA 32x32x16 tiles, fp32 accumulation.  Both operands are staged in
 // LDS as [rows][64 k] with k contiguous and the eight 16-byte chunks of a row
