@@ -252,3 +252,42 @@ def test_rope_table_matches_oracle(oracle):
         g = tab.cpu().numpy()
         # fp64 angle rounded to fp32 on both sides: at most one ulp apart
         assert np.max(np.abs(g[..., 0] - c)) <= 6e-8 and np.max(np.abs(g[..., 1] - s)) <= 6e-8
+
+
+@pytest.mark.parametrize("lens,d,H,Hkv", [
+    ([700, 1500, 3000, 1], 512, 4, 1),      # several 512-key chunks, G = 4, a length-1 sequence
+    ([40000], 256, 2, 2),                   # more chunks than the partial buffer holds: chunk growth
+    ([5000, 2047], 512, 8, 2),              # dh = 64, G = 4
+])
+def test_decode_long_cache_chunks(oracle, lens, d, H, Hkv):
+    """Decode against caches filled with seeded post-RoPE keys and values."""
+    torch = _torch()
+    import synth
+    from tests.gpu_util import to_dev
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype="bf16", base=500000.0, number=91)
+    tc = tfb.Config.of(cfg)
+    B, dh = len(lens), d // H
+    t_max = max(lens) + 8
+    shape = (B, Hkv, t_max, dh)
+    kf, kb = synth.normal(cfg.seed, 11, shape, 1.0, True)
+    vf, vb = synth.normal(cfg.seed, 12, shape, 1.0, True)
+    rows = np.arange(t_max)[None, None, :, None]
+    valid = rows < np.array(lens)[:, None, None, None]
+    kb = np.where(valid, kb, np.uint16(0x7FC0))  # NaN beyond each sequence
+    vb = np.where(valid, vb, np.uint16(0x7FC0))
+    kf = np.where(valid, kf, np.nan).astype(np.float32)
+    vf = np.where(valid, vf, np.nan).astype(np.float32)
+    kc, vc = to_dev(kf, kb), to_dev(vf, vb)
+    w32, w = dev_weights(cfg)
+    x32, x = dev_x(cfg, B, 1)
+    rope = tfb.rope_table_init(tc, t_max)
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(x)
+    print("case: decode lens", lens, flush=True)
+    tfb.block_decode(tc, w, rope, x, o, (kc, vc), pos, max(lens))
+    torch.cuda.synchronize()
+    okc, ovc = kf.copy(), vf.copy()
+    ref = oracle.block_forward(cfg, w32, x32, start=np.array(lens, np.int32), kc=okc, vc=ovc)
+    got = to_np(o)
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= 2e-2

@@ -127,7 +127,7 @@ hipError_t staged(int stage, hipStream_t s, F &&launch) {
 //   -> causal GQA attention -> Wo GEMM + residual -> RMSNorm_2
 //   -> fused gate-up GEMM (+SiLU * up) -> W2 GEMM + residual.
 tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
-                     const void *x,
+                     int max_pos, const void *x,
                      void *out, int B, int T, int start, const int32_t *pos, void *kc, void *vc, int t_max,
                      uint8_t *ws, const WsLayout &L, hipStream_t s) {
     const int M = B * T, d = c.d, H = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, f = c.d_ff;
@@ -163,7 +163,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.scale = 1.0f / sqrtf((float)dh);
     a.partials = ws + L.part;
     a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
-    a.max_keys = pos ? t_max : start + T;
+    a.max_keys = pos ? max_pos + 1 : start + T;
+    a.max_splits = kMaxSplits;
     TRY_HIP(STAGE(ST_ATTN, pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s)));
 
     GemmCall o{};
@@ -284,7 +285,7 @@ tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weight
     void *kc = cache ? cache->k : (void *)(wsb + L.kv_k);
     void *vc = cache ? cache->v : (void *)(wsb + L.kv_v);
     const int t_max = cache ? cache->t_max : T;
-    return run_block(*cfg, *w, rope_table, t_max_table, x, out, B, T, start_pos, nullptr, kc, vc, t_max, wsb, L,
+    return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, start_pos, nullptr, kc, vc, t_max, wsb, L,
                      (hipStream_t)stream);
 }
 
@@ -302,7 +303,7 @@ tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights
     const WsLayout L = ws_layout(*cfg, B, 1, 0);
     if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
     if (!aligned(ws)) return TFB_ERR_ALIGN;
-    return run_block(*cfg, *w, rope_table, t_max_table, x, out, B, 1, 0, pos, cache->k, cache->v, cache->t_max, (uint8_t *)ws,
+    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v, cache->t_max, (uint8_t *)ws,
                      L, (hipStream_t)stream);
 }
 
@@ -358,10 +359,10 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     void *cur = wsb + L.x0, *nxt = wsb + L.x1;
     for (int l = 0; l < model->n_layers; ++l) {
         if (T > 1)
-            st = run_block(c, model->layers[l], rope_table, t_max_table, cur, nxt, B, T, 0, nullptr, caches[l].k, caches[l].v,
+            st = run_block(c, model->layers[l], rope_table, t_max_table, 0, cur, nxt, B, T, 0, nullptr, caches[l].k, caches[l].v,
                            caches[l].t_max, wsb, L, s);
         else
-            st = run_block(c, model->layers[l], rope_table, t_max_table, cur, nxt, B, 1, 0, lens, caches[l].k, caches[l].v,
+            st = run_block(c, model->layers[l], rope_table, t_max_table, h_max_len, cur, nxt, B, 1, 0, lens, caches[l].k, caches[l].v,
                            caches[l].t_max, wsb, L, s);
         if (st != TFB_OK) return st;
         void *tmp = cur; cur = nxt; nxt = tmp;

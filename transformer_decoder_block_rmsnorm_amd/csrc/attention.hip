@@ -78,6 +78,495 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 prefill: flash-style attention on MFMA 32x32x16 ([GEN] FlashAttention
+// entry and [MSA] 6: exact attention computed tile by tile with a running
+// softmax, never materialising the T x T score matrix).
+//
+// Workgroup = 4 waves = 128 query rows of one KV head's group: HG heads of the
+// group side by side times 128/HG positions, so every K/V tile loaded into LDS
+// serves all query heads that share it (GQA).  Each wave owns 32 queries.
+//   S^T[keys, queries] = K . Q^T : lane l holds query l%32, so the softmax of
+//                                  a query lives in one lane (plus lane l^32).
+//   O^T[e, queries]   += V^T . P^T : P^T comes straight from the S^T
+//                                  accumulators (converted to bf16); V is
+//                                  stored transposed in LDS with the keys of
+//                                  each 16-key slice permuted to the order in
+//                                  which the accumulator holds them.
+// Tiles entirely above the causal diagonal are skipped per wave; the
+// workgroups with the longest key ranges are scheduled first.  Keys at or
+// beyond start + T are zero-filled in LDS, so unwritten cache rows (even NaN)
+// never reach the result.
+// ---------------------------------------------------------------------------
+struct FlashArgs {
+    const bf16_t *q, *kc, *vc;
+    bf16_t *o;
+    int B, T, H, Hkv, t_max, start;
+    int HG, PB, n_qblocks, n_hsub;
+    float scale_log2e;
+};
+
+// Slot of key k (0..15) inside its 16-key slice in the transposed V tile:
+// lane half h reads slots [8h, 8h+8) and must find there the keys it holds in
+// the S^T accumulator: {4h..4h+3, 8+4h..8+4h+3}.
+__device__ __forceinline__ int v_slot(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+template <int DH>
+__global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
+    constexpr int BKV = 64;          // keys per tile
+    constexpr int NS = DH / 16;      // 16-wide dh slices of q.k
+    constexpr int NE = DH / 32;      // 32-row e tiles of O^T
+    constexpr int KCH = DH / 8;      // 16-byte chunks per K row
+    constexpr int K_PER = BKV * KCH / 256;
+    constexpr int NVB = (BKV / 8) * (DH / 8);  // 8x8 V blocks per tile
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BKV * DH];
+    auto Ks = [&](int bf) { return lds + bf * 2 * BKV * DH; };
+    auto Vs = [&](int bf) { return lds + bf * 2 * BKV * DH + BKV * DH; };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int nbh = a.B * a.Hkv * a.n_hsub;
+    const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / nbh);  // longest key ranges first
+    int rem = blockIdx.x % nbh;
+    const int hsub = rem % a.n_hsub;
+    rem /= a.n_hsub;
+    const int kvh = rem % a.Hkv, b = rem / a.Hkv;
+    const int G = a.H / a.Hkv;
+    const int hl = wave % a.HG, pw = wave / a.HG;
+    const int h = kvh * G + hsub * a.HG + hl;
+    const int t0 = qb * a.PB + pw * 32;
+    const int kv_len = a.start + a.T;
+    const int t_last_wg = min(qb * a.PB + a.PB - 1, a.T - 1);
+    const int n_tiles = (a.start + t_last_wg) / BKV + 1;
+    const bool wave_active = t0 < a.T;
+    const int wave_tiles = wave_active ? (a.start + min(t0 + 31, a.T - 1)) / BKV + 1 : 0;
+
+    // q fragments (B operand of S^T): row t0 + lr, dh [16s + 8lh, +8)
+    bf16x8 qf[NS];
+    {
+        const int t = t0 + lr;
+        const bf16_t *qrow = a.q + (((int64_t)b * a.H + h) * a.T + min(t, a.T - 1)) * DH;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            u32x4 v = *(const u32x4 *)(qrow + 16 * s + 8 * lh);
+            if (t >= a.T) v = u32x4{0, 0, 0, 0};
+            qf[s] = as_bf16x8(v);
+        }
+    }
+    const int qpos = a.start + t0 + lr;
+    const bf16_t *Kg = a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
+    const bf16_t *Vg = a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
+
+    u32x4 rk[K_PER], rv[8];
+    auto load_tile = [&](int it) {
+        const int j0 = it * BKV;
+#pragma unroll
+        for (int i = 0; i < K_PER; ++i) {
+            const int c = tid + 256 * i, key = c / KCH, ch = c % KCH, j = j0 + key;
+            rk[i] = (j < kv_len) ? *(const u32x4 *)(Kg + (int64_t)j * DH + ch * 8) : u32x4{0, 0, 0, 0};
+        }
+        if (tid < NVB) {
+            const int kb = tid / (DH / 8), eb = tid % (DH / 8);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int j = j0 + kb * 8 + r;
+                rv[r] = (j < kv_len) ? *(const u32x4 *)(Vg + (int64_t)j * DH + eb * 8) : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int bf) {
+#pragma unroll
+        for (int i = 0; i < K_PER; ++i) {
+            const int c = tid + 256 * i, key = c / KCH, ch = c % KCH;
+            *(u32x4 *)(Ks(bf) + key * DH + ((ch ^ (key & (KCH - 1))) * 8)) = rk[i];
+        }
+        if (tid < NVB) {
+            const int kb = tid / (DH / 8), eb = tid % (DH / 8);
+            u32x4 t[8];
+            transpose8x8_bf16(rv, t);
+            // keys kb*8 .. kb*8+7: first four go to slot v_slot(8*(kb&1)), last four to v_slot(8*(kb&1)+4)
+            const int base = (kb >> 1) * 16;
+            const int p_lo = base + v_slot(8 * (kb & 1)), p_hi = base + v_slot(8 * (kb & 1) + 4);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int e = eb * 8 + c;
+                bf16_t *row = Vs(bf) + e * BKV;
+                *(u32x2 *)(row + (((p_lo >> 3) ^ (e & 7)) << 3) + (p_lo & 7)) = u32x2{t[c][0], t[c][1]};
+                *(u32x2 *)(row + (((p_hi >> 3) ^ (e & 7)) << 3) + (p_hi & 7)) = u32x2{t[c][2], t[c][3]};
+            }
+        }
+    };
+
+    f32x16 oacc[NE];
+#pragma unroll
+    for (int te = 0; te < NE; ++te)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[te][v] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int it = 0; it < n_tiles; ++it) {
+        const int bf = it & 1;
+        if (it + 1 < n_tiles) load_tile(it + 1);
+        if (it < wave_tiles) {
+            const int j0 = it * BKV;
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.0f;
+                const int key = kt * 32 + lr;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const bf16x8 kf =
+                        as_bf16x8(*(const u32x4 *)(Ks(bf) + key * DH + (((2 * s + lh) ^ (key & (KCH - 1))) * 8)));
+                    sacc[kt] = mfma32(kf, qf[s], sacc[kt]);
+                }
+            }
+            // online softmax in the log2 domain
+            const bool need_mask = (j0 + BKV - 1 > a.start + t0);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float x = sacc[kt][v] * a.scale_log2e;
+                    if (need_mask) {
+                        const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                        if (key > qpos) x = -INFINITY;
+                    }
+                    sacc[kt][v] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run, mx);
+            const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            float sum = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = __builtin_amdgcn_exp2f(sacc[kt][v] - msub);
+                    sacc[kt][v] = p;
+                    sum += p;
+                }
+            sum += __shfl_xor(sum, 32, 64);
+            l_run = l_run * alpha + sum;
+            m_run = m_new;
+#pragma unroll
+            for (int te = 0; te < NE; ++te)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[te][v] *= alpha;
+            bf16x8 pf[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const f32x16 &src = sacc[s2 >> 1];
+                const int o = 8 * (s2 & 1);
+                u32x4 w;
+                w[0] = pack_bf16x2(src[o + 0], src[o + 1]);
+                w[1] = pack_bf16x2(src[o + 2], src[o + 3]);
+                w[2] = pack_bf16x2(src[o + 4], src[o + 5]);
+                w[3] = pack_bf16x2(src[o + 6], src[o + 7]);
+                pf[s2] = as_bf16x8(w);
+            }
+#pragma unroll
+            for (int te = 0; te < NE; ++te) {
+                const int e = te * 32 + lr;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const bf16x8 vf =
+                        as_bf16x8(*(const u32x4 *)(Vs(bf) + e * BKV + (((2 * s2 + lh) ^ (e & 7)) * 8)));
+                    oacc[te] = mfma32(vf, pf[s2], oacc[te]);
+                }
+            }
+        }
+        if (it + 1 < n_tiles) store_tile(bf ^ 1);
+        __syncthreads();
+    }
+
+    const int t = t0 + lr;
+    if (wave_active && t < a.T) {
+        const float inv = 1.0f / l_run;
+        bf16_t *orow = a.o + ((int64_t)b * a.T + t) * ((int64_t)a.H * DH) + (int64_t)h * DH;
+#pragma unroll
+        for (int te = 0; te < NE; ++te)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int e = te * 32 + 8 * g + 4 * lh;
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[te][4 * g] * inv, oacc[te][4 * g + 1] * inv);
+                w[1] = pack_bf16x2(oacc[te][4 * g + 2] * inv, oacc[te][4 * g + 3] * inv);
+                *(u32x2 *)(orow + e) = w;
+            }
+    }
+}
+
+static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
+    FlashArgs a;
+    a.q = (const bf16_t *)c.q;
+    a.kc = (const bf16_t *)c.kc;
+    a.vc = (const bf16_t *)c.vc;
+    a.o = (bf16_t *)c.o;
+    a.B = c.B; a.T = c.T; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max; a.start = c.start;
+    const int G = c.H / c.Hkv;
+    a.HG = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
+    if (G % a.HG) a.HG = 1;
+    a.PB = 128 / a.HG;
+    a.n_hsub = G / a.HG;
+    a.n_qblocks = (c.T + a.PB - 1) / a.PB;
+    a.scale_log2e = c.scale * 1.4426950408889634f;
+    const int blocks = a.n_qblocks * c.B * c.Hkv * a.n_hsub;
+    if (c.dh == 128)
+        hipLaunchKernelGGL(flash_prefill_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(flash_prefill_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 decode: split-KV streaming over the cache ([GEN] KV cache and inference
+// math: a decode step reads the whole cache and is bandwidth bound).
+// One workgroup per (sequence b, KV head, chunk of keys); all G = H/Hkv query
+// heads of the KV head are served by one read of each K and V row.
+//   scores: lane = key, q.k with v_dot2_f32_bf16, q broadcast from LDS;
+//   P.V:    lane = (row group, 8-wide e chunk), 16-byte V loads, p from LDS.
+// Each workgroup writes (max, sum, unnormalised o) per head; a second kernel
+// merges the chunks of a (b, h) with log-sum-exp weights.  Keys at or beyond
+// pos[b] + 1 are never loaded.
+// ---------------------------------------------------------------------------
+constexpr int kDecChunk = 512;  // keys per workgroup (multiple of 256)
+
+struct DecArgs {
+    const bf16_t *q, *kc, *vc;
+    bf16_t *o;
+    const int32_t *pos;
+    float *part;      // [B][H][max_chunks][DH + 4]
+    int B, H, Hkv, t_max, max_chunks, chunk_keys;
+    float scale_log2e;
+};
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int DH, int G>
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
+    constexpr int KC = DH / 8;         // 16-byte chunks per row
+    constexpr int EC = DH / 8;         // lanes per V row (8 e each)
+    constexpr int RG = 64 / EC;        // row groups per wave
+    constexpr int RPL = 64 / RG;       // V rows per lane per 64-key step
+    __shared__ __attribute__((aligned(16))) bf16_t q_s[G][DH];
+    __shared__ __attribute__((aligned(16))) float p_s[4][64][G];
+    __shared__ float red_ml[4][G][2];
+    __shared__ __attribute__((aligned(16))) float red_o[4][G][DH];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    int n_keys = a.pos[b] + 1;
+    n_keys = min(n_keys, a.t_max);
+    const int k_begin = ch * a.chunk_keys;
+    if (k_begin >= n_keys) return;  // whole block: no barrier has been reached yet
+    const int k_end = min(n_keys, k_begin + a.chunk_keys);
+    const int h0 = kvh * G;
+
+    for (int i = tid; i < G * DH / 8; i += 256) {
+        const int h = i / (DH / 8), c = i % (DH / 8);
+        *(u32x4 *)(&q_s[h][c * 8]) = *(const u32x4 *)(a.q + ((int64_t)b * a.H + h0 + h) * DH + c * 8);
+    }
+    __syncthreads();
+
+    const bf16_t *Kg = a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
+    const bf16_t *Vg = a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
+    const int rg = lane / EC, ec = lane % EC;
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    }
+
+    for (int base = k_begin + wave * 64; base < k_end; base += 256) {
+        const int j = base + lane;
+        const bool valid = j < k_end;
+        u32x4 kr[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            kr[c] = valid ? *(const u32x4 *)(Kg + (int64_t)j * DH + c * 8) : u32x4{0, 0, 0, 0};
+        u32x4 vr[RPL];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int jr = base + rg + RG * i;
+            vr[i] = (jr < k_end) ? *(const u32x4 *)(Vg + (int64_t)jr * DH + ec * 8) : u32x4{0, 0, 0, 0};
+        }
+        float x[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float d = 0.0f;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const u32x4 qv = *(const u32x4 *)(&q_s[h][c * 8]);
+                d = dot2_bf16(kr[c][0], qv[0], d);
+                d = dot2_bf16(kr[c][1], qv[1], d);
+                d = dot2_bf16(kr[c][2], qv[2], d);
+                d = dot2_bf16(kr[c][3], qv[3], d);
+            }
+            x[h] = valid ? d * a.scale_log2e : -INFINITY;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float m_new = fmaxf(m[h], wave_max(x[h]));  // lane 0 is valid: finite
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
+            const float p = __builtin_amdgcn_exp2f(x[h] - m_new);
+            l[h] = l[h] * alpha + wave_sum(p);
+            m[h] = m_new;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+            p_s[wave][lane][h] = p;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int r = rg + RG * i;
+            float pv[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) pv[h] = p_s[wave][r][h];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float v0 = bf16_lo(vr[i][w]), v1 = bf16_hi(vr[i][w]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    acc[h][2 * w] += pv[h] * v0;
+                    acc[h][2 * w + 1] += pv[h] * v1;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    // sum the row groups (lanes with equal ec)
+#pragma unroll
+    for (int o = EC; o < 64; o <<= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
+    if (lane < EC) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            *(f32x4 *)(&red_o[wave][h][ec * 8]) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+            *(f32x4 *)(&red_o[wave][h][ec * 8 + 4]) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            red_ml[wave][h][0] = m[h];
+            red_ml[wave][h][1] = l[h];
+        }
+    }
+    __syncthreads();
+    // merge the four waves and write this chunk's partial result
+    for (int i = tid; i < G * DH; i += 256) {
+        const int h = i / DH, e = i % DH;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, red_ml[w][h][0]);
+        float L = 0.0f, O = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float sc = (red_ml[w][h][0] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(red_ml[w][h][0] - M);
+            L += sc * red_ml[w][h][1];
+            O += sc * red_o[w][h][e];
+        }
+        float *dst = a.part + (((int64_t)b * a.H + h0 + h) * a.max_chunks + ch) * (DH + 4);
+        dst[4 + e] = O;
+        if (e == 0) { dst[0] = M; dst[1] = L; }
+    }
+}
+
+// Merge the chunk partials of each (b, h): one wave per pair.
+template <int DH>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int bh = blockIdx.x * 4 + wave;
+    if (bh >= a.B * a.H) return;
+    const int b = bh / a.H;
+    const int n_keys = min(a.pos[b] + 1, a.t_max);
+    const int n_ch = min((n_keys + a.chunk_keys - 1) / a.chunk_keys, a.max_chunks);
+    const float *base = a.part + (int64_t)bh * a.max_chunks * (DH + 4);
+    float M = -INFINITY;
+    for (int c = 0; c < n_ch; ++c) M = fmaxf(M, base[c * (DH + 4)]);
+    constexpr int EPL = DH / 64;
+    float L = 0.0f, O[EPL] = {};
+    for (int c = 0; c < n_ch; ++c) {
+        const float *p = base + c * (DH + 4);
+        const float sc = __builtin_amdgcn_exp2f(p[0] - M);
+        L += sc * p[1];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) O[i] += sc * p[4 + lane * EPL + i];
+    }
+    const float inv = 1.0f / L;
+    bf16_t *out = a.o + (int64_t)bh * DH + lane * EPL;
+    if constexpr (EPL == 2) {
+        *(uint32_t *)out = pack_bf16x2(O[0] * inv, O[1] * inv);
+    } else {
+        out[0] = f32_to_bf16(O[0] * inv);
+    }
+}
+
+size_t decode_part_bytes(int B, int H, int dh, int max_chunks) {
+    return (size_t)B * H * max_chunks * (dh + 4) * sizeof(float);
+}
+
+template <int DH>
+static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s) {
+    const int G = c.H / c.Hkv;
+    dim3 grid(a.max_chunks, c.Hkv, c.B);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((decode_attn_kernel<DH, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_attn_kernel<DH, 4>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_attn_kernel<DH, 8>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3((c.B * c.H + 3) / 4), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+static hipError_t split_decode_launch(const AttnCall &c, hipStream_t s) {
+    DecArgs a;
+    a.q = (const bf16_t *)c.q;
+    a.kc = (const bf16_t *)c.kc;
+    a.vc = (const bf16_t *)c.vc;
+    a.o = (bf16_t *)c.o;
+    a.pos = c.pos;
+    a.part = (float *)c.partials;
+    a.B = c.B; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max;
+    // chunk size: kDecChunk keys, grown in steps of kDecChunk when the longest
+    // sequence would need more chunks than the partial buffer holds
+    const int max_keys = c.max_keys;
+    int chunks = (max_keys + kDecChunk - 1) / kDecChunk;
+    int chunk_keys = kDecChunk;
+    if (chunks > c.max_splits) {
+        chunk_keys = kDecChunk * ((chunks + c.max_splits - 1) / c.max_splits);
+        chunks = (max_keys + chunk_keys - 1) / chunk_keys;
+    }
+    a.chunk_keys = chunk_keys;
+    a.max_chunks = chunks;
+    a.scale_log2e = c.scale * 1.4426950408889634f;
+    if (decode_part_bytes(c.B, c.H, c.dh, chunks) > c.partial_bytes) return hipErrorInvalidValue;
+    return c.dh == 128 ? decode_launch_dh<128>(c, a, s) : decode_launch_dh<64>(c, a, s);
+}
+
 static hipError_t rowwise_launch(const AttnCall &a, hipStream_t s) {
     const int64_t waves = (int64_t)a.B * a.H * a.T;
     dim3 grid((unsigned)((waves + 3) / 4));
@@ -88,8 +577,18 @@ static hipError_t rowwise_launch(const AttnCall &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s) { return rowwise_launch(a, s); }
-hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s) { return rowwise_launch(a, s); }
-size_t attention_decode_scratch_bytes(int, int, int, int) { return 0; }
+hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s) {
+    if (a.dtype == TFB_BF16 && (a.dh == 128 || a.dh == 64)) return flash_launch(a, s);
+    return rowwise_launch(a, s);
+}
+hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s) {
+    const int G = a.H / a.Hkv;
+    if (a.dtype == TFB_BF16 && (a.dh == 128 || a.dh == 64) && (G == 1 || G == 2 || G == 4 || G == 8))
+        return split_decode_launch(a, s);
+    return rowwise_launch(a, s);
+}
+size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits) {
+    return decode_part_bytes(B, H, dh, max_splits);
+}
 
 }  // namespace tfb

@@ -41,6 +41,7 @@ struct AttnCall {
     void *partials;       // split-KV scratch (decode), may be NULL
     size_t partial_bytes;
     int max_keys;         // host bound on keys per query (for work sizing)
+    int max_splits;       // chunks per (b, h) the partial buffer holds
 };
 hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
