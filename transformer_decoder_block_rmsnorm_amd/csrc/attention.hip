@@ -330,9 +330,8 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
 // bf16 decode: split-KV streaming over the cache ([GEN] KV cache and inference
 // math: a decode step reads the whole cache and is bandwidth bound).
 // One workgroup per (sequence b, KV head, chunk of keys); all G = H/Hkv query
-// heads of the KV head are served by one read of each K and V row.
-//   scores: lane = key, q.k with v_dot2_f32_bf16, q broadcast from LDS;
-//   P.V:    lane = (row group, 8-wide e chunk), 16-byte V loads, p from LDS.
+// heads of the KV head are served by one read of each K and V row, and both
+// products run on MFMA 16x16x32 with the heads as matrix columns.
 // Each workgroup writes (max, sum, unnormalised o) per head; a second kernel
 // merges the chunks of a (b, h) with log-sum-exp weights.  Keys at or beyond
 // pos[b] + 1 are never loaded.
@@ -348,128 +347,137 @@ struct DecArgs {
     float scale_log2e;
 };
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 template <int DH, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
-    constexpr int KC = DH / 8;         // 16-byte chunks per row
-    constexpr int EC = DH / 8;         // lanes per V row (8 e each)
-    constexpr int RG = 64 / EC;        // row groups per wave
-    constexpr int RPL = 64 / RG;       // V rows per lane per 64-key step
-    __shared__ __attribute__((aligned(16))) bf16_t q_s[G][DH];
-    __shared__ __attribute__((aligned(16))) float p_s[4][64][G];
-    __shared__ float red_ml[4][G][2];
+    // Per wave, 64 keys at a time on MFMA 16x16x32 (lane l: column l%16,
+    // k group g = l/16):
+    //   S^T[keys, heads] = K . Q^T   K rows from global, 16 rows x 64
+    //                                 contiguous bytes per load;
+    //   O[heads, e]     += P . V     V loaded 8 rows x 16 bytes per lane
+    //                                 (whole rows per instruction) and
+    //                                 transposed 8x8 in registers; output
+    //                                 column n of tile c is e = 8n + c.
+    // Heads are MFMA columns: G <= 16 (unused columns are zero).
+    static_assert(G <= 16, "at most 16 query heads per KV head");
+    constexpr int NS = DH / 32;        // 32-wide dh slices
+    constexpr int NCH = DH / 8;        // 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) float red_o[4][G][DH];
+    __shared__ float red_ml[4][G][2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, g4 = lane >> 4;
     const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    int n_keys = a.pos[b] + 1;
-    n_keys = min(n_keys, a.t_max);
+    const int n_keys = min(a.pos[b] + 1, a.t_max);
     const int k_begin = ch * a.chunk_keys;
-    if (k_begin >= n_keys) return;  // whole block: no barrier has been reached yet
+    if (k_begin >= n_keys) return;  // whole block leaves before any barrier
     const int k_end = min(n_keys, k_begin + a.chunk_keys);
     const int h0 = kvh * G;
 
-    for (int i = tid; i < G * DH / 8; i += 256) {
-        const int h = i / (DH / 8), c = i % (DH / 8);
-        *(u32x4 *)(&q_s[h][c * 8]) = *(const u32x4 *)(a.q + ((int64_t)b * a.H + h0 + h) * DH + c * 8);
+    // Q^T operand: column = head ln, k slots = dh chunk 4s + g4
+    bf16x8 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        u32x4 v = {0, 0, 0, 0};
+        if (ln < G) v = *(const u32x4 *)(a.q + ((int64_t)b * a.H + h0 + ln) * DH + (4 * s + g4) * 8);
+        qf[s] = as_bf16x8(v);
     }
-    __syncthreads();
-
     const bf16_t *Kg = a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
     const bf16_t *Vg = a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
-    const int rg = lane / EC, ec = lane % EC;
+    const bool v_lane = ln < NCH;  // dh = 64 uses half the output columns
 
-    float m[G], l[G], acc[G][8];
+    float m_run = -INFINITY, l_run = 0.0f;  // for head ln
+    f32x4 oacc[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-    }
+    for (int c = 0; c < 8; ++c) oacc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int base = k_begin + wave * 64; base < k_end; base += 256) {
-        const int j = base + lane;
-        const bool valid = j < k_end;
-        u32x4 kr[KC];
+        u32x4 kr[4][NS], vr[2][8];
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-            kr[c] = valid ? *(const u32x4 *)(Kg + (int64_t)j * DH + c * 8) : u32x4{0, 0, 0, 0};
-        u32x4 vr[RPL];
+        for (int t = 0; t < 4; ++t) {
+            const int j = base + 16 * t + ln;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int jr = base + rg + RG * i;
-            vr[i] = (jr < k_end) ? *(const u32x4 *)(Vg + (int64_t)jr * DH + ec * 8) : u32x4{0, 0, 0, 0};
+            for (int s = 0; s < NS; ++s)
+                kr[t][s] = (j < k_end) ? *(const u32x4 *)(Kg + (int64_t)j * DH + (4 * s + g4) * 8)
+                                       : u32x4{0, 0, 0, 0};
         }
-        float x[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float d = 0.0f;
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                const u32x4 qv = *(const u32x4 *)(&q_s[h][c * 8]);
-                d = dot2_bf16(kr[c][0], qv[0], d);
-                d = dot2_bf16(kr[c][1], qv[1], d);
-                d = dot2_bf16(kr[c][2], qv[2], d);
-                d = dot2_bf16(kr[c][3], qv[3], d);
+            for (int r = 0; r < 8; ++r) {
+                // slots 0-3: keys 32u + 4g + v; slots 4-7: keys 32u + 16 + 4g + v
+                const int j = base + 32 * u + 16 * (r >> 2) + 4 * g4 + (r & 3);
+                vr[u][r] = (v_lane && j < k_end) ? *(const u32x4 *)(Vg + (int64_t)j * DH + ln * 8)
+                                                 : u32x4{0, 0, 0, 0};
             }
-            x[h] = valid ? d * a.scale_log2e : -INFINITY;
+        f32x4 sacc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) sacc[t] = mfma16(as_bf16x8(kr[t][s]), qf[s], sacc[t]);
         }
+        // online softmax for head ln over keys 16t + 4g + v
+        float mx = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float m_new = fmaxf(m[h], wave_max(x[h]));  // lane 0 is valid: finite
-            const float alpha = __builtin_amdgcn_exp2f(m[h] - m_new);
-            const float p = __builtin_amdgcn_exp2f(x[h] - m_new);
-            l[h] = l[h] * alpha + wave_sum(p);
-            m[h] = m_new;
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-            p_s[wave][lane][h] = p;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int r = rg + RG * i;
-            float pv[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) pv[h] = p_s[wave][r][h];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float v0 = bf16_lo(vr[i][w]), v1 = bf16_hi(vr[i][w]);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    acc[h][2 * w] += pv[h] * v0;
-                    acc[h][2 * w + 1] += pv[h] * v1;
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int j = base + 16 * t + 4 * g4 + v;
+                const float x = (j < k_end) ? sacc[t][v] * a.scale_log2e : -INFINITY;
+                sacc[t][v] = x;
+                mx = fmaxf(mx, x);
             }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);  // key `base` is valid: finite
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        float sum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float p = __builtin_amdgcn_exp2f(sacc[t][v] - m_new);
+                sacc[t][v] = p;
+                sum += p;
+            }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        l_run = l_run * alpha + sum;
+        m_run = m_new;
+        // O rows are heads 4*g4 + v: fetch their rescale factors
+        float al[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) al[v] = __shfl(alpha, 4 * g4 + v, 64);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) oacc[c][v] *= al[v];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            u32x4 pw;
+            pw[0] = pack_bf16x2(sacc[2 * u][0], sacc[2 * u][1]);
+            pw[1] = pack_bf16x2(sacc[2 * u][2], sacc[2 * u][3]);
+            pw[2] = pack_bf16x2(sacc[2 * u + 1][0], sacc[2 * u + 1][1]);
+            pw[3] = pack_bf16x2(sacc[2 * u + 1][2], sacc[2 * u + 1][3]);
+            const bf16x8 pf = as_bf16x8(pw);
+            u32x4 vt[8];
+            transpose8x8_bf16(vr[u], vt);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) oacc[c] = mfma16(pf, as_bf16x8(vt[c]), oacc[c]);
         }
-        __builtin_amdgcn_wave_barrier();
     }
-    // sum the row groups (lanes with equal ec)
+    // per-wave results to LDS: head 4*g4 + v, e = 8*ln + c
 #pragma unroll
-    for (int o = EC; o < 64; o <<= 1)
+    for (int v = 0; v < 4; ++v) {
+        const int h = 4 * g4 + v;
+        if (h < G && v_lane) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], o, 64);
-    if (lane < EC) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            *(f32x4 *)(&red_o[wave][h][ec * 8]) = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-            *(f32x4 *)(&red_o[wave][h][ec * 8 + 4]) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+            for (int c = 0; c < 8; ++c) red_o[wave][h][8 * ln + c] = oacc[c][v];
         }
     }
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            red_ml[wave][h][0] = m[h];
-            red_ml[wave][h][1] = l[h];
-        }
+    if (g4 == 0 && ln < G) {
+        red_ml[wave][ln][0] = m_run;
+        red_ml[wave][ln][1] = l_run;
     }
     __syncthreads();
     // merge the four waves and write this chunk's partial result
@@ -534,6 +542,7 @@ static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s)
         case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2>), grid, dim3(256), 0, s, a); break;
         case 4: hipLaunchKernelGGL((decode_attn_kernel<DH, 4>), grid, dim3(256), 0, s, a); break;
         case 8: hipLaunchKernelGGL((decode_attn_kernel<DH, 8>), grid, dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((decode_attn_kernel<DH, 16>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
@@ -583,7 +592,7 @@ hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s) {
 }
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s) {
     const int G = a.H / a.Hkv;
-    if (a.dtype == TFB_BF16 && (a.dh == 128 || a.dh == 64) && (G == 1 || G == 2 || G == 4 || G == 8))
+    if (a.dtype == TFB_BF16 && (a.dh == 128 || a.dh == 64) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16))
         return split_decode_launch(a, s);
     return rowwise_launch(a, s);
 }
