@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -23,7 +24,7 @@ inline size_t esize(int dtype) { return dtype == TFB_BF16 ? 2 : 4; }
 constexpr int kMaxSplits = 64;
 
 struct WsLayout {
-    size_t h, q, att, r, act, kv_k, kv_v, part, x0, x1, last, logits, total;
+    size_t h, q, att, r, act, kv_k, kv_v, part, skinny, skinny_bytes, x0, x1, last, logits, total;
 };
 
 WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
@@ -40,6 +41,20 @@ WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
     L.kv_k = take(M * kvd * es);  // keys and values when no cache is given
     L.kv_v = take(M * kvd * es);
     L.part = take(attention_decode_scratch_bytes(B, c.n_heads, c.head_dim, kMaxSplits));
+    if (c.dtype == TFB_BF16) {
+        // split-K partials of the skinny GEMMs (rows <= kSkinnyMaxM): the
+        // block's GEMMs in decode and the LM head over the last rows
+        size_t sk = 0;
+        if (M <= (size_t)kSkinnyMaxM)
+            sk = std::max({skinny_part_bytes((int)M, c.d, (int)(qd + 2 * kvd)),
+                           skinny_part_bytes((int)M, (int)qd, c.d), skinny_part_bytes((int)M, c.d, 2 * c.d_ff),
+                           skinny_part_bytes((int)M, c.d_ff, c.d)});
+        if (vocab > 0 && B <= kSkinnyMaxM) sk = std::max(sk, skinny_part_bytes(B, c.d, vocab));
+        if (sk) {
+            L.skinny_bytes = sk;
+            L.skinny = take(sk);
+        }
+    }
     if (vocab > 0) {
         L.x0 = take(M * c.d * es);
         L.x1 = take(M * c.d * es);
@@ -154,6 +169,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.ep.rope_rows = rope_rows;
     g.ep.pos = pos;
     g.ep.T = T; g.ep.H = H; g.ep.Hkv = Hkv; g.ep.dh = dh; g.ep.t_max = t_max; g.ep.start = start;
+    g.scratch = L.skinny_bytes ? ws + L.skinny : nullptr;
+    g.scratch_bytes = L.skinny_bytes;
     TRY_HIP(STAGE(ST_QKV, gemm_launch(g, s)));
 
     AttnCall a{};
@@ -173,6 +190,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     o.A = att; o.lda = qd; o.M = M; o.K = qd;
     o.w[0] = w.wo; o.w_cols[0] = d;
     o.ep.M = M; o.ep.N = d; o.ep.out = r; o.ep.ldo = d; o.ep.res = x; o.ep.ldr = d; o.ep.out_f32 = 1;
+    o.scratch = g.scratch;
+    o.scratch_bytes = g.scratch_bytes;
     TRY_HIP(STAGE(ST_WO, gemm_launch(o, s)));
 
     TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
@@ -183,6 +202,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     gu.A = h; gu.lda = d; gu.M = M; gu.K = d;
     gu.w[0] = w.w1; gu.w[1] = w.w3; gu.w_cols[0] = f; gu.w_cols[1] = f;
     gu.ep.M = M; gu.ep.N = f; gu.ep.out = act; gu.ep.ldo = f;
+    gu.scratch = g.scratch;
+    gu.scratch_bytes = g.scratch_bytes;
     TRY_HIP(STAGE(ST_GATEUP, gemm_launch(gu, s)));
 
     GemmCall dn{};
@@ -191,6 +212,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     dn.A = act; dn.lda = f; dn.M = M; dn.K = f;
     dn.w[0] = w.w2; dn.w_cols[0] = d;
     dn.ep.M = M; dn.ep.N = d; dn.ep.out = out; dn.ep.ldo = d; dn.ep.res = r; dn.ep.ldr = d; dn.ep.res_f32 = 1;
+    dn.scratch = g.scratch;
+    dn.scratch_bytes = g.scratch_bytes;
     TRY_HIP(STAGE(ST_W2, gemm_launch(dn, s)));
     return TFB_OK;
 }
@@ -393,6 +416,8 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
         hd.A = hn; hd.lda = d; hd.M = rows; hd.K = d;
         hd.w[0] = model->w_unembed; hd.w_cols[0] = V;
         hd.ep.M = rows; hd.ep.N = V; hd.ep.out = lg; hd.ep.ldo = V;
+        hd.scratch = L.skinny_bytes ? wsb + L.skinny : nullptr;
+        hd.scratch_bytes = L.skinny_bytes;
         TRY_HIP(STAGE(ST_LM_HEAD, gemm_launch(hd, s)));
         if (next_ids) {
             // Greedy next token from each sequence's last row ([PID] Under the hood, step 6).

@@ -397,8 +397,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
             const int j = base + 16 * t + ln;
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-                kr[t][s] = (j < k_end) ? *(const u32x4 *)(Kg + (int64_t)j * DH + (4 * s + g4) * 8)
-                                       : u32x4{0, 0, 0, 0};
+                kr[t][s] = (j < k_end) ? ld_stream(Kg + (int64_t)j * DH + (4 * s + g4) * 8) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -406,8 +405,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
             for (int r = 0; r < 8; ++r) {
                 // slots 0-3: keys 32u + 4g + v; slots 4-7: keys 32u + 16 + 4g + v
                 const int j = base + 32 * u + 16 * (r >> 2) + 4 * g4 + (r & 3);
-                vr[u][r] = (v_lane && j < k_end) ? *(const u32x4 *)(Vg + (int64_t)j * DH + ln * 8)
-                                                 : u32x4{0, 0, 0, 0};
+                vr[u][r] = (v_lane && j < k_end) ? ld_stream(Vg + (int64_t)j * DH + ln * 8) : u32x4{0, 0, 0, 0};
             }
         f32x4 sacc[4];
 #pragma unroll

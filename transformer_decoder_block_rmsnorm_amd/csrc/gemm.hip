@@ -315,6 +315,7 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
         }
         return hipGetLastError();
     }
+    if (c.M <= kSkinnyMaxM && c.scratch) return skinny_gemm_launch(c, c.scratch, c.scratch_bytes, s);
     switch (c.epi) {
         case EPI_QKV:
             g.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2];

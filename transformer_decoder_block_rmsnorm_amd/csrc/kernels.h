@@ -17,8 +17,14 @@ struct GemmCall {
     const void *w[3];      // QKV: wq, wk, wv; SWIGLU: w1, w3; else w[0]
     int w_cols[3];
     EpiParams ep;
+    void *scratch;         // split-K partials for skinny (decode) shapes, may be NULL
+    size_t scratch_bytes;
 };
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s);
+// Skinny (M <= 64) weight-streaming GEMM with split-K partials in `part`.
+constexpr int kSkinnyMaxM = 64;
+hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, hipStream_t s);
+size_t skinny_part_bytes(int M, int K, int N);
 
 // y[m] = x[m] * rsqrt(mean(x[m]^2) + eps) * g, rows of width d.
 // x_f32: the input rows are fp32 (the block-internal residual) whatever the storage type.
