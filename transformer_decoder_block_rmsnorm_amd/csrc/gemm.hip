@@ -219,6 +219,177 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g, EpiP
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 GEMM, second form: the weight tile stays N-contiguous in LDS (plain
+// 16-byte writes of the loaded row segments) and MFMA B fragments are read
+// with the gfx950 transpose load ds_read_b64_tr_b16.  Within each 16-lane
+// group that instruction hands lane j element (j % 4) of the 8-byte rows
+// addressed by lanes j/4 + 4i, i = 0..3; so lane s of a group points at
+// B[kb + s/4][n0 + 4 (s % 4)] and lane j receives B[kb + 0..3][n0 + j].
+// B rows are padded by 64 bytes so the four rows one group reads fall in
+// different LDS banks.  A tiles are as in the first form.
+// ---------------------------------------------------------------------------
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t *p) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(__attribute__((address_space(3))) void *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, EpiParams ep) {
+    constexpr int NT = WM * WN * 64;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int BROW = BN + 32;                 // padded B row (elements)
+    constexpr int A_CH = BM * BK / 8 / NT;        // 16-byte A chunks per thread
+    constexpr int B_CH = BK * BN / 8 / NT;        // 16-byte B chunks per thread
+    constexpr int STAGE = BM * BK + BK * BROW;    // elements per LDS stage
+    static_assert(BM * BK / 8 % NT == 0 && BK * BN / 8 % NT == 0, "tiles must split evenly");
+    static_assert(SRC != SRC_DUAL || TN % 2 == 0, "dual source needs gate/up tile pairs");
+
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+    auto As = [&](int b) { return lds + b * STAGE; };
+    auto Bs = [&](int b) { return lds + b * STAGE + BM * BK; };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(g, blockIdx.x, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const bf16_t *A = (const bf16_t *)g.A;
+    const bf16_t *a_ptr[A_CH];
+    int a_lds[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int id = tid + i * NT, row = id >> 3, ch = id & 7;
+        a_ptr[i] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + ch * 8;
+        a_lds[i] = row * BK + ((ch ^ (row & 7)) * 8);
+    }
+    const bf16_t *b_ptr[B_CH];
+    int b_ld[B_CH], b_lds[B_CH];
+    bool b_ok[B_CH];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+        const int id = tid + i * NT, row = id / (BN / 8), cc = id % (BN / 8);
+        const int c = n0 + cc * 8;
+        const bf16_t *base;
+        int ld, col;
+        if constexpr (SRC == SRC_ONE) {
+            base = (const bf16_t *)g.w[0]; ld = g.w_cols[0]; col = c;
+        } else if constexpr (SRC == SRC_CONCAT) {
+            int sidx = 0, c2 = c;
+            if (c2 >= g.w_cols[0]) { c2 -= g.w_cols[0]; sidx = 1; if (c2 >= g.w_cols[1]) { c2 -= g.w_cols[1]; sidx = 2; } }
+            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = c2;
+        } else {
+            const int sidx = (c >> 5) & 1;
+            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = 32 * (c >> 6) + (c & 31);
+        }
+        b_ok[i] = col < ld;
+        b_ld[i] = ld;
+        b_ptr[i] = base + (int64_t)row * ld + (b_ok[i] ? col : 0);
+        b_lds[i] = row * BROW + cc * 8;
+    }
+
+    u32x4 ra[A_CH], rb[B_CH];
+    auto load_global = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) ra[i] = *(const u32x4 *)(a_ptr[i] + kt * BK);
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i)
+            rb[i] = b_ok[i] ? *(const u32x4 *)(b_ptr[i] + (int64_t)kt * BK * b_ld[i]) : u32x4{0, 0, 0, 0};
+    };
+    auto store_lds = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) *(u32x4 *)(As(buf) + a_lds[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_CH; ++i) *(u32x4 *)(Bs(buf) + b_lds[i]) = rb[i];
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int KT = g.K / BK;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int q = lane >> 4, sl = lane & 15;     // 16-lane group and lane in it
+    // B fragment source of this lane: row offset sl/4 (+ 8*(q/2), +4 for the
+    // second half), columns 16*(q%2) + 4*(sl%4) within a 32-column tile
+    const int b_frag_off = ((q >> 1) * 8 + (sl >> 2)) * BROW + (q & 1) * 16 + (sl & 3) * 4;
+    load_global(0);
+    store_lds(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load_global(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int ch = ks * 2 + lh;
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WTM + i * 32 + lr;
+                af[i] = as_bf16x8(*(const u32x4 *)(As(buf) + row * BK + ((ch ^ (row & 7)) * 8)));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const bf16_t *p = Bs(buf) + ks * 16 * BROW + wn * WTN + j * 32 + b_frag_off;
+                const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * BROW);
+                bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+        if (kt + 1 < KT) store_lds(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue through LDS: per wave, one 32-row slice at a time is
+    // written as fp32 and read back as row-major column pairs
+    static_assert(WM * WN * 32 * WTN * 4 <= 2 * STAGE * 2, "epilogue staging must fit in the tile buffers");
+    float *stage = (float *)lds + wave * (32 * WTN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * WTN + j * 32 + lr] = acc[i][j][v];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row0 = m0 + wm * WTM + i * 32;
+        if constexpr (EPI == EPI_SWIGLU) {
+            // logical column u of this wave: gate at 64 (u/32) + u%32, up 32 further
+            constexpr int UW = WTN / 2;
+#pragma unroll
+            for (int r = 0; r < 32 * UW / 64; ++r) {
+                const int p = r * 64 + lane, rl = p / UW, u = p % UW;
+                const int cg = 64 * (u >> 5) + (u & 31);
+                epi_store_swiglu<bf16_t>(ep, row0 + rl, tn * (BN / 2) + wn * UW + u, stage[rl * WTN + cg],
+                                         stage[rl * WTN + cg + 32]);
+            }
+        } else {
+            constexpr int PW = WTN / 2;
+#pragma unroll
+            for (int r = 0; r < 32 * PW / 64; ++r) {
+                const int p = r * 64 + lane, rl = p / PW, cp = p % PW;
+                const float2 v = *(const float2 *)(stage + rl * WTN + 2 * cp);
+                epi_store_pair<EPI, bf16_t>(ep, row0 + rl, n0 + wn * WTN + 2 * cp, v.x, v.y);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // fp32 storage: 64x64 output tile per 256 threads, 16-wide k steps in LDS,
 // each thread computes a 4 (rows) x 4 (columns) patch.  SWIGLU computes the
 // gate and up dot products of each logical column side by side.
@@ -295,6 +466,17 @@ static hipError_t launch_bf16(GemmArgs g, const EpiParams &ep, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+static hipError_t launch_tr(GemmArgs g, const EpiParams &ep, hipStream_t s) {
+    g.tiles_m = (g.M + BM - 1) / BM;
+    g.tiles_n = (g.N + BN - 1) / BN;
+    g.group_m = 8;
+    const int blocks = g.tiles_m * g.tiles_n;
+    hipLaunchKernelGGL((gemm_bf16_tr_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s,
+                       g, ep);
+    return hipGetLastError();
+}
+
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
     GemmArgs g{};
     g.A = c.A;
@@ -316,19 +498,26 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
         return hipGetLastError();
     }
     if (c.M <= kSkinnyMaxM && c.scratch) return skinny_gemm_launch(c, c.scratch, c.scratch_bytes, s);
+    // large M: 256x256 tiles on 8 waves (128 x 64 each) when the launch still
+    // fills the chip, 128x128 tiles on 4 waves otherwise
+    const bool big = ((c.M + 255) / 256) * ((c.ep.N * (c.epi == EPI_SWIGLU ? 2 : 1) + 255) / 256) >= 256;
     switch (c.epi) {
         case EPI_QKV:
             g.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2];
-            return launch_bf16<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, s);
+            return big ? launch_tr<256, 256, 2, 4, SRC_CONCAT, EPI_QKV>(g, ep, s)
+                       : launch_tr<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, s);
         case EPI_RESID:
             g.N = c.w_cols[0];
-            return launch_bf16<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, s);
+            return big ? launch_tr<256, 256, 2, 4, SRC_ONE, EPI_RESID>(g, ep, s)
+                       : launch_tr<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, s);
         case EPI_SWIGLU:
             g.N = 2 * c.w_cols[0];
-            return launch_bf16<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, s);
+            return big ? launch_tr<256, 256, 2, 4, SRC_DUAL, EPI_SWIGLU>(g, ep, s)
+                       : launch_tr<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, s);
         case EPI_F32:
             g.N = c.w_cols[0];
-            return launch_bf16<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, s);
+            return big ? launch_tr<256, 256, 2, 4, SRC_ONE, EPI_F32>(g, ep, s)
+                       : launch_tr<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, s);
         default: return hipErrorInvalidValue;
     }
 }
