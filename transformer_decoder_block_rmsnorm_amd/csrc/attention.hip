@@ -191,8 +191,8 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
             for (int c = 0; c < 8; ++c) {
                 const int e = eb * 8 + c;
                 bf16_t *row = Vs(bf) + e * BKV;
-                *(u32x2 *)(row + (((p_lo >> 3) ^ (e & 7)) << 3) + (p_lo & 7)) = u32x2{t[c][0], t[c][1]};
-                *(u32x2 *)(row + (((p_hi >> 3) ^ (e & 7)) << 3) + (p_hi & 7)) = u32x2{t[c][2], t[c][3]};
+                *(u32x2 *)(row + (((p_lo >> 3) ^ swz_row(e)) << 3) + (p_lo & 7)) = u32x2{t[c][0], t[c][1]};
+                *(u32x2 *)(row + (((p_hi >> 3) ^ swz_row(e)) << 3) + (p_hi & 7)) = u32x2{t[c][2], t[c][3]};
             }
         }
     };
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
                     const bf16x8 vf =
-                        as_bf16x8(*(const u32x4 *)(Vs(bf) + e * BKV + (((2 * s2 + lh) ^ (e & 7)) * 8)));
+                        as_bf16x8(*(const u32x4 *)(Vs(bf) + e * BKV + (((2 * s2 + lh) ^ swz_row(e)) * 8)));
                     oacc[te] = mfma32(vf, pf[s2], oacc[te]);
                 }
             }

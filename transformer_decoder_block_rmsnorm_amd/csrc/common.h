@@ -76,6 +76,16 @@ __device__ __forceinline__ void transpose8x8_bf16(const u32x4 in[8], u32x4 out[8
     }
 }
 
+// LDS swizzles (XOR on 16-byte chunks / 32-byte granules), chosen so that
+// the fragment reads below hit distinct banks whether the LDS interleaves 32
+// or 64 four-byte banks:
+//  - rows of 128 bytes read as 16-byte chunks, one chunk column, 16
+//    consecutive rows at a time: chunk ^ swz_row(row);
+//  - rows read by ds_read_b64_tr_b16 (four consecutive rows of 32 bytes per
+//    16-lane group, two groups on adjacent granules): granule ^ swz_tr(row).
+__device__ __forceinline__ int swz_row(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_tr(int k) { return (0x6530 >> (4 * (k & 3))) & 0xF; }  // 0, 3, 5, 6
+
 // Swap with the neighbouring lane (l ^ 1) through DPP quad_perm [1,0,3,2].
 __device__ __forceinline__ float swap_lane_pair(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));

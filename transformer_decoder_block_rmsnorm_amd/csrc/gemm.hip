@@ -226,8 +226,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g, EpiP
 // group that instruction hands lane j element (j % 4) of the 8-byte rows
 // addressed by lanes j/4 + 4i, i = 0..3; so lane s of a group points at
 // B[kb + s/4][n0 + 4 (s % 4)] and lane j receives B[kb + 0..3][n0 + j].
-// B rows are padded by 64 bytes so the four rows one group reads fall in
-// different LDS banks.  A tiles are as in the first form.
+// B tiles are stored with their 32-byte granules XOR-swizzled by row
+// (swz_tr) so the four rows one group reads fall in different LDS banks; A
+// chunks are swizzled with swz_row.
 // ---------------------------------------------------------------------------
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, E
     constexpr int NT = WM * WN * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int BROW = BN + 32;                 // padded B row (elements)
+    constexpr int BROW = BN;                      // B row (elements), granules swizzled
     constexpr int A_CH = BM * BK / 8 / NT;        // 16-byte A chunks per thread
     constexpr int B_CH = BK * BN / 8 / NT;        // 16-byte B chunks per thread
     constexpr int STAGE = BM * BK + BK * BROW;    // elements per LDS stage
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, E
     for (int i = 0; i < A_CH; ++i) {
         const int id = tid + i * NT, row = id >> 3, ch = id & 7;
         a_ptr[i] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + ch * 8;
-        a_lds[i] = row * BK + ((ch ^ (row & 7)) * 8);
+        a_lds[i] = row * BK + ((ch ^ swz_row(row)) * 8);
     }
     const bf16_t *b_ptr[B_CH];
     int b_ld[B_CH], b_lds[B_CH];
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, E
         b_ok[i] = col < ld;
         b_ld[i] = ld;
         b_ptr[i] = base + (int64_t)row * ld + (b_ok[i] ? col : 0);
-        b_lds[i] = row * BROW + cc * 8;
+        b_lds[i] = row * BROW + (((cc >> 1) ^ swz_tr(row)) * 16) + (cc & 1) * 8;
     }
 
     u32x4 ra[A_CH], rb[B_CH];
@@ -319,9 +320,11 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, E
     const int KT = g.K / BK;
     const int lr = lane & 31, lh = lane >> 5;
     const int q = lane >> 4, sl = lane & 15;     // 16-lane group and lane in it
-    // B fragment source of this lane: row offset sl/4 (+ 8*(q/2), +4 for the
-    // second half), columns 16*(q%2) + 4*(sl%4) within a 32-column tile
-    const int b_frag_off = ((q >> 1) * 8 + (sl >> 2)) * BROW + (q & 1) * 16 + (sl & 3) * 4;
+    // B fragment source of this lane: row (q/2)*8 + sl/4 (+4 for the second
+    // half) of the 16-row slice, 16-column granule 2j + q%2 of the wave's
+    // columns, element 4*(sl%4) inside it; the granule is swizzled by row
+    const int b_row = (q >> 1) * 8 + (sl >> 2);
+    const int b_in = (sl & 3) * 4;
     load_global(0);
     store_lds(0);
     __syncthreads();
@@ -335,12 +338,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, E
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int row = wm * WTM + i * 32 + lr;
-                af[i] = as_bf16x8(*(const u32x4 *)(As(buf) + row * BK + ((ch ^ (row & 7)) * 8)));
+                af[i] = as_bf16x8(*(const u32x4 *)(As(buf) + row * BK + ((ch ^ swz_row(row)) * 8)));
             }
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const bf16_t *p = Bs(buf) + ks * 16 * BROW + wn * WTN + j * 32 + b_frag_off;
-                const u32x2 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * BROW);
+                const int gran = (wn * WTN + j * 32) / 16 + (q & 1);
+                const int r0 = ks * 16 + b_row, r1 = r0 + 4;
+                const u32x2 lo = lds_read_tr16(Bs(buf) + r0 * BROW + ((gran ^ swz_tr(r0)) * 16) + b_in);
+                const u32x2 hi = lds_read_tr16(Bs(buf) + r1 * BROW + ((gran ^ swz_tr(r1)) * 16) + b_in);
                 bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
 #pragma unroll
@@ -369,6 +374,192 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, E
         const int row0 = m0 + wm * WTM + i * 32;
         if constexpr (EPI == EPI_SWIGLU) {
             // logical column u of this wave: gate at 64 (u/32) + u%32, up 32 further
+            constexpr int UW = WTN / 2;
+#pragma unroll
+            for (int r = 0; r < 32 * UW / 64; ++r) {
+                const int p = r * 64 + lane, rl = p / UW, u = p % UW;
+                const int cg = 64 * (u >> 5) + (u & 31);
+                epi_store_swiglu<bf16_t>(ep, row0 + rl, tn * (BN / 2) + wn * UW + u, stage[rl * WTN + cg],
+                                         stage[rl * WTN + cg + 32]);
+            }
+        } else {
+            constexpr int PW = WTN / 2;
+#pragma unroll
+            for (int r = 0; r < 32 * PW / 64; ++r) {
+                const int p = r * 64 + lane, rl = p / PW, cp = p % PW;
+                const float2 v = *(const float2 *)(stage + rl * WTN + 2 * cp);
+                epi_store_pair<EPI, bf16_t>(ep, row0 + rl, n0 + wn * WTN + 2 * cp, v.x, v.y);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 GEMM, third form: operands go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane i of an instruction writes the i-th 16-byte
+// slot of a 1 KB block), through a ring of NST stages of BK = 32, so three
+// k steps of loads are in flight while one is multiplied.  Each lane fetches
+// the global chunk that belongs in its slot, which lays the tiles out already
+// swizzled: A rows (64 bytes, k contiguous) with chunk ^ ((row >> 2) & 3),
+// B rows (N contiguous) with 32-byte granules ^ swz_tr(row).  Fragments are
+// read as in the second form.  The waits are explicit: before a stage is
+// used, s_waitcnt vmcnt leaves only the younger stages outstanding, then a
+// barrier makes every wave's slots visible.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+// Issued as inline assembly so that the compiler neither tracks the LDS write
+// nor inserts its own vmcnt waits; callers order it with wait_vmcnt and a
+// barrier.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte_addr), "v"(gptr)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+__global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, EpiParams ep) {
+    constexpr int NW = WM * WN, NT = NW * 64;
+    constexpr int BKD = 32, NST = 4;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    constexpr int A_INS = BM * BKD * 2 / 1024 / NW;   // 1 KB A blocks per wave per stage
+    constexpr int B_INS = BKD * BN * 2 / 1024 / NW;
+    constexpr int A_ELEMS = BM * BKD, STAGE = BM * BKD + BKD * BN;  // elements
+    static_assert(A_INS * NW * 1024 == BM * BKD * 2 && B_INS * NW * 1024 == BKD * BN * 2, "tiles split in 1 KB blocks");
+    static_assert(BN / 16 >= 8, "granule swizzle needs 8 granules per row");
+    static_assert(SRC != SRC_DUAL || TN % 2 == 0, "dual source needs gate/up tile pairs");
+    static_assert(NW * 32 * WTN * 4 <= NST * STAGE * 2, "epilogue staging must fit");
+
+    __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;  // LDS byte address of the ring
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    int tm, tn;
+    tile_of(g, blockIdx.x, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- per-lane source of each 1 KB block this wave fills
+    const bf16_t *A = (const bf16_t *)g.A;
+    const bf16_t *a_src[A_INS];
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) {
+        const int slot = (wave * A_INS + j) * 64 + lane;
+        const int row = slot >> 2, p = slot & 3, c = p ^ ((row >> 2) & 3);
+        a_src[j] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + 8 * c;
+    }
+    const bf16_t *b_src[B_INS];
+    int b_ld[B_INS];
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+        const int slot = (wave * B_INS + j) * 64 + lane;
+        const int k = slot / (BN / 8), p = slot % (BN / 8);
+        const int gsw = (p >> 1) ^ swz_tr(k);
+        const int cglob = n0 + 16 * gsw + 8 * (p & 1);
+        const bf16_t *base;
+        int ld, col;
+        if constexpr (SRC == SRC_ONE) {
+            base = (const bf16_t *)g.w[0]; ld = g.w_cols[0]; col = cglob;
+        } else if constexpr (SRC == SRC_CONCAT) {
+            int sidx = 0, c2 = cglob;
+            if (c2 >= g.w_cols[0]) { c2 -= g.w_cols[0]; sidx = 1; if (c2 >= g.w_cols[1]) { c2 -= g.w_cols[1]; sidx = 2; } }
+            if (sidx == 2 && c2 >= g.w_cols[2]) c2 = g.w_cols[2] - 8;  // ragged tail: a valid, unused column
+            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = c2;
+        } else {
+            const int sidx = (cglob >> 5) & 1;
+            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = 32 * (cglob >> 6) + (cglob & 31);
+        }
+        if (col >= ld) col = ld - 8;  // ragged tail: a valid column whose outputs are never stored
+        b_ld[j] = ld;
+        b_src[j] = base + (int64_t)k * ld + col;
+    }
+    auto issue = [&](int kt, int stage) {
+        // LDS byte address of this wave's first block in the stage (wave-uniform)
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE * 2 + wave * A_INS * 1024);
+        const uint32_t stb = __builtin_amdgcn_readfirstlane(lds_base + stage * STAGE * 2 + A_ELEMS * 2 +
+                                                            wave * B_INS * 1024);
+#pragma unroll
+        for (int j = 0; j < A_INS; ++j) dma16(a_src[j] + kt * BKD, st + j * 1024);
+#pragma unroll
+        for (int j = 0; j < B_INS; ++j) dma16(b_src[j] + (int64_t)kt * BKD * b_ld[j], stb + j * 1024);
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int KT = g.K / BKD;
+    const int lr = lane & 31, lh = lane >> 5;
+    const int q = lane >> 4, sl = lane & 15;
+    const int b_row = (q >> 1) * 8 + (sl >> 2);
+    const int b_in = (sl & 3) * 4;
+    constexpr int PER = A_INS + B_INS;  // vmem instructions per stage per thread
+
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+        if (st < KT) issue(st, st);
+    for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 2 < KT) wait_vmcnt<2 * PER>();
+        else if (kt + 1 < KT) wait_vmcnt<PER>();
+        else wait_vmcnt<0>();
+        // every wave's slots of stage kt have landed, and every wave is done
+        // reading the stage about to be refilled
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are complete
+        asm volatile("s_barrier" ::: "memory");  // no LDS access moves across it
+        if (kt + NST - 1 < KT) issue(kt + NST - 1, (kt + NST - 1) % NST);
+        const bf16_t *As = lds + (kt % NST) * STAGE;
+        const bf16_t *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int ks = 0; ks < BKD / 16; ++ks) {
+            const int ch = ks * 2 + lh;
+            bf16x8 af[TM], bfr[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int row = wm * WTM + i * 32 + lr;
+                af[i] = as_bf16x8(*(const u32x4 *)(As + row * BKD + ((ch ^ ((row >> 2) & 3)) * 8)));
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int gran = (wn * WTN + j * 32) / 16 + (q & 1);
+                const int r0 = ks * 16 + b_row, r1 = r0 + 4;
+                const u32x2 lo = lds_read_tr16(Bs + r0 * BN + ((gran ^ swz_tr(r0)) * 16) + b_in);
+                const u32x2 hi = lds_read_tr16(Bs + r1 * BN + ((gran ^ swz_tr(r1)) * 16) + b_in);
+                bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave is done with the ring before it is reused for staging
+
+    float *stage = (float *)lds + wave * (32 * WTN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * WTN + j * 32 + lr] = acc[i][j][v];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row0 = m0 + wm * WTM + i * 32;
+        if constexpr (EPI == EPI_SWIGLU) {
             constexpr int UW = WTN / 2;
 #pragma unroll
             for (int r = 0; r < 32 * UW / 64; ++r) {
@@ -477,6 +668,17 @@ static hipError_t launch_tr(GemmArgs g, const EpiParams &ep, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, hipStream_t s) {
+    g.tiles_m = (g.M + BM - 1) / BM;
+    g.tiles_n = (g.N + BN - 1) / BN;
+    g.group_m = 8;
+    const int blocks = g.tiles_m * g.tiles_n;
+    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s,
+                       g, ep);
+    return hipGetLastError();
+}
+
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
     GemmArgs g{};
     g.A = c.A;
@@ -504,20 +706,20 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
     switch (c.epi) {
         case EPI_QKV:
             g.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2];
-            return big ? launch_tr<256, 256, 2, 4, SRC_CONCAT, EPI_QKV>(g, ep, s)
-                       : launch_tr<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_CONCAT, EPI_QKV>(g, ep, s)
+                       : launch_dma<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, s);
         case EPI_RESID:
             g.N = c.w_cols[0];
-            return big ? launch_tr<256, 256, 2, 4, SRC_ONE, EPI_RESID>(g, ep, s)
-                       : launch_tr<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_RESID>(g, ep, s)
+                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, s);
         case EPI_SWIGLU:
             g.N = 2 * c.w_cols[0];
-            return big ? launch_tr<256, 256, 2, 4, SRC_DUAL, EPI_SWIGLU>(g, ep, s)
-                       : launch_tr<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_DUAL, EPI_SWIGLU>(g, ep, s)
+                       : launch_dma<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, s);
         case EPI_F32:
             g.N = c.w_cols[0];
-            return big ? launch_tr<256, 256, 2, 4, SRC_ONE, EPI_F32>(g, ep, s)
-                       : launch_tr<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_F32>(g, ep, s)
+                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, s);
         default: return hipErrorInvalidValue;
     }
 }
