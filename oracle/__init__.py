@@ -37,7 +37,7 @@ def build(src: str | None = None, out: str | None = None, extra: list[str] | Non
 class _Cfg(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("gemm_bf16", ctypes.c_int32)]
 
 
 class _W(ctypes.Structure):
@@ -106,7 +106,10 @@ class Oracle:
 
     @staticmethod
     def _cfg(cfg) -> _Cfg:
-        return _Cfg(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d // cfg.n_heads, cfg.d_ff, cfg.rope_base, cfg.rms_eps)
+        # bf16 storage: GEMM operands are rounded to bf16 (tirogla "Transformer
+        # block", Implementation notes: bf16 GEMMs with fp32 accumulation)
+        return _Cfg(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d // cfg.n_heads, cfg.d_ff, cfg.rope_base, cfg.rms_eps,
+                    1 if cfg.dtype == "bf16" else 0)
 
     def _weights(self, w: dict):
         arrs = {n: self._f32(w[n]) for n in WEIGHT_NAMES}

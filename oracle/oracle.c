@@ -9,7 +9,13 @@
  * Precision: every value is fp32 and every sum runs in ascending index order,
  * as in the scalar block printed on tirogla "Transformer block" (section Code),
  * which computes in f32; that page's Implementation notes keep softmax and
- * norms in fp32.  Build with -ffp-contract=off so no multiply-add is fused.
+ * norms in fp32 and run the GEMMs on bf16 operands with fp32 accumulation.
+ * So with gemm_bf16 set (the bf16 storage configuration) each GEMM operand is
+ * rounded to bf16 (nearest, ties to even) where it is produced: the normed
+ * rows h and h2, q and k after RoPE, v, the attention output, the SwiGLU
+ * product, the block output passed between layers and the final-norm rows.
+ * Softmax probabilities and the residual inside a block stay fp32.
+ * Build with -ffp-contract=off so no multiply-add is fused.
  * OpenMP only splits independent outputs (matmul rows, attention query rows),
  * never a sum, so results are bitwise independent of the thread count.
  *
@@ -37,7 +43,26 @@
 typedef struct {
     int32_t d, n_heads, n_kv_heads, head_dim, d_ff;
     float rope_base, rms_eps;
+    int32_t gemm_bf16;  /* 1: GEMM operands rounded to bf16 (see Precision above) */
 } o_config;
+
+/* fp32 -> nearest bf16 value (ties to even), returned widened to fp32.  A bf16
+ * is the upper 16 bits of an fp32; NaN stays NaN. */
+static float bf16_round(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return x;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    u &= 0xFFFF0000u;
+    memcpy(&x, &u, 4);
+    return x;
+}
+
+/* Rounds n values in place when the configuration asks for bf16 operands. */
+static void operand_round(const o_config *cfg, float *v, int64_t n) {
+    if (!cfg->gemm_bf16) return;
+    for (int64_t i = 0; i < n; ++i) v[i] = bf16_round(v[i]);
+}
 
 typedef struct {
     const float *g_attn, *g_mlp; /* [d] RMSNorm gains */
@@ -223,6 +248,7 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
     float *k = (float *)malloc(sizeof(float) * M * kvd);
     float *v = (float *)malloc(sizeof(float) * M * kvd);
     o_rms_norm(x, w->g_attn, M, d, cfg->rms_eps, h);
+    operand_round(cfg, h, M * d);
     o_matmul(h, w->wk, M, d, kvd, k, cnt);
     o_matmul(h, w->wv, M, d, kvd, v, cnt);
 
@@ -250,6 +276,9 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
     /* RoPE on q and k only, never on v ([TIR] Pitfalls). */
     o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);
     o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);
+    operand_round(cfg, q, R * qd);
+    operand_round(cfg, k, M * kvd);
+    operand_round(cfg, v, M * kvd);
 
     /* Append post-RoPE k and v to the cache. */
     for (int b = 0; b < B; ++b)
@@ -295,6 +324,7 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
 
     /* Wo and the first residual: r = x + att.Wo ([TIR] How it works step 2). */
     float *a = (float *)malloc(sizeof(float) * R * d);
+    operand_round(cfg, att, R * qd);
     o_matmul(att, w->wo, R, qd, d, a, cnt);
     if (inter && inter->att) memcpy(inter->att, att, sizeof(float) * R * qd);
     free(att);
@@ -308,6 +338,7 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
      * ([TIR] How it works step 3; [MSA] 2. Transformer Block Anatomy). */
     float *h2 = (float *)malloc(sizeof(float) * R * d);
     o_rms_norm(r, w->g_mlp, R, d, cfg->rms_eps, h2);
+    operand_round(cfg, h2, R * d);
     float *gate = (float *)malloc(sizeof(float) * R * f);
     float *up = (float *)malloc(sizeof(float) * R * f);
     o_matmul(h2, w->w1, R, d, f, gate, cnt);
@@ -315,6 +346,7 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
     free(h2);
     for (int64_t i = 0; i < R * f; ++i) gate[i] = silu(gate[i]) * up[i];
     free(up);
+    operand_round(cfg, gate, R * f);
     if (inter && inter->act) memcpy(inter->act, gate, sizeof(float) * R * f);
     float *m = (float *)malloc(sizeof(float) * R * d);
     o_matmul(gate, w->w2, R, f, d, m, cnt);
@@ -383,12 +415,15 @@ int o_model_forward(const o_config *cfg, int n_layers, int vocab, const float *e
          * keys and values of every row to the next. */
         rc = o_block_forward(cfg, &layers[l], cos_tab, sin_tab, t_max_table, x, B, T, start, kcs[l], vcs[l], t_max,
                              last ? rows : NULL, last ? n_rows : T, y, NULL, cnt);
+        /* the block output is the next block's input activation */
+        operand_round(cfg, y, (last ? (int64_t)B * n_rows : M) * d);
         float *tmp = x; x = y; y = tmp;
     }
     if (rc == 0) {
         const int64_t R = (int64_t)B * n_rows;
         float *hn = (float *)malloc(sizeof(float) * R * d);
         o_rms_norm(x, g_final, R, d, cfg->rms_eps, hn);
+        operand_round(cfg, hn, R * d);
         o_matmul(hn, w_unembed, R, d, vocab, logits, cnt);
         free(hn);
         if (next_ids)

@@ -33,10 +33,24 @@ MUTANTS = {
     "cache_layout_b_g_swapped": ("int64_t dst = (((int64_t)b * Hkv + g) * t_max + p) * dh;",
                                  "int64_t dst = (((int64_t)g * B + b) * t_max + p) * dh;"),
     "matmul_transposed_operand": ("const float *wr = w + (int64_t)p * n;", "const float *wr = w + (int64_t)(k - 1 - p) * n;"),
+    # bf16 storage: a rounding of a GEMM operand dropped, misplaced or wrong
+    "bf16_att_not_rounded": ("    operand_round(cfg, att, R * qd);\n", ""),
+    "bf16_k_not_rounded": ("    operand_round(cfg, k, M * kvd);\n", ""),
+    "bf16_act_not_rounded": ("    operand_round(cfg, gate, R * f);", ""),
+    "bf16_q_rounded_before_rope": (
+        "    o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);\n    o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);\n"
+        "    operand_round(cfg, q, R * qd);\n",
+        "    operand_round(cfg, q, R * qd);\n    o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);\n"
+        "    o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);\n"),
+    "bf16_round_truncates": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
+    "bf16_layer_output_not_rounded": ("operand_round(cfg, y, (last ? (int64_t)B * n_rows : M) * d);", ""),
+    "bf16_final_norm_not_rounded": ("operand_round(cfg, hn, R * d);", ""),
 }
 
 PINS = [
     P.test_block_matches_fp64_library_composition,
+    P.test_bf16_operands_match_fp64_composition,
+    P.test_bf16_model_matches_fp64_composition,
     P.test_decode_matches_fp64_library_composition,
     P.test_decode_equals_prefill_bitwise,
     P.test_gqa_equals_mha_with_repeated_kv_bitwise,

@@ -24,14 +24,22 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")
 # --------------------------------------------------------------------------
 # An independent fp64 composition out of PyTorch library routines (rms_norm,
 # matmul, complex rotation, scaled_dot_product_attention with is_causal, silu).
+# With bf16=True every GEMM operand is rounded to bf16 by torch's own
+# conversion where the pages' precision rule puts it ([TIR] Implementation
+# notes: bf16 GEMMs with fp32 accumulation, softmax and norms in fp32).
 # --------------------------------------------------------------------------
-def torch_block_f64(cfg, w, x, start=0):
+def _bf16(a):
+    return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def torch_block_f64(cfg, w, x, start=0, bf16=False):
     d, H, Hkv = cfg.d, cfg.n_heads, cfg.n_kv_heads
     dh = d // H
+    rb = _bf16 if bf16 else (lambda a: a)
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
     X = t(x)
     B, T, _ = X.shape
-    h = F.rms_norm(X, (d,), weight=t(w["g_attn"]), eps=cfg.rms_eps)
+    h = rb(F.rms_norm(X, (d,), weight=t(w["g_attn"]), eps=cfg.rms_eps))
     q = (h @ t(w["wq"])).reshape(B, T, H, dh)
     k = (h @ t(w["wk"])).reshape(B, T, Hkv, dh)
     v = (h @ t(w["wv"])).reshape(B, T, Hkv, dh)
@@ -43,15 +51,15 @@ def torch_block_f64(cfg, w, x, start=0):
         c = torch.view_as_complex(a.reshape(*a.shape[:-1], dh // 2, 2).contiguous())
         return torch.view_as_real(c * rot[None, :, None, :]).reshape(a.shape)
 
-    q, k = rope(q), rope(k)
+    q, k, v = rb(rope(q)), rb(rope(k)), rb(v)
     g = H // Hkv
     K = k.repeat_interleave(g, dim=2).transpose(1, 2)
     V = v.repeat_interleave(g, dim=2).transpose(1, 2)
     o = F.scaled_dot_product_attention(q.transpose(1, 2), K, V, is_causal=True)
-    o = o.transpose(1, 2).reshape(B, T, H * dh)
+    o = rb(o.transpose(1, 2).reshape(B, T, H * dh))
     r = X + o @ t(w["wo"])
-    h2 = F.rms_norm(r, (d,), weight=t(w["g_mlp"]), eps=cfg.rms_eps)
-    act = F.silu(h2 @ t(w["w1"])) * (h2 @ t(w["w3"]))
+    h2 = rb(F.rms_norm(r, (d,), weight=t(w["g_mlp"]), eps=cfg.rms_eps))
+    act = rb(F.silu(h2 @ t(w["w1"])) * (h2 @ t(w["w3"])))
     return (r + act @ t(w["w2"])).numpy(), {"q": q.reshape(B, T, H * dh).numpy(), "att": o.numpy(),
                                             "r": r.numpy(), "act": act.numpy()}
 
@@ -65,14 +73,14 @@ TINY_SHAPES = [
 ]
 
 
-def _run_pins_vs_torch(orc, shapes=TINY_SHAPES, gains="random"):
+def _run_pins_vs_torch(orc, shapes=TINY_SHAPES, gains="random", dtype="f32"):
     worst = 0.0
     for i, s in enumerate(shapes):
-        cfg = small_cfg(d=s["d"], H=s["H"], Hkv=s["Hkv"], f=s["f"], number=40 + i)
+        cfg = small_cfg(d=s["d"], H=s["H"], Hkv=s["Hkv"], f=s["f"], number=40 + i, dtype=dtype)
         w, _ = block_weights(cfg, gains=gains)
         x, _ = activations(cfg, 2, s["T"])
         got, inter = orc.block_forward(cfg, w, x, intermediates=True)
-        ref, rint = torch_block_f64(cfg, w, x)
+        ref, rint = torch_block_f64(cfg, w, x, bf16=dtype == "bf16")
         worst = max(worst, rel_err(got, ref))
         for key in ("q", "att", "r", "act"):
             worst = max(worst, rel_err(inter[key], rint[key]))
@@ -83,6 +91,55 @@ def test_block_matches_fp64_library_composition(oracle):
     """Every step at once, against library routines in fp64 ([TIR] How it works)."""
     assert _run_pins_vs_torch(oracle) <= 1e-5
     assert _run_pins_vs_torch(oracle, gains="ones") <= 1e-5
+
+
+def _bf16_gap(got, ref):
+    """(largest gap, number of values) between two arrays of bf16 values that
+    are not bitwise equal: 1 means neighbouring bf16 values, more is a real
+    difference."""
+    a = np.asarray(got, np.float32).view(np.uint32).astype(np.int64)
+    b = np.asarray(ref, np.float64).astype(np.float32).view(np.uint32).astype(np.int64)
+    assert not np.any((a | b) & 0xFFFF), "operands must be bf16 values"
+    diff = np.abs((a >> 16) - (b >> 16))
+    diff[(a >> 31) != (b >> 31)] = 1 << 16  # sign differs
+    return int(diff.max(initial=0)), int(np.count_nonzero(diff))
+
+
+def test_bf16_operands_match_fp64_composition(oracle):
+    """bf16 storage: the oracle rounds each GEMM operand to bf16 and nothing
+    else ([TIR] Implementation notes).  Against the fp64 composition that rounds
+    at the same places with torch's conversion, the only gap is fp32 vs fp64
+    arithmetic: the output agrees to 1e-5 rms, and each rounded operand (q, att,
+    act) is bitwise equal except where a value fell so close to a rounding
+    boundary that the two sides picked neighbouring bf16 values (rare).  A
+    dropped or misplaced rounding leaves non-bf16 values or moves many values."""
+    for gains in ("random", "ones"):
+        for i, s in enumerate(TINY_SHAPES):
+            cfg = small_cfg(d=s["d"], H=s["H"], Hkv=s["Hkv"], f=s["f"], number=40 + i, dtype="bf16")
+            w, _ = block_weights(cfg, gains=gains)
+            x, _ = activations(cfg, 2, s["T"])
+            got, inter = oracle.block_forward(cfg, w, x, intermediates=True)
+            ref, rint = torch_block_f64(cfg, w, x, bf16=True)
+            assert rel_err(got, ref) <= 1e-5
+            assert rel_err(inter["r"], rint["r"]) <= 1e-5
+            for key in ("q", "att", "act"):
+                gap, n = _bf16_gap(inter[key], rint[key])
+                assert gap <= 1 and n <= max(2, inter[key].size // 500), (key, gap, n)
+
+
+def test_bf16_operands_are_bf16_values(oracle):
+    """The GEMM operands the oracle hands on are bf16 values (the low 16 bits of
+    their fp32 patterns are zero); the residual inside the block is not rounded."""
+    cfg = small_cfg(d=64, H=4, Hkv=2, f=192, number=47, dtype="bf16")
+    w, _ = block_weights(cfg, gains="random")
+    x, _ = activations(cfg, 2, 16)
+    _, inter = oracle.block_forward(cfg, w, x, intermediates=True)
+    for key in ("q", "att", "act"):
+        assert not np.any(inter[key].view(np.uint32) & 0xFFFF), key
+    assert np.any(inter["r"].view(np.uint32) & 0xFFFF)
+    # the fp32 storage configuration rounds nothing
+    _, i32 = oracle.block_forward(cfg.with_(dtype="f32"), w, x, intermediates=True)
+    assert np.any(i32["act"].view(np.uint32) & 0xFFFF)
 
 
 def test_decode_matches_fp64_library_composition(oracle):
@@ -309,6 +366,28 @@ def test_model_matches_fp64_composition(oracle):
     ref = hn @ wu.astype(np.float64)
     assert rel_err(logits, ref) <= 1e-5
     assert np.array_equal(nxt, np.argmax(logits[:, -1], axis=-1))
+
+
+def test_bf16_model_matches_fp64_composition(oracle):
+    """bf16 storage: block outputs handed to the next block and the final-norm
+    rows are bf16 operands too ([TIR] Implementation notes)."""
+    cfg = small_cfg(number=73, dtype="bf16")
+    L, V, T = 2, 40, 7
+    import synth
+    layers = [block_weights(cfg, layer=l, gains="random")[0] for l in range(L)]
+    emb, _ = synth.normal(cfg.seed, 15, (V, cfg.d), 1.0, True)
+    wu, _ = synth.normal(cfg.seed, 17, (cfg.d, V), 0.1, True)
+    gf = synth.to_bf16(1.0 + synth.normal(cfg.seed, 16, (cfg.d,), 0.1, False)[0])[1]
+    ids = synth.integers(cfg.seed, 14, (2, T), 0, V - 1)
+    kcs = [np.zeros((2, cfg.n_kv_heads, T, cfg.head_dim), np.float32) for _ in range(L)]
+    vcs = [a.copy() for a in kcs]
+    logits, _ = oracle.model_forward(cfg, L, V, emb, layers, gf, wu, ids, kcs, vcs)
+    x = torch.from_numpy(emb[ids].astype(np.float64))
+    for l in range(L):
+        x = _bf16(torch.from_numpy(torch_block_f64(cfg, layers[l], x.numpy(), bf16=True)[0]))
+    hn = _bf16(F.rms_norm(x, (cfg.d,), weight=torch.from_numpy(gf.astype(np.float64)), eps=cfg.rms_eps))
+    ref = (hn @ torch.from_numpy(wu.astype(np.float64))).numpy()
+    assert rel_err(logits, ref) <= 1e-5
 
 
 def test_argmax_ties_take_lowest_index(oracle):
