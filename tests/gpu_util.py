@@ -42,6 +42,28 @@ def tol(cfg) -> float:
     return BF16_TOL if cfg.dtype == "bf16" else F32_TOL
 
 
+# Allowance for a value that is itself stored in bf16, as a fraction of its
+# magnitude.  Half a unit in the last place (2^-8 |v|) when the reference is
+# fp32 (the block output); one unit (2^-7 |v|) when the reference is also a
+# bf16 value (cache rows: both sides round a nearly equal fp32 value, and one
+# lying next to a rounding boundary may land on neighbouring bf16 values).
+HALF_ULP = 2.0 ** -8
+ONE_ULP = 2.0 ** -7
+
+
+def stored_ok(got, ref, tol_rms: float, ulp_frac: float) -> bool:
+    """|got - ref| <= tol_rms * rms(ref) + ulp_frac * |ref| for every value."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    r = np.sqrt(np.mean(ref * ref))
+    return bool(np.all(np.abs(got - ref) <= tol_rms * r + ulp_frac * np.abs(ref)))
+
+
+def cache_ok(cfg, got, ref) -> bool:
+    """Cache rows: the stated bound, plus one bf16 unit for bf16 storage."""
+    return stored_ok(got, ref, tol(cfg), ONE_ULP if cfg.dtype == "bf16" else 0.0)
+
+
 def new_cache(cfg, B, t_max, fill=float("nan")):
     import torch
     k = torch.full((B, cfg.n_kv_heads, t_max, cfg.d // cfg.n_heads), fill, dtype=torch_dtype(cfg), device="cuda")
@@ -50,3 +72,20 @@ def new_cache(cfg, B, t_max, fill=float("nan")):
 
 def widen_cache(t) -> np.ndarray:
     return np.ascontiguousarray(to_np(t), dtype=np.float32)
+
+
+def logits_ok(cfg, got, ref) -> bool:
+    """Model logits.  fp32 storage: the stated bound.  bf16 storage: a logit is
+    a contraction over the whole final hidden state, so it carries the
+    bf16-operand noise of all d hidden values (and of every block before
+    them); that noise is near-Gaussian across logits, so the bound is on its
+    rms, rms(got - ref) <= 2e-2 rms(ref), and on its largest value at the
+    Gaussian extreme for ~10^5 draws, 5 x 2e-2 rms(ref).  A wiring mistake
+    (wrong layer, row, vocabulary column or norm) moves logits by O(rms)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    r = np.sqrt(np.mean(ref * ref))
+    if cfg.dtype != "bf16":
+        return bool(np.max(np.abs(got - ref)) <= F32_TOL * r)
+    e = got - ref
+    return bool(np.sqrt(np.mean(e * e)) <= BF16_TOL * r and np.max(np.abs(e)) <= 5 * BF16_TOL * r)

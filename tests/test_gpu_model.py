@@ -1,0 +1,122 @@
+"""GPU parity of the model path (embedding, L blocks, final RMSNorm, untied LM
+head, greedy next token) against the CPU oracle, in prefill and decode.
+
+Decode steps are teacher-forced: the token fed at each step is the GPU's own
+greedy choice, and the oracle is given the same ids, so a near-tie argmax
+cannot make the two sides diverge."""
+import numpy as np
+import pytest
+
+import synth
+from synth.configs import tensor_id
+from tests.conftest import gpu_available
+from tests.gpu_util import cache_ok, dev_weights, logits_ok, to_dev, to_np
+from tests.inputs import rel_err, small_cfg
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+import transformer_decoder_block_rmsnorm_amd as tfb  # noqa: E402
+
+
+def model_inputs(cfg, L, V):
+    bf = cfg.dtype == "bf16"
+    layers32, layers = [], []
+    for l in range(L):
+        w32, w = dev_weights(cfg, layer=l, gains="random")
+        layers32.append(w32)
+        layers.append(w)
+    emb32, embb = synth.normal(cfg.seed, tensor_id("embed"), (V, cfg.d), 1.0, bf)
+    wu32, wub = synth.normal(cfg.seed, tensor_id("w_unembed"), (cfg.d, V), 0.02, bf)
+    gf = 1.0 + synth.normal(cfg.seed, tensor_id("g_final"), (cfg.d,), 0.1, False)[0]
+    if bf:
+        gfb, gf32 = synth.to_bf16(gf)
+    else:
+        gfb, gf32 = None, gf.astype(np.float32)
+    return (layers32, emb32, gf32, wu32), (layers, to_dev(emb32, embb), to_dev(gf32, gfb), to_dev(wu32, wub))
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv,f,L,V,B,T,steps", [
+    ("f32", 64, 4, 2, 192, 2, 100, 2, 12, 3),
+    ("bf16", 512, 4, 2, 1024, 2, 1024, 2, 40, 3),
+    ("bf16", 256, 2, 1, 512, 3, 512, 3, 70, 2),
+])
+def test_model_prefill_then_greedy_decode(oracle, dtype, d, H, Hkv, f, L, V, B, T, steps):
+    import torch
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=f, dtype=dtype, base=500000.0, number=95)
+    print("case: model", dtype, d, L, V, B, T, steps, flush=True)
+    (l32, e32, g32, u32), (ld, ed, gd, ud) = model_inputs(cfg, L, V)
+    tc = tfb.Config.of(cfg)
+    h = tfb.ModelHandle(tc, ld, ed, gd, ud)
+    t_max = T + steps + 2
+    dh = d // H
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    caches = [(torch.full((B, Hkv, t_max, dh), float("nan"), dtype=tdt, device="cuda"),
+               torch.full((B, Hkv, t_max, dh), float("nan"), dtype=tdt, device="cuda")) for _ in range(L)]
+    rope = tfb.rope_table_init(tc, t_max)
+    ids = synth.integers(cfg.seed, tensor_id("ids"), (B, T), 0, V - 1)
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    logits = torch.empty((B, T, V), dtype=torch.float32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    tfb.model_forward(h, rope, torch.from_numpy(ids).cuda(), caches, lens, 0, logits=logits, next_ids=nxt)
+    torch.cuda.synchronize()
+    okc = [np.full((B, Hkv, t_max, dh), np.nan, np.float32) for _ in range(L)]
+    ovc = [a.copy() for a in okc]
+    ref, ref_next = oracle.model_forward(cfg, L, V, e32, l32, g32, u32, ids, okc, ovc)
+    got = logits.cpu().numpy()
+    assert logits_ok(cfg, got, ref), rel_err(got, ref)
+    g_next = nxt.cpu().numpy()
+    assert np.array_equal(g_next, np.argmax(got[:, -1], axis=-1))
+    assert lens.cpu().numpy().tolist() == [T] * B
+    # every layer's cache rows 0..T-1 hold the oracle's keys; rows beyond stay NaN
+    for l in range(L):
+        gk = to_np(caches[l][0])
+        assert cache_ok(cfg, gk[:, :, :T], okc[l][:, :, :T])
+        assert np.isnan(gk[:, :, T:]).all()
+
+    cur = g_next.copy()
+    for s in range(steps):
+        pos = T + s
+        ids1 = cur.reshape(B, 1).astype(np.int32)
+        lg1 = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
+        tfb.model_forward(h, rope, torch.from_numpy(ids1).cuda(), caches, lens, pos, logits=lg1, next_ids=nxt)
+        torch.cuda.synchronize()
+        r1, _ = oracle.model_forward(cfg, L, V, e32, l32, g32, u32, ids1, okc, ovc,
+                                     start=np.full(B, pos, np.int32))
+        g1 = lg1.cpu().numpy()
+        assert logits_ok(cfg, g1, r1), (s, rel_err(g1, r1))
+        cur = nxt.cpu().numpy()
+        assert np.array_equal(cur, np.argmax(g1[:, -1], axis=-1))
+        assert lens.cpu().numpy().tolist() == [pos + 1] * B
+
+
+def test_model_last_only_and_next_ids_only(oracle):
+    import torch
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=96)
+    L, V, B, T = 2, 1024, 2, 33
+    (l32, e32, g32, u32), (ld, ed, gd, ud) = model_inputs(cfg, L, V)
+    tc = tfb.Config.of(cfg)
+    h = tfb.ModelHandle(tc, ld, ed, gd, ud)
+    dh = cfg.d // cfg.n_heads
+    ids = synth.integers(cfg.seed, tensor_id("ids"), (B, T), 0, V - 1)
+    okc = [np.zeros((B, cfg.n_kv_heads, T, dh), np.float32) for _ in range(L)]
+    ovc = [a.copy() for a in okc]
+    ref, ref_next = oracle.model_forward(cfg, L, V, e32, l32, g32, u32, ids, okc, ovc, rows=[T - 1])
+    for mode in ("last_only", "next_only"):
+        caches = [(torch.zeros((B, cfg.n_kv_heads, T, dh), dtype=torch.bfloat16, device="cuda"),
+                   torch.zeros((B, cfg.n_kv_heads, T, dh), dtype=torch.bfloat16, device="cuda")) for _ in range(L)]
+        rope = tfb.rope_table_init(tc, T)
+        lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+        nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+        lg = torch.empty((B, 1, V), dtype=torch.float32, device="cuda") if mode == "last_only" else None
+        tfb.model_forward(h, rope, torch.from_numpy(ids).cuda(), caches, lens, 0, logits=lg, last_only=True,
+                          next_ids=nxt)
+        torch.cuda.synchronize()
+        if lg is not None:
+            got = lg.cpu().numpy()
+            assert logits_ok(cfg, got, ref), rel_err(got, ref)
+            assert np.array_equal(nxt.cpu().numpy(), np.argmax(got[:, -1], axis=-1))
+        # the oracle's greedy choice agrees unless its top two logits nearly tie
+        top2 = np.sort(ref[:, -1], axis=-1)[:, -2:]
+        margin = (top2[:, 1] - top2[:, 0]) / np.sqrt(np.mean(ref ** 2))
+        agree = nxt.cpu().numpy() == ref_next
+        assert np.all(agree | (margin < 0.05))

@@ -2,13 +2,12 @@
 // (tirogla "Transformer block", Code: weights are kept [in, out] and applied
 // as y = x W).
 //
-// bf16: MFMA 32x32x16 tiles, fp32 accumulation.  Both operands are staged in
-// LDS as [rows][64 k] with k contiguous and the eight 16-byte chunks of a row
-// XOR-swizzled by (row & 7), so fragment reads of 32 consecutive rows are
-// bank-conflict free.  The weight tile arrives N-contiguous; each thread
-// loads an 8x8 block and transposes it in registers (byte permutes) before
-// writing it k-contiguous.  One barrier per 64-wide k step, LDS double
-// buffered, next tile's global loads in flight during the current MFMAs.
+// bf16 (large M): MFMA 32x32x16 tiles with fp32 accumulation.  Operands go
+// from global memory straight into LDS through a ring of k stages; the A
+// fragments are plain 16-byte LDS reads, the weight fragments come from the
+// N-contiguous weight tile through the gfx950 transpose read
+// ds_read_b64_tr_b16, so no operand is transposed in registers.  Small M
+// (decode) goes to the split-K weight-streaming kernel in skinny.hip.
 //
 // Fused epilogues (epilogue.h): RoPE + KV-cache scatter for the fused QKV
 // projection, residual add for Wo and W2, SiLU(gate) * up for the fused
@@ -40,8 +39,6 @@ struct GemmArgs {
     int tiles_m, tiles_n, group_m;
 };
 
-constexpr int BK = 64;
-
 // Logical tile (tm, tn) of workgroup `bid`.  Workgroups are dealt to the 8
 // XCDs round robin; the remap gives each XCD a contiguous run of logical
 // tiles, and the run is ordered in groups of `group_m` row panels so that the
@@ -59,177 +56,11 @@ __device__ __forceinline__ void tile_of(const GemmArgs &g, int bid, int &tm, int
     tn = r / gm;
 }
 
-template <int BM, int BN, int WM, int WN, int SRC, int EPI>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_kernel(GemmArgs g, EpiParams ep) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-    constexpr int TM = WTM / 32, TN = WTN / 32;  // MFMA tiles per wave
-    constexpr int A_CH = BM * BK / 8 / NT;       // 16-byte A chunks per thread
-    constexpr int B_BLK = (BK / 8) * (BN / 8);   // 8x8 weight blocks per tile
-    constexpr int B_PER = (B_BLK + NT - 1) / NT;
-    static_assert(BM * BK / 8 % NT == 0, "A tile must split evenly");
-    static_assert(SRC != SRC_DUAL || TN % 2 == 0, "dual source needs gate/up tile pairs");
-
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * BK];
-    // buffer b: A tile at lds + b*(BM+BN)*BK, B tile right after it
-    auto As = [&](int b) { return lds + b * (BM + BN) * BK; };
-    auto Bs = [&](int b) { return lds + b * (BM + BN) * BK + BM * BK; };
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_of(g, blockIdx.x, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    // ---- A source rows (clamped: rows >= M compute garbage that is never stored)
-    const bf16_t *A = (const bf16_t *)g.A;
-    const bf16_t *a_ptr[A_CH];
-    int a_lds[A_CH];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        int id = tid + i * NT;
-        int row = id >> 3, ch = id & 7;
-        int gr = min(m0 + row, g.M - 1);
-        a_ptr[i] = A + (int64_t)gr * g.lda + ch * 8;
-        a_lds[i] = row * BK + ((ch ^ (row & 7)) * 8);
-    }
-    // ---- B source columns: each thread owns B_PER 8(k) x 8(n) blocks
-    const bf16_t *b_ptr[B_PER];
-    int b_ld[B_PER], b_nb[B_PER], b_kb[B_PER];
-    bool b_ok[B_PER];
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-        int id = tid + i * NT;
-        b_ok[i] = id < B_BLK;
-        int nb = id % (BN / 8), kb = id / (BN / 8);
-        b_nb[i] = nb;
-        b_kb[i] = kb;
-        int c = n0 + nb * 8;  // column within this launch's B
-        const bf16_t *base;
-        int ld, col;
-        if constexpr (SRC == SRC_ONE) {
-            base = (const bf16_t *)g.w[0]; ld = g.w_cols[0]; col = c;
-        } else if constexpr (SRC == SRC_CONCAT) {
-            int s = 0, cc = c;
-            if (cc >= g.w_cols[0]) { cc -= g.w_cols[0]; s = 1; if (cc >= g.w_cols[1]) { cc -= g.w_cols[1]; s = 2; } }
-            base = (const bf16_t *)g.w[s]; ld = g.w_cols[s]; col = cc;
-        } else {
-            int s = (c >> 5) & 1;
-            base = (const bf16_t *)g.w[s]; ld = g.w_cols[s]; col = 32 * (c >> 6) + (c & 31);
-        }
-        if (col >= ld) b_ok[i] = false;  // ragged last tile: zero fill
-        b_ld[i] = ld;
-        b_ptr[i] = base + (int64_t)(kb * 8) * ld + (b_ok[i] ? col : 0);
-    }
-
-    u32x4 ra[A_CH], rb[B_PER][8];
-    auto load_global = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) ra[i] = *(const u32x4 *)(a_ptr[i] + kt * BK);
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            if (b_ok[i]) {
-                const bf16_t *p = b_ptr[i] + (int64_t)kt * BK * b_ld[i];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) rb[i][r] = *(const u32x4 *)(p + (int64_t)r * b_ld[i]);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) rb[i][r] = u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) *(u32x4 *)(As(buf) + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) {
-            if (tid + i * NT < B_BLK) {
-                u32x4 t[8];
-                transpose8x8_bf16(rb[i], t);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    int n = b_nb[i] * 8 + j;
-                    *(u32x4 *)(Bs(buf) + n * BK + ((b_kb[i] ^ (n & 7)) * 8)) = t[j];
-                }
-            }
-        }
-    };
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    const int KT = g.K / BK;
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    const int lr = lane & 31, lh = lane >> 5;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) load_global(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ks * 2 + lh;
-            bf16x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                int row = wm * WTM + i * 32 + lr;
-                af[i] = as_bf16x8(*(const u32x4 *)(As(buf) + row * BK + ((ch ^ (row & 7)) * 8)));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                int n = wn * WTN + j * 32 + lr;
-                bfr[j] = as_bf16x8(*(const u32x4 *)(Bs(buf) + n * BK + ((ch ^ (n & 7)) * 8)));
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-        }
-        if (kt + 1 < KT) store_lds(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue straight from the accumulator layout
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            if constexpr (EPI == EPI_SWIGLU) {
-                if (j & 1) continue;
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                if constexpr (EPI == EPI_SWIGLU) {
-                    const int col = tn * (BN / 2) + wn * (WTN / 2) + 16 * j + lr;
-                    epi_store_swiglu<bf16_t>(ep, row, col, acc[i][j][v], acc[i][j + 1][v]);
-                } else {
-                    const int col = n0 + wn * WTN + j * 32 + lr;
-                    float mine = acc[i][j][v];
-                    float other = swap_lane_pair(mine);
-                    if ((lr & 1) == 0) epi_store_pair<EPI, bf16_t>(ep, row, col, mine, other);
-                }
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 GEMM, second form: the weight tile stays N-contiguous in LDS (plain
-// 16-byte writes of the loaded row segments) and MFMA B fragments are read
-// with the gfx950 transpose load ds_read_b64_tr_b16.  Within each 16-lane
-// group that instruction hands lane j element (j % 4) of the 8-byte rows
-// addressed by lanes j/4 + 4i, i = 0..3; so lane s of a group points at
-// B[kb + s/4][n0 + 4 (s % 4)] and lane j receives B[kb + 0..3][n0 + j].
-// B tiles are stored with their 32-byte granules XOR-swizzled by row
-// (swz_tr) so the four rows one group reads fall in different LDS banks; A
-// chunks are swizzled with swz_row.
-// ---------------------------------------------------------------------------
+// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
+// (j % 4) of the 8-byte rows addressed by lanes j/4 + 4i, i = 0..3.  So when
+// lane s of a group points at B[kb + s/4][n0 + 4 (s % 4)], lane j receives
+// B[kb + 0..3][n0 + j]: four consecutive k values of column n0 + j, the
+// layout of an MFMA B fragment.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -238,174 +69,17 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-template <int BM, int BN, int WM, int WN, int SRC, int EPI>
-__global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_tr_kernel(GemmArgs g, EpiParams ep) {
-    constexpr int NT = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 32, TN = WTN / 32;
-    constexpr int BROW = BN;                      // B row (elements), granules swizzled
-    constexpr int A_CH = BM * BK / 8 / NT;        // 16-byte A chunks per thread
-    constexpr int B_CH = BK * BN / 8 / NT;        // 16-byte B chunks per thread
-    constexpr int STAGE = BM * BK + BK * BROW;    // elements per LDS stage
-    static_assert(BM * BK / 8 % NT == 0 && BK * BN / 8 % NT == 0, "tiles must split evenly");
-    static_assert(SRC != SRC_DUAL || TN % 2 == 0, "dual source needs gate/up tile pairs");
-
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
-    auto As = [&](int b) { return lds + b * STAGE; };
-    auto Bs = [&](int b) { return lds + b * STAGE + BM * BK; };
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_of(g, blockIdx.x, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const bf16_t *A = (const bf16_t *)g.A;
-    const bf16_t *a_ptr[A_CH];
-    int a_lds[A_CH];
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-        const int id = tid + i * NT, row = id >> 3, ch = id & 7;
-        a_ptr[i] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + ch * 8;
-        a_lds[i] = row * BK + ((ch ^ swz_row(row)) * 8);
-    }
-    const bf16_t *b_ptr[B_CH];
-    int b_ld[B_CH], b_lds[B_CH];
-    bool b_ok[B_CH];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-        const int id = tid + i * NT, row = id / (BN / 8), cc = id % (BN / 8);
-        const int c = n0 + cc * 8;
-        const bf16_t *base;
-        int ld, col;
-        if constexpr (SRC == SRC_ONE) {
-            base = (const bf16_t *)g.w[0]; ld = g.w_cols[0]; col = c;
-        } else if constexpr (SRC == SRC_CONCAT) {
-            int sidx = 0, c2 = c;
-            if (c2 >= g.w_cols[0]) { c2 -= g.w_cols[0]; sidx = 1; if (c2 >= g.w_cols[1]) { c2 -= g.w_cols[1]; sidx = 2; } }
-            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = c2;
-        } else {
-            const int sidx = (c >> 5) & 1;
-            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = 32 * (c >> 6) + (c & 31);
-        }
-        b_ok[i] = col < ld;
-        b_ld[i] = ld;
-        b_ptr[i] = base + (int64_t)row * ld + (b_ok[i] ? col : 0);
-        b_lds[i] = row * BROW + (((cc >> 1) ^ swz_tr(row)) * 16) + (cc & 1) * 8;
-    }
-
-    u32x4 ra[A_CH], rb[B_CH];
-    auto load_global = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) ra[i] = *(const u32x4 *)(a_ptr[i] + kt * BK);
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i)
-            rb[i] = b_ok[i] ? *(const u32x4 *)(b_ptr[i] + (int64_t)kt * BK * b_ld[i]) : u32x4{0, 0, 0, 0};
-    };
-    auto store_lds = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < A_CH; ++i) *(u32x4 *)(As(buf) + a_lds[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) *(u32x4 *)(Bs(buf) + b_lds[i]) = rb[i];
-    };
-
-    f32x16 acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    const int KT = g.K / BK;
-    const int lr = lane & 31, lh = lane >> 5;
-    const int q = lane >> 4, sl = lane & 15;     // 16-lane group and lane in it
-    // B fragment source of this lane: row (q/2)*8 + sl/4 (+4 for the second
-    // half) of the 16-row slice, 16-column granule 2j + q%2 of the wave's
-    // columns, element 4*(sl%4) inside it; the granule is swizzled by row
-    const int b_row = (q >> 1) * 8 + (sl >> 2);
-    const int b_in = (sl & 3) * 4;
-    load_global(0);
-    store_lds(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) load_global(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ks * 2 + lh;
-            bf16x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 32 + lr;
-                af[i] = as_bf16x8(*(const u32x4 *)(As(buf) + row * BK + ((ch ^ swz_row(row)) * 8)));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int gran = (wn * WTN + j * 32) / 16 + (q & 1);
-                const int r0 = ks * 16 + b_row, r1 = r0 + 4;
-                const u32x2 lo = lds_read_tr16(Bs(buf) + r0 * BROW + ((gran ^ swz_tr(r0)) * 16) + b_in);
-                const u32x2 hi = lds_read_tr16(Bs(buf) + r1 * BROW + ((gran ^ swz_tr(r1)) * 16) + b_in);
-                bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-        }
-        if (kt + 1 < KT) store_lds(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue through LDS: per wave, one 32-row slice at a time is
-    // written as fp32 and read back as row-major column pairs
-    static_assert(WM * WN * 32 * WTN * 4 <= 2 * STAGE * 2, "epilogue staging must fit in the tile buffers");
-    float *stage = (float *)lds + wave * (32 * WTN);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * WTN + j * 32 + lr] = acc[i][j][v];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int row0 = m0 + wm * WTM + i * 32;
-        if constexpr (EPI == EPI_SWIGLU) {
-            // logical column u of this wave: gate at 64 (u/32) + u%32, up 32 further
-            constexpr int UW = WTN / 2;
-#pragma unroll
-            for (int r = 0; r < 32 * UW / 64; ++r) {
-                const int p = r * 64 + lane, rl = p / UW, u = p % UW;
-                const int cg = 64 * (u >> 5) + (u & 31);
-                epi_store_swiglu<bf16_t>(ep, row0 + rl, tn * (BN / 2) + wn * UW + u, stage[rl * WTN + cg],
-                                         stage[rl * WTN + cg + 32]);
-            }
-        } else {
-            constexpr int PW = WTN / 2;
-#pragma unroll
-            for (int r = 0; r < 32 * PW / 64; ++r) {
-                const int p = r * 64 + lane, rl = p / PW, cp = p % PW;
-                const float2 v = *(const float2 *)(stage + rl * WTN + 2 * cp);
-                epi_store_pair<EPI, bf16_t>(ep, row0 + rl, n0 + wn * WTN + 2 * cp, v.x, v.y);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-}
-
 // ---------------------------------------------------------------------------
-// bf16 GEMM, third form: operands go from global memory straight into LDS
+// bf16 GEMM: operands go from global memory straight into LDS
 // (global_load_lds_dwordx4: lane i of an instruction writes the i-th 16-byte
 // slot of a 1 KB block), through a ring of NST stages of BK = 32, so three
 // k steps of loads are in flight while one is multiplied.  Each lane fetches
 // the global chunk that belongs in its slot, which lays the tiles out already
 // swizzled: A rows (64 bytes, k contiguous) with chunk ^ ((row >> 2) & 3),
-// B rows (N contiguous) with 32-byte granules ^ swz_tr(row).  Fragments are
-// read as in the second form.  The waits are explicit: before a stage is
-// used, s_waitcnt vmcnt leaves only the younger stages outstanding, then a
-// barrier makes every wave's slots visible.
+// B rows (N contiguous) with 32-byte granules ^ swz_tr(row), so the transpose
+// reads of one 16-lane group fall in different banks.  The waits are
+// explicit: before a stage is used, s_waitcnt vmcnt leaves only the younger
+// stages outstanding, then a barrier makes every wave's slots visible.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -646,28 +320,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams ep)
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int SRC, int EPI>
-static hipError_t launch_bf16(GemmArgs g, const EpiParams &ep, hipStream_t s) {
-    g.tiles_m = (g.M + BM - 1) / BM;
-    g.tiles_n = (g.N + BN - 1) / BN;
-    g.group_m = 8;
-    const int blocks = g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s, g,
-                       ep);
-    return hipGetLastError();
-}
-
-template <int BM, int BN, int WM, int WN, int SRC, int EPI>
-static hipError_t launch_tr(GemmArgs g, const EpiParams &ep, hipStream_t s) {
-    g.tiles_m = (g.M + BM - 1) / BM;
-    g.tiles_n = (g.N + BN - 1) / BN;
-    g.group_m = 8;
-    const int blocks = g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL((gemm_bf16_tr_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s,
-                       g, ep);
-    return hipGetLastError();
-}
-
 template <int BM, int BN, int WM, int WN, int SRC, int EPI>
 static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, hipStream_t s) {
     g.tiles_m = (g.M + BM - 1) / BM;
