@@ -9,12 +9,16 @@ kernel's achieved HBM bandwidth.  Inputs are synthetic and seeded, resident
 in HBM before timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+       python bench.py --copy-calibration   (a plain 1 GiB device copy, for
+                                             scaling the HBM byte counters)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +28,34 @@ sys.path.insert(0, ROOT)
 METRIC = "block prefill TFLOP/s + decode tok/s, as % of MFMA / HBM roofline on 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBPS = 8000.0      # HBM3E
+
+# HBM traffic of the gate-up GEMM from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+# with the sources of the kernel it was taken on (stale counters give null)
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gateup_gemm_7b_prefill_pmc.md")
+GEMM_SOURCES = [os.path.join(ROOT, "transformer_decoder_block_rmsnorm_amd", "csrc", n)
+                for n in ("gemm.hip", "epilogue.h", "common.h", "kernels.h")]
+
+
+def gemm_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel sources."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    s = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or not s or s.group(1) != gemm_source_digest():
+        return None
+    return int(m.group(1))
 
 
 def _dev_tensor(f32, bits):
@@ -61,22 +93,36 @@ def time_prefill(cfg, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # timed region: K steps; the dominant kernel (the fused gate-up GEMM) is
+    # bracketed by HIP events on its launch stream
+    tfb.profile_read()
+    tfb.profile_stages(["gateup_gemm"])
+    tfb.profile_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
+    tfb.profile_enable(False)
     ms = e0.elapsed_time(e1) / steps
-    flops = FM.block_prefill_flops_causal(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
-    # per-kernel durations, measured with HIP events on the launch stream
+    dominant = tfb.profile_read()
+    # the same K steps with every launch bracketed: per-stage breakdown (the
+    # event pairs add gaps between launches, so this pass is not the headline)
+    tfb.profile_stages(None)
     tfb.profile_enable(True)
+    e0.record()
     for _ in range(steps):
         step()
+    e1.record()
     torch.cuda.synchronize()
-    stages = tfb.profile_read()
     tfb.profile_enable(False)
-    return dict(ms=ms, flops=flops, stages=stages, w32=w32, x32=x32)
+    ms_all_events = e0.elapsed_time(e1) / steps
+    stages = tfb.profile_read()
+    flops = FM.block_prefill_flops_causal(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    return dict(ms=ms, ms_all_events=ms_all_events, flops=flops, stages=stages, dominant=dominant, w32=w32,
+                x32=x32)
 
 
 def time_decode(cfg, steps, warmup):
@@ -110,26 +156,33 @@ def time_decode(cfg, steps, warmup):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    tfb.profile_read()
+    tfb.profile_stages(["attention", "attention_combine"])
     total = 0.0
     for _ in range(steps):
         flush.fill_(1)  # evict the caches between steps; not timed
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        tfb.profile_enable(True)
         e0.record()
         step()
         e1.record()
         torch.cuda.synchronize()
+        tfb.profile_enable(False)
         total += e0.elapsed_time(e1)
     ms = total / steps
+    dominant = tfb.profile_read()
+    tfb.profile_stages(None)
     tfb.profile_enable(True)
     for _ in range(steps):
         flush.fill_(1)
         step()
     torch.cuda.synchronize()
-    stages = tfb.profile_read()
     tfb.profile_enable(False)
+    stages = tfb.profile_read()
     attn_bytes = FM.decode_attention_bytes(lens, cfg.n_kv_heads, dh) + 2 * B * cfg.d * 2
     wbytes = 2 * FM.block_matrix_params(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
-    return dict(ms=ms, stages=stages, attn_bytes=attn_bytes, weight_bytes=wbytes, lens=lens)
+    return dict(ms=ms, stages=stages, dominant=dominant, attn_bytes=attn_bytes, weight_bytes=wbytes, lens=lens)
 
 
 def cpu_baseline(cfg, w32, x32, rows):
@@ -149,11 +202,12 @@ def cpu_baseline(cfg, w32, x32, rows):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -164,21 +218,31 @@ def main():
     from synth.configs import C2, C4
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.backends.cuda.matmul.allow_tf32 = False
+    if args.copy_calibration:
+        # one plain device copy kernel of known size per launch, three launches
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+        return
 
     pre = time_prefill(C2, args.steps, args.warmup)
     tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
-    gms, gcalls = pre["stages"]["gateup_gemm"]
+    gms, gcalls = pre["dominant"]["gateup_gemm"]
     g_ms = gms / gcalls
     g_flops = 2 * C2.B * C2.T * C2.d * 2 * C2.d_ff
     roof = {"kernel": "gateup_gemm (fused W1|W3 GEMM + SiLU*up)", "bound": "mfma",
             "achieved": round(g_flops / (g_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
             "launch_ms": round(g_ms, 4), "flops_per_launch": g_flops}
     stages = {k: round(v[0] / v[1], 4) for k, v in pre["stages"].items()}
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4), "ms_per_step_all_events": round(pre["ms_all_events"], 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "Llama-2-7B-shaped block prefill: d=4096 H=Hkv=32 dh=128 f=11008 B=1 T=2048, "
                                "KV cache written", "global_batch": C2.B, "seq_len": C2.T, "parallelism": "none"},
@@ -189,8 +253,8 @@ def main():
     }
     if not args.no_decode:
         dec = time_decode(C4, args.steps, args.warmup)
-        ams, acalls = dec["stages"]["attention"]
-        cms, ccalls = dec["stages"].get("attention_combine", (0.0, 1))
+        ams, acalls = dec["dominant"]["attention"]
+        cms, ccalls = dec["dominant"].get("attention_combine", (0.0, 1))
         a_ms = ams / acalls + (cms / ccalls if ccalls else 0.0)
         a_gbps = dec["attn_bytes"] / (a_ms * 1e-3) / 1e9
         result["decode"] = {

@@ -165,14 +165,18 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
                              void *stream);
 
 /* Benchmark instrumentation (host side, off by default).  While enabled,
- * every launch made by the calls above is bracketed by a pair of HIP events
- * recorded on the call's stream.  tfb_profile_read waits for the recorded
+ * every launch of a selected stage made by the calls above is bracketed by a
+ * pair of HIP events recorded on the call's stream.  tfb_profile_stages
+ * selects the stages: bit i of mask selects stage i (default: all; an event
+ * pair costs the stream a short gap, so timing one kernel inside a timed
+ * region selects just that one).  tfb_profile_read waits for the recorded
  * events, writes the summed milliseconds and launch counts per stage into
  * ms[i] and calls[i] for i < n (either may be NULL), forgets the records and
  * returns the number of stages.  Stage i is named by tfb_profile_stage_name.
  * Not for use under graph capture; the event pool is created lazily on the
  * host and holds no device memory. */
 tfb_status tfb_profile_enable(int32_t on);
+tfb_status tfb_profile_stages(uint32_t mask);
 int32_t tfb_profile_read(float *ms, int32_t *calls, int32_t n);
 const char *tfb_profile_stage_name(int32_t stage);
 

@@ -20,7 +20,7 @@ STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTY
           -5: "TFB_ERR_WORKSPACE", -6: "TFB_ERR_CACHE_OVERFLOW", -7: "TFB_ERR_HIP", -8: "TFB_ERR_UNSUPPORTED"}
 EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
            "tfb_model_forward", "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
-           "tfb_profile_stage_name")
+           "tfb_profile_stages", "tfb_profile_stage_name")
 
 _VP = ctypes.c_void_p
 
@@ -86,6 +86,8 @@ def lib():
         L.tfb_version.restype = ctypes.c_int32
         L.tfb_profile_enable.argtypes = [ctypes.c_int32]
         L.tfb_profile_enable.restype = ctypes.c_int
+        L.tfb_profile_stages.argtypes = [ctypes.c_uint32]
+        L.tfb_profile_stages.restype = ctypes.c_int
         L.tfb_profile_read.argtypes = [_VP, _VP, ctypes.c_int32]
         L.tfb_profile_read.restype = ctypes.c_int32
         L.tfb_profile_stage_name.argtypes = [ctypes.c_int32]
@@ -219,6 +221,25 @@ def model_forward(h: ModelHandle, rope, ids, caches: list, lens, h_max_len: int,
 
 def profile_enable(on: bool = True):
     _check(lib().tfb_profile_enable(1 if on else 0), "tfb_profile_enable")
+
+
+def profile_stages(names=None):
+    """Stages bracketed while profiling: an iterable of stage names, or None for all."""
+    L = lib()
+    if names is None:
+        mask = 0xFFFFFFFF
+    else:
+        index = {}
+        for k in range(32):
+            n = L.tfb_profile_stage_name(k)
+            if n:
+                index[n.decode()] = k
+        mask = 0
+        for n in names:
+            if n not in index:
+                raise ValueError("unknown stage %r" % n)
+            mask |= 1 << index[n]
+    _check(L.tfb_profile_stages(ctypes.c_uint32(mask)), "tfb_profile_stages")
 
 
 def profile_read() -> dict:

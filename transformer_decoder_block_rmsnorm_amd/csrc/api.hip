@@ -113,6 +113,7 @@ const char *kStageNames[ST_COUNT] = {"rmsnorm_attn", "qkv_gemm", "attention", "a
 struct ProfRec { int stage; hipEvent_t a, b; };
 std::mutex g_prof_mu;
 bool g_prof = false;
+uint32_t g_prof_mask = 0xFFFFFFFFu;  // stages bracketed while profiling
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -126,7 +127,7 @@ hipEvent_t prof_event() {
 // Runs one launch; when profiling, brackets it with an event pair.
 template <typename F>
 hipError_t staged(int stage, hipStream_t s, F &&launch) {
-    if (!g_prof) return launch();
+    if (!g_prof || !((g_prof_mask >> stage) & 1u)) return launch();
     std::lock_guard<std::mutex> lk(g_prof_mu);
     ProfRec r{stage, prof_event(), prof_event()};
     if (r.a) hipEventRecord(r.a, s);
@@ -227,6 +228,12 @@ int32_t tfb_version(void) { return 100; }
 tfb_status tfb_profile_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof = on != 0;
+    return TFB_OK;
+}
+
+tfb_status tfb_profile_stages(uint32_t mask) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_mask = mask;
     return TFB_OK;
 }
 
