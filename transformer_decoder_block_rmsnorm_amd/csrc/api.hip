@@ -24,7 +24,8 @@ inline size_t esize(int dtype) { return dtype == TFB_BF16 ? 2 : 4; }
 constexpr int kMaxSplits = 64;
 
 struct WsLayout {
-    size_t h, q, att, r, act, kv_k, kv_v, part, skinny, skinny_bytes, x0, x1, last, logits, total;
+    size_t h, q, att, r, act, kv_k, kv_v, part, skinny, skinny_bytes, gsplit, gsplit_bytes, x0, x1, last, logits,
+        total;
 };
 
 WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
@@ -53,6 +54,17 @@ WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
         if (sk) {
             L.skinny_bytes = sk;
             L.skinny = take(sk);
+        }
+    }
+    if (c.dtype == TFB_BF16) {
+        // split-K tail partials of the large-M GEMMs (one GEMM at a time)
+        const int Mi = (int)M;
+        size_t gs = std::max({gemm_split_bytes(Mi, (int)(qd + 2 * kvd), c.d), gemm_split_bytes(Mi, c.d, (int)qd),
+                              gemm_split_bytes(Mi, 2 * c.d_ff, c.d), gemm_split_bytes(Mi, c.d, c.d_ff)});
+        if (vocab > 0) gs = std::max(gs, gemm_split_bytes(Mi, vocab, c.d));
+        if (gs) {
+            L.gsplit_bytes = gs;
+            L.gsplit = take(gs);
         }
     }
     if (vocab > 0) {
@@ -172,6 +184,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.ep.T = T; g.ep.H = H; g.ep.Hkv = Hkv; g.ep.dh = dh; g.ep.t_max = t_max; g.ep.start = start;
     g.scratch = L.skinny_bytes ? ws + L.skinny : nullptr;
     g.scratch_bytes = L.skinny_bytes;
+    g.split_scratch = L.gsplit_bytes ? ws + L.gsplit : nullptr;
+    g.split_bytes = L.gsplit_bytes;
     TRY_HIP(STAGE(ST_QKV, gemm_launch(g, s)));
 
     AttnCall a{};
@@ -193,6 +207,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     o.ep.M = M; o.ep.N = d; o.ep.out = r; o.ep.ldo = d; o.ep.res = x; o.ep.ldr = d; o.ep.out_f32 = 1;
     o.scratch = g.scratch;
     o.scratch_bytes = g.scratch_bytes;
+    o.split_scratch = g.split_scratch;
+    o.split_bytes = g.split_bytes;
     TRY_HIP(STAGE(ST_WO, gemm_launch(o, s)));
 
     TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
@@ -205,6 +221,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     gu.ep.M = M; gu.ep.N = f; gu.ep.out = act; gu.ep.ldo = f;
     gu.scratch = g.scratch;
     gu.scratch_bytes = g.scratch_bytes;
+    gu.split_scratch = g.split_scratch;
+    gu.split_bytes = g.split_bytes;
     TRY_HIP(STAGE(ST_GATEUP, gemm_launch(gu, s)));
 
     GemmCall dn{};
@@ -215,6 +233,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     dn.ep.M = M; dn.ep.N = d; dn.ep.out = out; dn.ep.ldo = d; dn.ep.res = r; dn.ep.ldr = d; dn.ep.res_f32 = 1;
     dn.scratch = g.scratch;
     dn.scratch_bytes = g.scratch_bytes;
+    dn.split_scratch = g.split_scratch;
+    dn.split_bytes = g.split_bytes;
     TRY_HIP(STAGE(ST_W2, gemm_launch(dn, s)));
     return TFB_OK;
 }
@@ -425,6 +445,8 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
         hd.ep.M = rows; hd.ep.N = V; hd.ep.out = lg; hd.ep.ldo = V;
         hd.scratch = L.skinny_bytes ? wsb + L.skinny : nullptr;
         hd.scratch_bytes = L.skinny_bytes;
+        hd.split_scratch = L.gsplit_bytes ? wsb + L.gsplit : nullptr;
+        hd.split_bytes = L.gsplit_bytes;
         TRY_HIP(STAGE(ST_LM_HEAD, gemm_launch(hd, s)));
         if (next_ids) {
             // Greedy next token from each sequence's last row ([PID] Under the hood, step 6).

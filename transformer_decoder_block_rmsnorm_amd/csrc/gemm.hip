@@ -16,6 +16,8 @@
 //
 // fp32: a plain LDS-tiled VALU GEMM with the same epilogues (the fp32 storage
 // path serves small shapes; it is launch-latency bound).
+#include <algorithm>
+
 #include "epilogue.h"
 #include "kernels.h"
 
@@ -37,16 +39,24 @@ struct GemmArgs {
     const void *w[3];
     int w_cols[3];      // columns (= leading dimension) of each matrix
     int tiles_m, tiles_n, group_m;
+    // split-K tail: workgroups [0, full_tiles) compute whole tiles; the
+    // remaining tiles are each computed by `splits` workgroups over equal
+    // k ranges, which write fp32 partials to `part`, and a fix-up kernel adds
+    // them in a fixed order and applies the epilogue
+    int full_tiles, splits;
+    float *part;        // [tiles - full_tiles][splits][BM][BN]
 };
 
-// Logical tile (tm, tn) of workgroup `bid`.  Workgroups are dealt to the 8
-// XCDs round robin; the remap gives each XCD a contiguous run of logical
-// tiles, and the run is ordered in groups of `group_m` row panels so that the
+// Workgroups are dealt to the 8 XCDs round robin.  xcd_remap gives each XCD a
+// contiguous run of n consecutive logical indices (n a multiple of 8), so the
 // tiles resident on one XCD share A and B panels in that XCD's L2.
-__device__ __forceinline__ void tile_of(const GemmArgs &g, int bid, int &tm, int &tn) {
-    const int total = g.tiles_m * g.tiles_n;
-    int L = bid;
-    if ((total & 7) == 0) L = (bid & 7) * (total >> 3) + (bid >> 3);
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+    return (n & 7) ? b : (b & 7) * (n >> 3) + (b >> 3);
+}
+
+// Tile index -> (tm, tn): runs of `group_m` row panels, column-major inside
+// a run, so consecutive tiles reuse the same weight columns.
+__device__ __forceinline__ void tile_coords(const GemmArgs &g, int L, int &tm, int &tn) {
     const int per_group = g.group_m * g.tiles_n;
     const int grp = L / per_group;
     const int first_m = grp * g.group_m;
@@ -54,6 +64,20 @@ __device__ __forceinline__ void tile_of(const GemmArgs &g, int bid, int &tm, int
     const int r = L - grp * per_group;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+
+// Work of workgroup `bid`: its tile and, for the split tail, its k split
+// (-1: the whole k range).  Whole tiles come first in launch order.
+__device__ __forceinline__ void wg_work(const GemmArgs &g, int bid, int &tile, int &split) {
+    if (bid < g.full_tiles) {
+        tile = xcd_remap(bid, g.full_tiles);
+        split = -1;
+    } else {
+        const int n_split = (g.tiles_m * g.tiles_n - g.full_tiles) * g.splits;
+        const int j = xcd_remap(bid - g.full_tiles, n_split);
+        tile = g.full_tiles + j / g.splits;
+        split = j % g.splits;
+    }
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
@@ -117,9 +141,14 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    int tm, tn;
-    tile_of(g, blockIdx.x, tm, tn);
+    int tile, split, tm, tn;
+    wg_work(g, blockIdx.x, tile, split);
+    tile_coords(g, tile, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // k steps of this workgroup
+    const int KT_all = g.K / BKD;
+    const int kt0 = split < 0 ? 0 : (split * KT_all) / g.splits;
+    const int kt1 = split < 0 ? KT_all : ((split + 1) * KT_all) / g.splits;
 
     // ---- per-lane source of each 1 KB block this wave fills
     const bf16_t *A = (const bf16_t *)g.A;
@@ -128,7 +157,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     for (int j = 0; j < A_INS; ++j) {
         const int slot = (wave * A_INS + j) * 64 + lane;
         const int row = slot >> 2, p = slot & 3, c = p ^ ((row >> 2) & 3);
-        a_src[j] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + 8 * c;
+        a_src[j] = A + (int64_t)min(m0 + row, g.M - 1) * g.lda + 8 * c + kt0 * BKD;
     }
     const bf16_t *b_src[B_INS];
     int b_ld[B_INS];
@@ -153,7 +182,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
         }
         if (col >= ld) col = ld - 8;  // ragged tail: a valid column whose outputs are never stored
         b_ld[j] = ld;
-        b_src[j] = base + (int64_t)k * ld + col;
+        b_src[j] = base + (int64_t)(k + kt0 * BKD) * ld + col;
     }
     auto issue = [&](int kt, int stage) {
         // LDS byte address of this wave's first block in the stage (wave-uniform)
@@ -174,7 +203,7 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int KT = g.K / BKD;
+    const int KT = kt1 - kt0;
     const int lr = lane & 31, lh = lane >> 5;
     const int q = lane >> 4, sl = lane & 15;
     const int b_row = (q >> 1) * 8 + (sl >> 2);
@@ -233,7 +262,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int row0 = m0 + wm * WTM + i * 32;
-        if constexpr (EPI == EPI_SWIGLU) {
+        if (split >= 0) {
+            // split tail: raw fp32 partial of this k range, tile-local layout
+            float *dst = g.part + ((int64_t)(tile - g.full_tiles) * g.splits + split) * (BM * BN) +
+                         (wm * WTM + i * 32) * BN + wn * WTN;
+#pragma unroll
+            for (int r = 0; r < 32 * WTN / 4 / 64; ++r) {
+                const int p = r * 64 + lane, rl = p / (WTN / 4), c4 = p % (WTN / 4);
+                *(f32x4 *)(dst + rl * BN + 4 * c4) = *(const f32x4 *)(stage + rl * WTN + 4 * c4);
+            }
+        } else if constexpr (EPI == EPI_SWIGLU) {
             constexpr int UW = WTN / 2;
 #pragma unroll
             for (int r = 0; r < 32 * UW / 64; ++r) {
@@ -320,15 +358,103 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams ep)
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Split tail: add the k-split partials of one tile in a fixed order (so the
+// result does not depend on which workgroup finished first) and apply the
+// epilogue.  One thread per 4 tile-local columns of a row.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiParams ep) {
+    const int pt = blockIdx.y;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= BM * BN) return;
+    int tm, tn;
+    tile_coords(g, g.full_tiles + pt, tm, tn);
+    const int row = e / BN, col = e % BN;
+    if constexpr (EPI == EPI_SWIGLU) {
+        if ((col & 63) >= 32) return;  // up columns are read by the gate's thread
+    }
+    const float *src = g.part + (int64_t)pt * g.splits * (BM * BN) + row * BN + col;
+    f32x4 v = *(const f32x4 *)src;
+    f32x4 u = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (EPI == EPI_SWIGLU) u = *(const f32x4 *)(src + 32);
+    for (int s = 1; s < g.splits; ++s) {
+        v += *(const f32x4 *)(src + (int64_t)s * (BM * BN));
+        if constexpr (EPI == EPI_SWIGLU) u += *(const f32x4 *)(src + (int64_t)s * (BM * BN) + 32);
+    }
+    const int m = tm * BM + row;
+    if constexpr (EPI == EPI_SWIGLU) {
+        const int lc = tn * (BN / 2) + (col >> 6) * 32 + (col & 31);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) epi_store_swiglu<bf16_t>(ep, m, lc + k, v[k], u[k]);
+    } else {
+        epi_store_pair<EPI, bf16_t>(ep, m, tn * BN + col, v[0], v[1]);
+        epi_store_pair<EPI, bf16_t>(ep, m, tn * BN + col + 2, v[2], v[3]);
+    }
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Split-K plan for the last, partial round of tiles: with `rem` tiles left
+// over after whole rounds on `cus` compute units, split each of them `splits`
+// ways so that rem * splits <= cus (at least 8 k steps per split, at most 4).
+struct SplitPlan {
+    int full_tiles, splits;
+    size_t part_bytes;
+};
+static SplitPlan plan_split(int tiles, int k_steps, int cus, int tile_elems) {
+    SplitPlan p{tiles, 1, 0};
+    const int rem = tiles % cus;
+    if (rem == 0) return p;
+    int s = std::min(std::min(cus / rem, k_steps / 8), 4);
+    if (s < 2) return p;
+    p.full_tiles = tiles - rem;
+    p.splits = s;
+    p.part_bytes = (size_t)rem * s * tile_elems * sizeof(float);
+    return p;
+}
+
 template <int BM, int BN, int WM, int WN, int SRC, int EPI>
-static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, hipStream_t s) {
+static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, void *part, size_t part_bytes, hipStream_t s) {
     g.tiles_m = (g.M + BM - 1) / BM;
     g.tiles_n = (g.N + BN - 1) / BN;
     g.group_m = 8;
-    const int blocks = g.tiles_m * g.tiles_n;
+    const int tiles = g.tiles_m * g.tiles_n;
+    SplitPlan sp = plan_split(tiles, g.K / 32, device_cus(), BM * BN);
+    if (!part || sp.part_bytes > part_bytes) sp = SplitPlan{tiles, 1, 0};
+    g.full_tiles = sp.full_tiles;
+    g.splits = sp.splits;
+    g.part = (float *)part;
+    const int blocks = sp.full_tiles + (tiles - sp.full_tiles) * sp.splits;
     hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s,
                        g, ep);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || sp.splits == 1) return e;
+    dim3 fg((BM * BN / 4 + 255) / 256, tiles - sp.full_tiles);
+    hipLaunchKernelGGL((gemm_split_fixup_kernel<BM, BN, EPI>), fg, dim3(256), 0, s, g, ep);
     return hipGetLastError();
+}
+
+// Tile shape of a large-M bf16 GEMM: 256x256 on 8 waves when at least half
+// the compute units get a tile (a partial last round is split along k),
+// 128x128 on 4 waves otherwise.
+static bool big_tiles(int M, int N_virtual) {
+    return ((M + 255) / 256) * ((N_virtual + 255) / 256) * 2 >= device_cus();
+}
+
+size_t gemm_split_bytes(int M, int N_virtual, int K) {
+    if (M <= kSkinnyMaxM || !big_tiles(M, N_virtual)) return 0;
+    const int tiles = ((M + 255) / 256) * ((N_virtual + 255) / 256);
+    return plan_split(tiles, K / 32, device_cus(), 256 * 256).part_bytes;
 }
 
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
@@ -352,26 +478,27 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
         return hipGetLastError();
     }
     if (c.M <= kSkinnyMaxM && c.scratch) return skinny_gemm_launch(c, c.scratch, c.scratch_bytes, s);
-    // large M: 256x256 tiles on 8 waves (128 x 64 each) when the launch still
-    // fills the chip, 128x128 tiles on 4 waves otherwise
-    const bool big = ((c.M + 255) / 256) * ((c.ep.N * (c.epi == EPI_SWIGLU ? 2 : 1) + 255) / 256) >= 256;
+    const int nv = c.ep.N * (c.epi == EPI_SWIGLU ? 2 : 1);
+    const bool big = big_tiles(c.M, nv);
+    void *part = c.split_scratch;
+    const size_t pb = c.split_bytes;
     switch (c.epi) {
         case EPI_QKV:
             g.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2];
-            return big ? launch_dma<256, 256, 2, 4, SRC_CONCAT, EPI_QKV>(g, ep, s)
-                       : launch_dma<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_CONCAT, EPI_QKV>(g, ep, part, pb, s)
+                       : launch_dma<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, nullptr, 0, s);
         case EPI_RESID:
             g.N = c.w_cols[0];
-            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_RESID>(g, ep, s)
-                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_RESID>(g, ep, part, pb, s)
+                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, nullptr, 0, s);
         case EPI_SWIGLU:
             g.N = 2 * c.w_cols[0];
-            return big ? launch_dma<256, 256, 2, 4, SRC_DUAL, EPI_SWIGLU>(g, ep, s)
-                       : launch_dma<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_DUAL, EPI_SWIGLU>(g, ep, part, pb, s)
+                       : launch_dma<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, nullptr, 0, s);
         case EPI_F32:
             g.N = c.w_cols[0];
-            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_F32>(g, ep, s)
-                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, s);
+            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_F32>(g, ep, part, pb, s)
+                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, nullptr, 0, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -19,8 +19,13 @@ struct GemmCall {
     EpiParams ep;
     void *scratch;         // split-K partials for skinny (decode) shapes, may be NULL
     size_t scratch_bytes;
+    void *split_scratch;   // large-M split-K tail partials (gemm_split_bytes), may be NULL
+    size_t split_bytes;
 };
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s);
+// Scratch the large-M bf16 GEMM uses for its split-K tail (0: none); with
+// less, it runs without splitting.  N_virtual: B columns (gate-up: 2 f).
+size_t gemm_split_bytes(int M, int N_virtual, int K);
 // Skinny (M <= 64) weight-streaming GEMM with split-K partials in `part`.
 constexpr int kSkinnyMaxM = 64;
 hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, hipStream_t s);
