@@ -96,14 +96,16 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t *p) {
 // ---------------------------------------------------------------------------
 // bf16 GEMM: operands go from global memory straight into LDS
 // (global_load_lds_dwordx4: lane i of an instruction writes the i-th 16-byte
-// slot of a 1 KB block), through a ring of NST stages of BK = 32, so three
-// k steps of loads are in flight while one is multiplied.  Each lane fetches
-// the global chunk that belongs in its slot, which lays the tiles out already
-// swizzled: A rows (64 bytes, k contiguous) with chunk ^ ((row >> 2) & 3),
-// B rows (N contiguous) with 32-byte granules ^ swz_tr(row), so the transpose
-// reads of one 16-lane group fall in different banks.  The waits are
-// explicit: before a stage is used, s_waitcnt vmcnt leaves only the younger
-// stages outstanding, then a barrier makes every wave's slots visible.
+// slot of a 1 KB block), through a ring of NST stages of BK = 32, so up to
+// three k steps of loads are in flight while one is multiplied.  Each lane
+// fetches the global chunk that belongs in its slot, which lays the tiles out
+// already swizzled: A rows (64 bytes, k contiguous) with
+// chunk ^ ((row >> 2) & 3), B rows (N contiguous) with 32-byte granules
+// ^ swz_tr(row), so the transpose reads of one 16-lane group fall in
+// different banks.  The waits are explicit: before a stage is used,
+// s_waitcnt vmcnt leaves only the younger stages outstanding, then a barrier
+// makes every wave's slots visible.  The MFMAs of one 16-wide k half run
+// while the fragments of the next half are read from LDS.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -125,7 +127,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int BM, int BN, int WM, int WN, int SRC, int EPI>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, EpiParams ep) {
     constexpr int NW = WM * WN, NT = NW * 64;
-    constexpr int BKD = 32, NST = 4;
+    constexpr int BKD = 32, NST = 4;  // ring stages of BKD k each
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     constexpr int A_INS = BM * BKD * 2 / 1024 / NW;   // 1 KB A blocks per wave per stage
@@ -210,43 +212,103 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     const int b_in = (sl & 3) * 4;
     constexpr int PER = A_INS + B_INS;  // vmem instructions per stage per thread
 
-#pragma unroll
-    for (int st = 0; st < NST - 1; ++st)
-        if (st < KT) issue(st, st);
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt + 2 < KT) wait_vmcnt<2 * PER>();
-        else if (kt + 1 < KT) wait_vmcnt<PER>();
-        else wait_vmcnt<0>();
-        // every wave's slots of stage kt have landed, and every wave is done
-        // reading the stage about to be refilled
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are complete
-        asm volatile("s_barrier" ::: "memory");  // no LDS access moves across it
-        if (kt + NST - 1 < KT) issue(kt + NST - 1, (kt + NST - 1) % NST);
-        const bf16_t *As = lds + (kt % NST) * STAGE;
+    static_assert(BKD == 32 && NST >= 3 && NST <= 6, "the pipeline below is written for two 16-wide k halves");
+    // Fragments of one 16-wide k half of a stage.
+    auto read_frags = [&](const bf16_t *As, int ks, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
         const bf16_t *Bs = As + A_ELEMS;
 #pragma unroll
-        for (int ks = 0; ks < BKD / 16; ++ks) {
-            const int ch = ks * 2 + lh;
-            bf16x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int row = wm * WTM + i * 32 + lr;
-                af[i] = as_bf16x8(*(const u32x4 *)(As + row * BKD + ((ch ^ ((row >> 2) & 3)) * 8)));
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int gran = (wn * WTN + j * 32) / 16 + (q & 1);
-                const int r0 = ks * 16 + b_row, r1 = r0 + 4;
-                const u32x2 lo = lds_read_tr16(Bs + r0 * BN + ((gran ^ swz_tr(r0)) * 16) + b_in);
-                const u32x2 hi = lds_read_tr16(Bs + r1 * BN + ((gran ^ swz_tr(r1)) * 16) + b_in);
-                bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) {
+            const int gran = (wn * WTN + j * 32) / 16 + (q & 1);
+            const int r0 = ks * 16 + b_row, r1 = r0 + 4;
+            const u32x2 lo = lds_read_tr16(Bs + r0 * BN + ((gran ^ swz_tr(r0)) * 16) + b_in);
+            const u32x2 hi = lds_read_tr16(Bs + r1 * BN + ((gran ^ swz_tr(r1)) * 16) + b_in);
+            bfr[j] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         }
+        const int ch = ks * 2 + lh;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row = wm * WTM + i * 32 + lr;
+            af[i] = as_bf16x8(*(const u32x4 *)(As + row * BKD + ((ch ^ ((row >> 2) & 3)) * 8)));
+        }
+    };
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];  // fragments of k halves 0 and 1
+    // The first MFMA of a k half (its operands are complete), then the rest.
+    auto first_product = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
+        acc[0][0] = mfma32(af[0], bfr[0], acc[0][0]);
+    };
+    auto other_products = [&](const bf16x8 (&af)[TM], const bf16x8 (&bfr)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                if (i | j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    };
+    // k half 0 of stage kt: its MFMAs run while half 1's fragments are read.
+    auto half0 = [&](const bf16_t *As) {
+        first_product(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(As, 1, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        other_products(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // k half 1 of stage kt: its MFMAs run while half 0 of the next stage is read.
+    auto half1 = [&](const bf16_t *An) {
+        first_product(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(An, 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        other_products(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's reads of stage kt are done
+        asm volatile("s_barrier" ::: "memory");  // every wave: stage kt+1 landed, stage kt read
+    };
+    auto slot = [&](int kt) { return (const bf16_t *)(lds + (kt % NST) * STAGE); };
+
+    // Software pipeline at half-stage granularity: the LDS reads of the next
+    // k half are in flight while the MFMAs of the current one run, so LDS and
+    // matrix cores work at the same time instead of in turn after each
+    // barrier.  Stage s lives in ring slot s % NST; all NST slots are filled
+    // ahead, and a slot is refilled right after the barrier that follows the
+    // last read of its stage.
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+        if (st < KT) issue(st, st);
+    // waits until at most n of this wave's stage loads are still in flight
+    auto wait_stages = [&](int n) {
+        switch (n) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<PER>(); break;
+            case 2: wait_vmcnt<2 * PER>(); break;
+            case 3: wait_vmcnt<3 * PER>(); break;
+            case 4: wait_vmcnt<4 * PER>(); break;
+            default: wait_vmcnt<5 * PER>(); break;
+        }
+    };
+    wait_stages(min(NST - 1, KT - 1));
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("s_barrier" ::: "memory");  // stage 0 visible to every wave
+    read_frags(slot(0), 0, fa0, fb0);
+    int kt = 0;
+    for (; kt + NST - 1 < KT; ++kt) {
+        // steady state: the loads of stages kt+2 .. kt+NST-1 may stay in flight
+        half0(slot(kt));
+        wait_vmcnt<(NST - 2) * PER>();
+        sync();
+        if (kt + NST < KT) issue(kt + NST, kt % NST);
+        half1(slot(kt + 1));
     }
+    for (; kt + 1 < KT; ++kt) {
+        half0(slot(kt));
+        wait_stages(KT - 2 - kt);
+        sync();
+        half1(slot(kt + 1));
+    }
+    half0(slot(KT - 1));
+    first_product(fa1, fb1);
+    other_products(fa1, fb1);
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with the ring before it is reused for staging
 
