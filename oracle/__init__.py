@@ -37,7 +37,7 @@ def build(src: str | None = None, out: str | None = None, extra: list[str] | Non
 class _Cfg(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("gemm_bf16", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("gemm_bf16", ctypes.c_int32), ("window", ctypes.c_int32)]
 
 
 class _W(ctypes.Structure):
@@ -71,6 +71,9 @@ def load(path: str | None = None):
     lib.o_rope_table.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, _VP, _VP]
     lib.o_rope_apply.argtypes = [_VP, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _VP, _VP, _VP]
     lib.o_attend_row.argtypes = [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int, _VP]
+    lib.o_attend_row_range.argtypes = [_VP, _VP, _VP, ctypes.c_int, ctypes.c_int, ctypes.c_int, _VP]
+    lib.o_window_first_key.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.o_window_first_key.restype = ctypes.c_int
     lib.o_block_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_W), _VP, _VP, ctypes.c_int, _VP,
                                     ctypes.c_int, ctypes.c_int, _VP, _VP, _VP, ctypes.c_int, _VP, ctypes.c_int,
                                     _VP, ctypes.POINTER(_Inter), ctypes.POINTER(Counters)]
@@ -109,7 +112,7 @@ class Oracle:
         # bf16 storage: GEMM operands are rounded to bf16 (tirogla "Transformer
         # block", Implementation notes: bf16 GEMMs with fp32 accumulation)
         return _Cfg(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d // cfg.n_heads, cfg.d_ff, cfg.rope_base, cfg.rms_eps,
-                    1 if cfg.dtype == "bf16" else 0)
+                    1 if cfg.dtype == "bf16" else 0, int(getattr(cfg, "window", 0)))
 
     def _weights(self, w: dict):
         arrs = {n: self._f32(w[n]) for n in WEIGHT_NAMES}
@@ -151,12 +154,19 @@ class Oracle:
                               self._p(self._f32(sin_tab)))
         return v
 
-    def attend_row(self, q, kc, vc, n_keys):
+    def attend_row(self, q, kc, vc, n_keys, first_key=None):
+        """Attention of one query over keys [first_key, n_keys) (default: from 0)."""
         q, kc, vc = self._f32(q), self._f32(kc), self._f32(vc)
         dh = q.shape[-1]
         o = np.empty(dh, np.float32)
-        self.lib.o_attend_row(self._p(q), self._p(kc), self._p(vc), n_keys, dh, self._p(o))
+        if first_key is None:
+            self.lib.o_attend_row(self._p(q), self._p(kc), self._p(vc), n_keys, dh, self._p(o))
+        else:
+            self.lib.o_attend_row_range(self._p(q), self._p(kc), self._p(vc), first_key, n_keys, dh, self._p(o))
         return o
+
+    def window_first_key(self, p: int, window: int) -> int:
+        return int(self.lib.o_window_first_key(p, window))
 
     # ---- block ---------------------------------------------------------
     def block_forward(self, cfg, w: dict, x, start=None, kc=None, vc=None, rows=None, rope=None,

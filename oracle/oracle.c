@@ -44,6 +44,7 @@ typedef struct {
     int32_t d, n_heads, n_kv_heads, head_dim, d_ff;
     float rope_base, rms_eps;
     int32_t gemm_bf16;  /* 1: GEMM operands rounded to bf16 (see Precision above) */
+    int32_t window;     /* sliding window: keys per query, the query's own included; 0 = full causal */
 } o_config;
 
 /* fp32 -> nearest bf16 value (ties to even), returned widened to fp32.  A bf16
@@ -165,15 +166,15 @@ void o_rope_apply(float *v, int64_t rows, int heads, int dh, const int32_t *pos,
 /* SiLU: [TIR] Code (silu), z / (1 + e^-z). */
 static float silu(float z) { return z / (1.0f + expf(-z)); }
 
-/* One query row of one head against keys 0..n_keys-1 of its KV head:
+/* One query row of one head against keys j0..n_keys-1 of its KV head:
  * [TIR] How it works step 2 and Code (scores = q.k * scale, causal j <= i,
  * max-subtracted softmax in fp32, p = e/z, o += p v);
  * [MSA] 1.3 Scaled dot-product attention and 5.1 Causal masking.
  * kc, vc point at row 0 of the head's [t_max, dh] cache slab. */
-static void attend_row(const float *q, const float *kc, const float *vc, int n_keys, int dh, float scale,
+static void attend_row(const float *q, const float *kc, const float *vc, int j0, int n_keys, int dh, float scale,
                        float *o, float *s) {
     float m = -INFINITY;
-    for (int j = 0; j < n_keys; ++j) {
+    for (int j = j0; j < n_keys; ++j) {
         const float *kj = kc + (int64_t)j * dh;
         float dot = 0.0f;
         for (int e = 0; e < dh; ++e) dot += q[e] * kj[e];
@@ -181,23 +182,38 @@ static void attend_row(const float *q, const float *kc, const float *vc, int n_k
         if (s[j] > m) m = s[j];
     }
     float z = 0.0f;
-    for (int j = 0; j < n_keys; ++j) {
+    for (int j = j0; j < n_keys; ++j) {
         s[j] = expf(s[j] - m);
         z += s[j];
     }
     for (int e = 0; e < dh; ++e) o[e] = 0.0f;
-    for (int j = 0; j < n_keys; ++j) {
+    for (int j = j0; j < n_keys; ++j) {
         const float *vj = vc + (int64_t)j * dh;
         float p = s[j] / z;
         for (int e = 0; e < dh; ++e) o[e] += p * vj[e];
     }
 }
 
-/* Exported for the pins on attention alone (V = ones, T = 1, uniform scores). */
-void o_attend_row(const float *q, const float *kc, const float *vc, int n_keys, int dh, float *o) {
+/* First key a query at position p sees under a sliding window of W keys:
+ * [PID] Sliding-window attention (a query attends to the last W tokens, its
+ * own included: with W = 4096 the query at 10000 sees 5905..10000).
+ * W = 0 is full causal attention. */
+int o_window_first_key(int p, int window) {
+    if (window <= 0) return 0;
+    int j0 = p - window + 1;
+    return j0 > 0 ? j0 : 0;
+}
+
+/* Exported for the pins on attention alone (V = ones, T = 1, uniform scores,
+ * windows). */
+void o_attend_row_range(const float *q, const float *kc, const float *vc, int j0, int n_keys, int dh, float *o) {
     float *s = (float *)malloc(sizeof(float) * (size_t)(n_keys > 0 ? n_keys : 1));
-    attend_row(q, kc, vc, n_keys, dh, 1.0f / sqrtf((float)dh), o, s);
+    attend_row(q, kc, vc, j0, n_keys, dh, 1.0f / sqrtf((float)dh), o, s);
     free(s);
+}
+
+void o_attend_row(const float *q, const float *kc, const float *vc, int n_keys, int dh, float *o) {
+    o_attend_row_range(q, kc, vc, 0, n_keys, dh, o);
 }
 
 /*
@@ -296,7 +312,8 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
     free(v);
 
     /* Attention, one (row, head) at a time.  GQA: query head hd reads KV head
-     * hd / (H / Hkv) ([TIR] Code; [PID] Tiny example). */
+     * hd / (H / Hkv) ([TIR] Code; [PID] Tiny example).  With a sliding
+     * window, the query at position p reads keys from o_window_first_key. */
     const float scale = 1.0f / sqrtf((float)dh);
     float *att = (float *)malloc(sizeof(float) * R * qd);
     const int group = H / Hkv;
@@ -313,8 +330,10 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
             int p = pos_q[rr];
             const float *kcs = kc + ((int64_t)b * Hkv + kvh) * t_max * dh;
             const float *vcs = vc + ((int64_t)b * Hkv + kvh) * t_max * dh;
-            attend_row(q + rr * qd + (int64_t)hd * dh, kcs, vcs, p + 1, dh, scale, att + rr * qd + (int64_t)hd * dh, s);
-            qk += (int64_t)(p + 1) * dh;
+            const int j0 = o_window_first_key(p, cfg->window);
+            attend_row(q + rr * qd + (int64_t)hd * dh, kcs, vcs, j0, p + 1, dh, scale, att + rr * qd + (int64_t)hd * dh,
+                       s);
+            qk += (int64_t)(p + 1 - j0) * dh;
         }
         free(s);
     }

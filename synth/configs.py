@@ -43,6 +43,7 @@ class Config:
     decode_steps: int = 0
     w_sigma: float = 0.02
     x_sigma: float = 1.0
+    window: int = 0        # sliding-window attention: keys per query (0 = full causal)
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property

@@ -39,9 +39,9 @@ def activations(cfg: Config, B: int, T: int, name: str = "x", sigma: float | Non
                         cfg.dtype == "bf16")
 
 
-def small_cfg(d=64, H=4, Hkv=2, f=192, dtype="f32", base=10000.0, number=1, eps=1e-6):
+def small_cfg(d=64, H=4, Hkv=2, f=192, dtype="f32", base=10000.0, number=1, eps=1e-6, window=0):
     return Config("test", number, d=d, n_heads=H, n_kv_heads=Hkv, d_ff=f, rope_base=base, dtype=dtype,
-                  B=1, T=16, rms_eps=eps)
+                  B=1, T=16, rms_eps=eps, window=window)
 
 
 def rms(a) -> float:

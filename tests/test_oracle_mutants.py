@@ -45,12 +45,18 @@ MUTANTS = {
     "bf16_round_truncates": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
     "bf16_layer_output_not_rounded": ("operand_round(cfg, y, (last ? (int64_t)B * n_rows : M) * d);", ""),
     "bf16_final_norm_not_rounded": ("operand_round(cfg, hn, R * d);", ""),
+    # sliding window
+    "window_off_by_one": ("int j0 = p - window + 1;", "int j0 = p - window;"),
+    "window_ignored_in_block": ("const int j0 = o_window_first_key(p, cfg->window);", "const int j0 = 0;"),
 }
 
 PINS = [
     P.test_block_matches_fp64_library_composition,
     P.test_bf16_operands_match_fp64_composition,
     P.test_bf16_model_matches_fp64_composition,
+    P.test_sliding_window_first_key_matches_page_example,
+    P.test_sliding_window_attention_reads_exactly_the_window,
+    P.test_sliding_window_block_matches_fp64_band_mask,
     P.test_decode_matches_fp64_library_composition,
     P.test_decode_equals_prefill_bitwise,
     P.test_gqa_equals_mha_with_repeated_kv_bitwise,

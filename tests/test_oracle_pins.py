@@ -32,7 +32,7 @@ def _bf16(a):
     return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
 
 
-def torch_block_f64(cfg, w, x, start=0, bf16=False):
+def torch_block_f64(cfg, w, x, start=0, bf16=False, window=0):
     d, H, Hkv = cfg.d, cfg.n_heads, cfg.n_kv_heads
     dh = d // H
     rb = _bf16 if bf16 else (lambda a: a)
@@ -55,7 +55,14 @@ def torch_block_f64(cfg, w, x, start=0, bf16=False):
     g = H // Hkv
     K = k.repeat_interleave(g, dim=2).transpose(1, 2)
     V = v.repeat_interleave(g, dim=2).transpose(1, 2)
-    o = F.scaled_dot_product_attention(q.transpose(1, 2), K, V, is_causal=True)
+    if window:
+        # band mask: key j visible to query i iff i - window < j <= i
+        i = torch.arange(T)[:, None]
+        j = torch.arange(T)[None, :]
+        band = (j <= i) & (j > i - window)
+        o = F.scaled_dot_product_attention(q.transpose(1, 2), K, V, attn_mask=band)
+    else:
+        o = F.scaled_dot_product_attention(q.transpose(1, 2), K, V, is_causal=True)
     o = rb(o.transpose(1, 2).reshape(B, T, H * dh))
     r = X + o @ t(w["wo"])
     h2 = rb(F.rms_norm(r, (d,), weight=t(w["g_mlp"]), eps=cfg.rms_eps))
@@ -140,6 +147,67 @@ def test_bf16_operands_are_bf16_values(oracle):
     # the fp32 storage configuration rounds nothing
     _, i32 = oracle.block_forward(cfg.with_(dtype="f32"), w, x, intermediates=True)
     assert np.any(i32["act"].view(np.uint32) & 0xFFFF)
+
+
+def test_sliding_window_first_key_matches_page_example(oracle):
+    """[PID] Sliding-window attention: with W = 4096 the query at position
+    10000 attends to tokens 5905..10000; W = 0 is full causal attention."""
+    g = json.load(open(GOLDEN))["sliding_window_example"]
+    assert oracle.window_first_key(g["query"], g["window"]) == g["first_key"]
+    assert oracle.window_first_key(g["query"], 0) == 0
+    assert oracle.window_first_key(3, 10) == 0 and oracle.window_first_key(9, 1) == 9
+
+
+def test_sliding_window_attention_reads_exactly_the_window(oracle):
+    """q = 0 gives equal weights, so with v_j = (j, j^2, 1) the output is the
+    mean of j and of j^2 over the keys read: that fixes the key range."""
+    n, W = 40, 7
+    kc = np.random.default_rng(9).normal(size=(n, 16)).astype(np.float32)
+    j = np.arange(n, dtype=np.float64)
+    vc = np.zeros((n, 16), np.float32)
+    vc[:, 0], vc[:, 1], vc[:, 2] = j, j * j, 1.0
+    for p in (0, 3, 6, 7, 20, 39):
+        j0 = oracle.window_first_key(p, W)
+        o = oracle.attend_row(np.zeros(16, np.float32), kc, vc, p + 1, first_key=j0)
+        sel = j[j0:p + 1]
+        assert len(sel) == min(W, p + 1)
+        assert abs(o[0] - sel.mean()) <= 1e-5 * max(1.0, sel.mean())
+        assert abs(o[1] - (sel * sel).mean()) <= 1e-5 * max(1.0, (sel * sel).mean())
+        assert abs(o[2] - 1.0) <= 1e-6
+
+
+def test_sliding_window_block_matches_fp64_band_mask(oracle):
+    """The block with a window against SDPA with an explicit band mask; a
+    window at least T long is full causal attention, bitwise."""
+    for W in (1, 3, 8):
+        cfg = small_cfg(number=74, window=W)
+        w, _ = block_weights(cfg, gains="random")
+        x, _ = activations(cfg, 2, 13)
+        got, inter = oracle.block_forward(cfg, w, x, intermediates=True)
+        ref, rint = torch_block_f64(cfg, w, x, window=W)
+        assert rel_err(got, ref) <= 1e-5 and rel_err(inter["att"], rint["att"]) <= 1e-5
+        if W == 1:  # each query sees only itself: the attention output is its own v
+            v = np.stack([oracle.matmul(oracle.rms_norm(x[b], w["g_attn"], cfg.rms_eps), w["wv"]) for b in range(2)])
+            g = cfg.n_heads // cfg.n_kv_heads
+            v = v.reshape(2, 13, cfg.n_kv_heads, 1, cfg.head_dim).repeat(g, axis=3).reshape(2, 13, -1)
+            assert np.array_equal(inter["att"], v)
+    cfg = small_cfg(number=75)
+    w, _ = block_weights(cfg)
+    x, _ = activations(cfg, 1, 10)
+    assert np.array_equal(oracle.block_forward(cfg.with_(window=10), w, x), oracle.block_forward(cfg, w, x))
+
+
+def test_sliding_window_decode_equals_prefill_bitwise(oracle):
+    cfg = small_cfg(number=76, window=5)
+    w, _ = block_weights(cfg)
+    x, _ = activations(cfg, 1, 20)
+    full = oracle.block_forward(cfg, w, x)
+    kc = np.zeros((1, cfg.n_kv_heads, 20, cfg.head_dim), np.float32)
+    vc = kc.copy()
+    oracle.block_forward(cfg, w, x[:, :12], kc=kc, vc=vc)
+    for p in range(12, 20):
+        out = oracle.block_forward(cfg, w, x[:, p:p + 1], start=[p], kc=kc, vc=vc)
+        assert np.array_equal(out[0, 0], full[0, p])
 
 
 def test_decode_matches_fp64_library_composition(oracle):
