@@ -62,11 +62,17 @@ typedef enum { TFB_F32 = 0, TFB_BF16 = 1 } tfb_dtype;
 
 /* Block hyper-parameters (the page's notation).  rope_base is the RoPE
  * frequency base (10000 or 500000 in the workloads); rms_eps is the RMSNorm
- * epsilon inside the square root. */
+ * epsilon inside the square root.  window > 0 limits attention to a sliding
+ * window: the query at position p attends to keys p - window + 1 .. p, its own
+ * included (pidoku "The Transformer", Sliding-window attention); 0 is full
+ * causal attention.  The cache layout does not change with a window: rows
+ * stay at their absolute positions, and rows below a query's window are not
+ * read. */
 typedef struct {
     int32_t d, n_heads, n_kv_heads, head_dim, d_ff;
     float rope_base, rms_eps;
-    int32_t dtype; /* tfb_dtype */
+    int32_t dtype;  /* tfb_dtype */
+    int32_t window; /* keys per query; 0 = full causal */
 } tfb_block_config;
 
 /* One block's weights, all in the config's storage type, [in, out] layout:

@@ -319,3 +319,101 @@ def test_chunked_prefill_matches_full_prefill(oracle, dtype, chunks):
     ref = oracle.block_forward(cfg, w32, x32)
     assert rel_err(got, ref) <= tol(cfg), rel_err(got, ref)
     assert np.isnan(widen_cache(kc)[:, :, T:]).all()
+
+
+# ---- sliding-window attention (pidoku "The Transformer", Sliding-window attention)
+@pytest.mark.parametrize("dtype,d,H,Hkv,T,W", [
+    ("f32", 64, 4, 2, 40, 7),
+    ("bf16", 256, 4, 2, 200, 1),     # dh = 64; each query sees only itself
+    ("bf16", 256, 4, 2, 200, 37),    # window edge inside tiles
+    ("bf16", 512, 4, 1, 300, 128),   # dh = 128, MQA, window = two key tiles
+    ("bf16", 512, 4, 4, 130, 500),   # window longer than the sequence
+])
+def test_sliding_window_prefill(oracle, dtype, d, H, Hkv, T, W):
+    torch = _torch()
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype=dtype, number=110, window=W)
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg)
+    x32, x = dev_x(cfg, 2, T)
+    rope = tfb.rope_table_init(tc, T)
+    kc, vc = new_cache(cfg, 2, T)
+    out = torch.empty_like(x)
+    print("case: window prefill", dtype, d, H, Hkv, T, W, flush=True)
+    tfb.block_prefill(tc, w, rope, x, out, cache=(kc, vc))
+    torch.cuda.synchronize()
+    okc = np.zeros((2, Hkv, T, d // H), np.float32)
+    ovc = okc.copy()
+    ref = oracle.block_forward(cfg, w32, x32, kc=okc, vc=ovc)
+    assert rel_err(to_np(out), ref) <= tol(cfg), rel_err(to_np(out), ref)
+    assert cache_ok(cfg, widen_cache(kc), okc)
+
+
+def test_sliding_window_chunked_prefill_and_decode(oracle):
+    """Chunks and decode steps past the window: rows below every query's
+    window are NaN in the cache and must never be read."""
+    torch = _torch()
+    cfg = small_cfg(d=256, H=4, Hkv=2, f=512, dtype="bf16", number=111, window=50)
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg)
+    T, steps = 160, 4
+    x32, x = dev_x(cfg, 2, T + steps)
+    t_max = T + steps
+    rope = tfb.rope_table_init(tc, t_max)
+    kc, vc = new_cache(cfg, 2, t_max)
+    print("case: window chunked prefill + decode", flush=True)
+    o1 = torch.empty((2, 100, cfg.d), dtype=x.dtype, device="cuda")
+    tfb.block_prefill(tc, w, rope, x[:, :100].contiguous(), o1, cache=(kc, vc))
+    torch.cuda.synchronize()
+    # poison rows 0..49: the chunk below starts at 100, so its earliest window starts at 51
+    kc[:, :, :50] = float("nan")
+    vc[:, :, :50] = float("nan")
+    o2 = torch.empty((2, 60, cfg.d), dtype=x.dtype, device="cuda")
+    tfb.block_prefill(tc, w, rope, x[:, 100:T].contiguous(), o2, start_pos=100, cache=(kc, vc))
+    dec = []
+    for s in range(steps):
+        o = torch.empty((2, 1, cfg.d), dtype=x.dtype, device="cuda")
+        pos = torch.full((2,), T + s, dtype=torch.int32, device="cuda")
+        tfb.block_decode(tc, w, rope, x[:, T + s:T + s + 1].contiguous(), o, (kc, vc), pos, T + s)
+        dec.append(to_np(o))
+    torch.cuda.synchronize()
+    got = np.concatenate([to_np(o1), to_np(o2)] + dec, axis=1)
+    ref = oracle.block_forward(cfg, w32, x32)
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= tol(cfg), rel_err(got, ref)
+
+
+@pytest.mark.parametrize("lens,W", [([1100, 4000, 2500, 700], 1000), ([3000, 513], 4096), ([2048, 2049], 1)])
+def test_sliding_window_decode_long_cache(oracle, lens, W):
+    """Split-KV decode over the window of long caches (NaN below the window
+    would poison the result if read)."""
+    torch = _torch()
+    import synth
+    from tests.gpu_util import to_dev
+    cfg = small_cfg(d=512, H=4, Hkv=1, f=1024, dtype="bf16", base=500000.0, number=112, window=W)
+    tc = tfb.Config.of(cfg)
+    B, dh = len(lens), cfg.head_dim
+    t_max = max(lens) + 8
+    shape = (B, 1, t_max, dh)
+    kf, kb = synth.normal(cfg.seed, 11, shape, 1.0, True)
+    vf, vb = synth.normal(cfg.seed, 12, shape, 1.0, True)
+    rows = np.arange(t_max)[None, None, :, None]
+    L = np.array(lens)[:, None, None, None]
+    valid = (rows < L) & (rows >= L + 1 - W)  # the window of the new token at position len
+    kb = np.where(valid, kb, np.uint16(0x7FC0))
+    vb = np.where(valid, vb, np.uint16(0x7FC0))
+    kf = np.where(valid, kf, np.nan).astype(np.float32)
+    vf = np.where(valid, vf, np.nan).astype(np.float32)
+    kc, vc = to_dev(kf, kb), to_dev(vf, vb)
+    w32, w = dev_weights(cfg)
+    x32, x = dev_x(cfg, B, 1)
+    rope = tfb.rope_table_init(tc, t_max)
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(x)
+    print("case: window decode", lens, W, flush=True)
+    tfb.block_decode(tc, w, rope, x, o, (kc, vc), pos, max(lens))
+    torch.cuda.synchronize()
+    okc, ovc = kf.copy(), vf.copy()
+    ref = oracle.block_forward(cfg, w32, x32, start=np.array(lens, np.int32), kc=okc, vc=ovc)
+    got = to_np(o)
+    assert np.isfinite(got).all() and np.isfinite(ref).all()
+    assert rel_err(got, ref) <= 2e-2

@@ -84,6 +84,7 @@ tfb_status check_cfg(const tfb_block_config *c) {
     if (c->n_heads % c->n_kv_heads != 0 || c->n_heads * c->head_dim != c->d || (c->head_dim & 1)) return TFB_ERR_SHAPE;
     if (!(c->rope_base > 0.0f) || !(c->rms_eps >= 0.0f) || !isfinite(c->rope_base) || !isfinite(c->rms_eps))
         return TFB_ERR_SHAPE;
+    if (c->window < 0) return TFB_ERR_SHAPE;
     if (c->dtype == TFB_BF16) {
         if (c->d % 64 || c->d_ff % 64 || (c->head_dim != 64 && c->head_dim != 128)) return TFB_ERR_SHAPE;
     } else {
@@ -197,6 +198,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
     a.max_keys = pos ? max_pos + 1 : start + T;
     a.max_splits = kMaxSplits;
+    a.window = c.window;
     TRY_HIP(STAGE(ST_ATTN, pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s)));
 
     GemmCall o{};

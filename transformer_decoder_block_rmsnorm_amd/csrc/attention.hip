@@ -9,6 +9,8 @@
 // head h reads KV head h / (H / Hkv): consecutive query heads share a KV head
 // ([TIR] Code, the GQA index in Block::forward).  Softmax in fp32 with a running maximum ([TIR]
 // Implementation notes; [MSA] 1.3).
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace tfb {
@@ -41,8 +43,10 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
     const T *K = (const T *)a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * a.dh;
     const T *V = (const T *)a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * a.dh;
 
+    // sliding window: keys from p - window + 1 ([PID] Sliding-window attention)
+    const int k_first = a.window > 0 ? max(0, p - a.window + 1) : 0;
     float m = -INFINITY, l = 0.0f, o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j0 = 0; j0 < n_keys; j0 += 64) {
+    for (int j0 = k_first; j0 < n_keys; j0 += 64) {
         const int j = j0 + lane;
         float s = -INFINITY;
         if (j < n_keys) {
@@ -95,13 +99,15 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
 //                                  which the accumulator holds them.
 // Tiles entirely above the causal diagonal are skipped per wave; the
 // workgroups with the longest key ranges are scheduled first.  Keys at or
-// beyond start + T are zero-filled in LDS, so unwritten cache rows (even NaN)
-// never reach the result.
+// beyond start + T, and (sliding window) below the earliest window of the
+// workgroup, are zero-filled in LDS, so cache rows no query may read (even
+// NaN) never reach the result.
 // ---------------------------------------------------------------------------
 struct FlashArgs {
     const bf16_t *q, *kc, *vc;
     bf16_t *o;
     int B, T, H, Hkv, t_max, start;
+    int window;  // keys per query (0: full causal)
     int HG, PB, n_qblocks, n_hsub;
     float scale_log2e;
 };
@@ -140,6 +146,13 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     const int n_tiles = (a.start + t_last_wg) / BKV + 1;
     const bool wave_active = t0 < a.T;
     const int wave_tiles = wave_active ? (a.start + min(t0 + 31, a.T - 1)) / BKV + 1 : 0;
+    // sliding window: query position p sees keys from p - window + 1, so
+    // tiles below the earliest query's window are never loaded, and a wave
+    // skips tiles below its own earliest query's window
+    const int W = a.window;
+    const int key_floor = W > 0 ? max(0, a.start + qb * a.PB - W + 1) : 0;  // no query here reads below it
+    const int first_tile = key_floor / BKV;
+    const int wave_first_tile = W > 0 ? max(0, a.start + t0 - W + 1) / BKV : 0;
 
     // q fragments (B operand of S^T): row t0 + lr, dh [16s + 8lh, +8)
     bf16x8 qf[NS];
@@ -163,14 +176,16 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
         for (int i = 0; i < K_PER; ++i) {
             const int c = tid + 256 * i, key = c / KCH, ch = c % KCH, j = j0 + key;
-            rk[i] = (j < kv_len) ? *(const u32x4 *)(Kg + (int64_t)j * DH + ch * 8) : u32x4{0, 0, 0, 0};
+            rk[i] = (j < kv_len && j >= key_floor) ? *(const u32x4 *)(Kg + (int64_t)j * DH + ch * 8)
+                                                   : u32x4{0, 0, 0, 0};
         }
         if (tid < NVB) {
             const int kb = tid / (DH / 8), eb = tid % (DH / 8);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int j = j0 + kb * 8 + r;
-                rv[r] = (j < kv_len) ? *(const u32x4 *)(Vg + (int64_t)j * DH + eb * 8) : u32x4{0, 0, 0, 0};
+                rv[r] = (j < kv_len && j >= key_floor) ? *(const u32x4 *)(Vg + (int64_t)j * DH + eb * 8)
+                                                       : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -204,13 +219,13 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
         for (int v = 0; v < 16; ++v) oacc[te][v] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    load_tile(0);
+    load_tile(first_tile);
     store_tile(0);
     __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-        const int bf = it & 1;
+    for (int it = first_tile; it < n_tiles; ++it) {
+        const int bf = (it - first_tile) & 1;
         if (it + 1 < n_tiles) load_tile(it + 1);
-        if (it < wave_tiles) {
+        if (it < wave_tiles && it >= wave_first_tile) {
             const int j0 = it * BKV;
             f32x16 sacc[2];
 #pragma unroll
@@ -226,7 +241,9 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
                 }
             }
             // online softmax in the log2 domain
-            const bool need_mask = (j0 + BKV - 1 > a.start + t0);
+            // the diagonal crosses this tile, or (window) its lower edge does
+            const bool need_mask = (j0 + BKV - 1 > a.start + t0) || (W > 0 && j0 < a.start + t0 + 31 - W + 1);
+            const int key_lo = W > 0 ? qpos - W + 1 : 0;
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
                     float x = sacc[kt][v] * a.scale_log2e;
                     if (need_mask) {
                         const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                        if (key > qpos) x = -INFINITY;
+                        if (key > qpos || key < key_lo) x = -INFINITY;
                     }
                     sacc[kt][v] = x;
                     mx = fmaxf(mx, x);
@@ -311,6 +328,7 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     a.vc = (const bf16_t *)c.vc;
     a.o = (bf16_t *)c.o;
     a.B = c.B; a.T = c.T; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max; a.start = c.start;
+    a.window = c.window;
     const int G = c.H / c.Hkv;
     a.HG = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
     if (G % a.HG) a.HG = 1;
@@ -344,6 +362,7 @@ struct DecArgs {
     const int32_t *pos;
     float *part;      // [B][H][max_chunks][DH + 4]
     int B, H, Hkv, t_max, max_chunks, chunk_keys;
+    int window;       // keys per query (0: full causal)
     float scale_log2e;
 };
 
@@ -368,7 +387,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     const int ln = lane & 15, g4 = lane >> 4;
     const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int n_keys = min(a.pos[b] + 1, a.t_max);
-    const int k_begin = ch * a.chunk_keys;
+    // keys [k_first, n_keys): all of them, or the last `window` ones
+    const int k_first = a.window > 0 ? max(0, n_keys - a.window) : 0;
+    const int k_begin = k_first + ch * a.chunk_keys;
     if (k_begin >= n_keys) return;  // whole block leaves before any barrier
     const int k_end = min(n_keys, k_begin + a.chunk_keys);
     const int h0 = kvh * G;
@@ -505,7 +526,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
     if (bh >= a.B * a.H) return;
     const int b = bh / a.H;
     const int n_keys = min(a.pos[b] + 1, a.t_max);
-    const int n_ch = min((n_keys + a.chunk_keys - 1) / a.chunk_keys, a.max_chunks);
+    const int n_range = a.window > 0 ? min(n_keys, a.window) : n_keys;
+    const int n_ch = min((n_range + a.chunk_keys - 1) / a.chunk_keys, a.max_chunks);
     const float *base = a.part + (int64_t)bh * a.max_chunks * (DH + 4);
     float M = -INFINITY;
     for (int c = 0; c < n_ch; ++c) M = fmaxf(M, base[c * (DH + 4)]);
@@ -560,7 +582,8 @@ static hipError_t split_decode_launch(const AttnCall &c, hipStream_t s) {
     a.B = c.B; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max;
     // chunk size: kDecChunk keys, grown in steps of kDecChunk when the longest
     // sequence would need more chunks than the partial buffer holds
-    const int max_keys = c.max_keys;
+    const int max_keys = c.window > 0 ? std::min(c.max_keys, c.window) : c.max_keys;
+    a.window = c.window;
     int chunks = (max_keys + kDecChunk - 1) / kDecChunk;
     int chunk_keys = kDecChunk;
     if (chunks > c.max_splits) {

@@ -53,6 +53,7 @@ struct AttnCall {
     size_t partial_bytes;
     int max_keys;         // host bound on keys per query (for work sizing)
     int max_splits;       // chunks per (b, h) the partial buffer holds
+    int window;           // sliding window: keys per query (0: full causal)
 };
 hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
