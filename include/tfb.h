@@ -131,6 +131,24 @@ tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weight
                              int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T, int32_t start_pos,
                              tfb_kv_cache *cache, void *ws, size_t ws_bytes, void *stream);
 
+/* Batched prefill of sequences of different lengths and start positions
+ * (variable-length, right-padded): row t of sequence b holds a real token
+ * when t < len[b], at absolute position start[b] + t, and is padding
+ * otherwise.  A real token attends to rows 0..start[b]+t of its own
+ * sequence's cache, so it never attends to a pad key (the tirogla page's
+ * Pitfalls: pad tokens must be masked in batched prefill); padding rows write
+ * nothing to the cache, and their rows of out hold unspecified values.
+ * x, out: [B, T, d]; start, len: [B] int32, device, read-only, with
+ * 0 <= len[b] <= T; rows 0..start[b]-1 of the cache must already hold the
+ * sequence's earlier keys and values.  h_max_end: host upper bound of
+ * max_b (start[b] + len[b]), at most cache t_max and t_max_table (checked;
+ * the device values are trusted to respect it).  Other arguments as
+ * tfb_block_prefill; the workspace is tfb_workspace_bytes(cfg, B, T, 0). */
+tfb_status tfb_block_prefill_varlen(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                    int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T,
+                                    const int32_t *start, const int32_t *len, int32_t h_max_end, tfb_kv_cache *cache,
+                                    void *ws, size_t ws_bytes, void *stream);
+
 /* One decode step of one block for B sequences: each new token's q
  * [B, H, 1, dh] attends over its sequence's cache (KV cache paragraph of
  * How it works).  x, out: [B, 1, d], out may alias x.  pos: [B] int32 (device,

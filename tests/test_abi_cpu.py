@@ -108,6 +108,28 @@ def test_prefill_rejects_invalid_arguments():
     f32 = _cfg(d=64, n_heads=4, n_kv_heads=2, d_ff=192, dtype="f32").c()
     f32.head_dim = 15
     assert _prefill(f32) == -2
+    neg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()
+    neg.window = -1
+    assert _prefill(neg) == -2                      # a window is a key count >= 0
+
+
+def test_varlen_prefill_rejects_invalid_arguments():
+    lib = tfb.lib()
+    cfg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()
+    w = _weights()
+    cache = tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 2, 32)
+
+    def run(h_max=20, t_tab=64, start=FAKE, lens=FAKE, B=2, T=8, kv=True, ws_n=1 << 40):
+        return lib.tfb_block_prefill_varlen(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(FAKE), t_tab,
+                                            ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), B, T,
+                                            ctypes.c_void_p(start), ctypes.c_void_p(lens), h_max,
+                                            ctypes.byref(cache) if kv else None, ctypes.c_void_p(FAKE), ws_n, None)
+    assert run(h_max=33) == -6                      # beyond the cache
+    assert run(h_max=30, t_tab=16) == -6            # beyond the RoPE table
+    assert run(start=0) == -1 and run(lens=0) == -1 and run(kv=False) == -1
+    assert run(B=3) == -2                           # cache batch != B
+    assert run(T=0) == -2 and run(h_max=-1) == -2
+    assert run(ws_n=16) == -5
 
 
 def test_decode_and_append_reject_invalid_arguments():

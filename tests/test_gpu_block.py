@@ -417,3 +417,59 @@ def test_sliding_window_decode_long_cache(oracle, lens, W):
     got = to_np(o)
     assert np.isfinite(got).all() and np.isfinite(ref).all()
     assert rel_err(got, ref) <= 2e-2
+
+
+# ---- variable-length batched prefill (tirogla "Transformer block", Pitfalls:
+# pad tokens must not be attended to in batched prefill)
+@pytest.mark.parametrize("dtype,d,H,Hkv,W", [("f32", 64, 4, 2, 0), ("bf16", 512, 4, 2, 0), ("bf16", 256, 4, 1, 30)])
+def test_varlen_prefill_matches_per_sequence(oracle, dtype, d, H, Hkv, W):
+    """Three right-padded sequences with their own starts and lengths (one
+    empty) in one call; each real row must match that sequence alone."""
+    torch = _torch()
+    from tests.gpu_util import to_dev
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype=dtype, number=120, window=W)
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg)
+    B, T = 3, 100
+    starts, lens = np.array([0, 20, 64], np.int32), np.array([100, 37, 0], np.int32)
+    t_max = int((starts + lens).max()) + 5
+    dh = d // H
+    xall32, xall = dev_x(cfg, B, int(starts.max()) + T)
+    # earlier rows of each sequence: keys and values from the oracle, so both
+    # sides start from the same cache
+    okc = np.full((B, Hkv, t_max, dh), np.nan, np.float32)
+    ovc = okc.copy()
+    for b in range(B):
+        if starts[b]:
+            kb, vb = okc[b:b + 1].copy(), ovc[b:b + 1].copy()
+            oracle.block_forward(cfg, w32, xall32[b:b + 1, :starts[b]], kc=kb, vc=vb)
+            okc[b], ovc[b] = kb[0], vb[0]
+    bits = None
+    if dtype == "bf16":
+        import synth
+        bits = [synth.to_bf16(a)[0] for a in (okc, ovc)]
+    kc = to_dev(okc, None if bits is None else bits[0])
+    vc = to_dev(ovc, None if bits is None else bits[1])
+    x32 = np.zeros((B, T, d), np.float32)
+    for b in range(B):
+        x32[b] = xall32[b, starts[b]:starts[b] + T]
+    x = torch.stack([xall[b, starts[b]:starts[b] + T] for b in range(B)]).contiguous()
+    rope = tfb.rope_table_init(tc, t_max)
+    out = torch.empty_like(x)
+    st = torch.from_numpy(starts).cuda()
+    ln = torch.from_numpy(lens).cuda()
+    print("case: varlen prefill", dtype, d, H, Hkv, W, flush=True)
+    tfb.block_prefill_varlen(tc, w, rope, x, out, st, ln, int((starts + lens).max()), (kc, vc))
+    torch.cuda.synchronize()
+    got, gk = to_np(out), widen_cache(kc)
+    for b in range(B):
+        n = int(lens[b])
+        kb, vb = okc[b:b + 1].copy(), ovc[b:b + 1].copy()
+        if n:
+            ref = oracle.block_forward(cfg, w32, x32[b:b + 1, :n], start=[int(starts[b])], kc=kb, vc=vb)
+            assert rel_err(got[b, :n], ref[0]) <= tol(cfg), (b, rel_err(got[b, :n], ref[0]))
+            s0 = int(starts[b])
+            assert cache_ok(cfg, gk[b, :, s0:s0 + n], kb[0, :, s0:s0 + n])
+        # padding rows write nothing; earlier rows are untouched
+        assert np.isnan(gk[b, :, int(starts[b] + lens[b]):]).all()
+        assert np.array_equal(gk[b, :, :int(starts[b])], okc[b, :, :int(starts[b])])

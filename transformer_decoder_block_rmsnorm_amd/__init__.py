@@ -19,7 +19,7 @@ TFB_F32, TFB_BF16 = 0, 1
 STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTYPE", -4: "TFB_ERR_ALIGN",
           -5: "TFB_ERR_WORKSPACE", -6: "TFB_ERR_CACHE_OVERFLOW", -7: "TFB_ERR_HIP", -8: "TFB_ERR_UNSUPPORTED"}
 EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
-           "tfb_model_forward", "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
+           "tfb_model_forward", "tfb_block_prefill_varlen", "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
            "tfb_profile_stages", "tfb_profile_stage_name")
 
 _VP = ctypes.c_void_p
@@ -70,6 +70,9 @@ def lib():
         L.tfb_block_prefill.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.POINTER(KVCache), _VP, ctypes.c_size_t, _VP]
+        L.tfb_block_prefill_varlen.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
+                                               ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP,
+                                               ctypes.c_int32, ctypes.POINTER(KVCache), _VP, ctypes.c_size_t, _VP]
         L.tfb_block_decode.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
                                        ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.POINTER(KVCache), _VP,
                                        ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
@@ -79,7 +82,7 @@ def lib():
                                         ctypes.c_int32, ctypes.POINTER(KVCache), _VP, ctypes.c_int32, _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
         for f in ("tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
-                  "tfb_model_forward"):
+                  "tfb_model_forward", "tfb_block_prefill_varlen"):
             getattr(L, f).restype = ctypes.c_int
         L.tfb_status_string.argtypes = [ctypes.c_int]
         L.tfb_status_string.restype = ctypes.c_char_p
@@ -176,6 +179,20 @@ def block_prefill(cfg: Config, w: dict, rope, x, out, start_pos: int = 0, cache=
     _check(lib().tfb_block_prefill(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
                                    rope.shape[0], _ptr(x), _ptr(out), B, T, start_pos, kv, _ptr(ws), ws_n,
                                    _stream()), "tfb_block_prefill")
+    return out
+
+
+def block_prefill_varlen(cfg: Config, w: dict, rope, x, out, start, lens, max_end: int, cache, ws=None):
+    """Right-padded batched prefill: sequence b has lens[b] real rows at positions
+    start[b] + t.  start, lens: int32 [B] device tensors; max_end >= max(start + lens)."""
+    B, T, _ = x.shape
+    if ws is None:
+        ws = workspace(cfg, B, T)
+    kv = ctypes.byref(cache_struct(*cache))
+    ws_n = ws.numel() * ws.element_size()
+    _check(lib().tfb_block_prefill_varlen(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
+                                          rope.shape[0], _ptr(x), _ptr(out), B, T, _ptr(start), _ptr(lens), max_end,
+                                          kv, _ptr(ws), ws_n, _stream()), "tfb_block_prefill_varlen")
     return out
 
 

@@ -158,7 +158,8 @@ hipError_t staged(int stage, hipStream_t s, F &&launch) {
 tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
                      int max_pos, const void *x,
                      void *out, int B, int T, int start, const int32_t *pos, void *kc, void *vc, int t_max,
-                     uint8_t *ws, const WsLayout &L, hipStream_t s) {
+                     uint8_t *ws, const WsLayout &L, hipStream_t s, const int32_t *starts = nullptr,
+                     const int32_t *lens = nullptr) {
     const int M = B * T, d = c.d, H = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, f = c.d_ff;
     const int qd = H * dh, kvd = Hkv * dh;
     void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
@@ -183,6 +184,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.ep.rope_rows = rope_rows;
     g.ep.pos = pos;
     g.ep.T = T; g.ep.H = H; g.ep.Hkv = Hkv; g.ep.dh = dh; g.ep.t_max = t_max; g.ep.start = start;
+    g.ep.starts = starts;
+    g.ep.lens = lens;
     g.scratch = L.skinny_bytes ? ws + L.skinny : nullptr;
     g.scratch_bytes = L.skinny_bytes;
     g.split_scratch = L.gsplit_bytes ? ws + L.gsplit : nullptr;
@@ -193,6 +196,8 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.dtype = c.dtype;
     a.q = q; a.kc = kc; a.vc = vc; a.o = att; a.pos = pos;
     a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.dh = dh; a.t_max = t_max; a.start = start;
+    a.starts = starts;
+    a.lens = lens;
     a.scale = 1.0f / sqrtf((float)dh);
     a.partials = ws + L.part;
     a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
@@ -339,6 +344,25 @@ tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weight
     const int t_max = cache ? cache->t_max : T;
     return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, start_pos, nullptr, kc, vc, t_max, wsb, L,
                      (hipStream_t)stream);
+}
+
+tfb_status tfb_block_prefill_varlen(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                    int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T,
+                                    const int32_t *start, const int32_t *len, int32_t h_max_end, tfb_kv_cache *cache,
+                                    void *ws, size_t ws_bytes, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if ((st = check_weights(w)) != TFB_OK) return st;
+    if (!rope_table || !x || !out || !cache || !start || !len) return TFB_ERR_NULL;
+    if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
+    if (B <= 0 || T <= 0 || h_max_end < 0) return TFB_ERR_SHAPE;
+    if ((st = check_cache(cache, B)) != TFB_OK) return st;
+    if (h_max_end > cache->t_max || h_max_end > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    const WsLayout L = ws_layout(*cfg, B, T, 0);
+    if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
+    if (!aligned(ws)) return TFB_ERR_ALIGN;
+    return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, 0, nullptr, cache->k, cache->v,
+                     cache->t_max, (uint8_t *)ws, L, (hipStream_t)stream, start, len);
 }
 
 tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,

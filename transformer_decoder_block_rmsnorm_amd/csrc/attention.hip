@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
     __syncthreads();
     if (!valid) return;
 
-    int p = a.pos ? a.pos[b] : a.start + t;
+    if (a.lens && t >= a.lens[b]) return;  // padding row (after the only barrier)
+    int p = a.pos ? a.pos[b] : (a.starts ? a.starts[b] : a.start) + t;
     if (p >= a.t_max) p = a.t_max - 1;  // never read past the cache
     const int n_keys = p + 1;
     const int kvh = h / (a.H / a.Hkv);
@@ -107,6 +108,7 @@ struct FlashArgs {
     const bf16_t *q, *kc, *vc;
     bf16_t *o;
     int B, T, H, Hkv, t_max, start;
+    const int32_t *starts, *lens;  // varlen: [B] first position and valid rows (NULL: start, T)
     int window;  // keys per query (0: full causal)
     int HG, PB, n_qblocks, n_hsub;
     float scale_log2e;
@@ -141,32 +143,36 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     const int hl = wave % a.HG, pw = wave / a.HG;
     const int h = kvh * G + hsub * a.HG + hl;
     const int t0 = qb * a.PB + pw * 32;
-    const int kv_len = a.start + a.T;
-    const int t_last_wg = min(qb * a.PB + a.PB - 1, a.T - 1);
-    const int n_tiles = (a.start + t_last_wg) / BKV + 1;
-    const bool wave_active = t0 < a.T;
-    const int wave_tiles = wave_active ? (a.start + min(t0 + 31, a.T - 1)) / BKV + 1 : 0;
+    // this sequence: rows 0..Tb-1 at positions start+0.. (varlen: its own start and length)
+    const int start = a.starts ? a.starts[b] : a.start;
+    const int Tb = a.lens ? min(a.lens[b], a.T) : a.T;
+    if (qb * a.PB >= Tb) return;  // only padding rows here: the whole block leaves before any barrier
+    const int kv_len = start + Tb;
+    const int t_last_wg = min(qb * a.PB + a.PB - 1, Tb - 1);
+    const int n_tiles = (start + t_last_wg) / BKV + 1;
+    const bool wave_active = t0 < Tb;
+    const int wave_tiles = wave_active ? (start + min(t0 + 31, Tb - 1)) / BKV + 1 : 0;
     // sliding window: query position p sees keys from p - window + 1, so
     // tiles below the earliest query's window are never loaded, and a wave
     // skips tiles below its own earliest query's window
     const int W = a.window;
-    const int key_floor = W > 0 ? max(0, a.start + qb * a.PB - W + 1) : 0;  // no query here reads below it
+    const int key_floor = W > 0 ? max(0, start + qb * a.PB - W + 1) : 0;  // no query here reads below it
     const int first_tile = key_floor / BKV;
-    const int wave_first_tile = W > 0 ? max(0, a.start + t0 - W + 1) / BKV : 0;
+    const int wave_first_tile = W > 0 ? max(0, start + t0 - W + 1) / BKV : 0;
 
     // q fragments (B operand of S^T): row t0 + lr, dh [16s + 8lh, +8)
     bf16x8 qf[NS];
     {
         const int t = t0 + lr;
-        const bf16_t *qrow = a.q + (((int64_t)b * a.H + h) * a.T + min(t, a.T - 1)) * DH;
+        const bf16_t *qrow = a.q + (((int64_t)b * a.H + h) * a.T + min(t, Tb - 1)) * DH;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             u32x4 v = *(const u32x4 *)(qrow + 16 * s + 8 * lh);
-            if (t >= a.T) v = u32x4{0, 0, 0, 0};
+            if (t >= Tb) v = u32x4{0, 0, 0, 0};
             qf[s] = as_bf16x8(v);
         }
     }
-    const int qpos = a.start + t0 + lr;
+    const int qpos = start + t0 + lr;
     const bf16_t *Kg = a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
     const bf16_t *Vg = a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
 
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
             }
             // online softmax in the log2 domain
             // the diagonal crosses this tile, or (window) its lower edge does
-            const bool need_mask = (j0 + BKV - 1 > a.start + t0) || (W > 0 && j0 < a.start + t0 + 31 - W + 1);
+            const bool need_mask = (j0 + BKV - 1 > start + t0) || (W > 0 && j0 < start + t0 + 31 - W + 1);
             const int key_lo = W > 0 ? qpos - W + 1 : 0;
             float mx = -INFINITY;
 #pragma unroll
@@ -305,7 +311,7 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     }
 
     const int t = t0 + lr;
-    if (wave_active && t < a.T) {
+    if (wave_active && t < Tb) {
         const float inv = 1.0f / l_run;
         bf16_t *orow = a.o + ((int64_t)b * a.T + t) * ((int64_t)a.H * DH) + (int64_t)h * DH;
 #pragma unroll
@@ -328,6 +334,8 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     a.vc = (const bf16_t *)c.vc;
     a.o = (bf16_t *)c.o;
     a.B = c.B; a.T = c.T; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max; a.start = c.start;
+    a.starts = c.starts;
+    a.lens = c.lens;
     a.window = c.window;
     const int G = c.H / c.Hkv;
     a.HG = G >= 4 ? 4 : (G >= 2 ? 2 : 1);

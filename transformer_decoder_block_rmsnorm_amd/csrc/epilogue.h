@@ -23,6 +23,8 @@ struct EpiParams {
     void *q, *kc, *vc;       // q [B,H,T,dh]; caches [B,Hkv,t_max,dh]
     const float *rope;       // [t_max_table][dh/2][2] (cos, sin)
     const int32_t *pos;      // decode: [B] positions (T == 1); NULL: start + t
+    const int32_t *starts;   // varlen prefill: [B] position of row 0 (NULL: start)
+    const int32_t *lens;     // varlen prefill: [B] valid rows; later rows are padding (NULL: all T)
     int T, H, Hkv, dh, t_max, start;
     int rope_rows;           // rows of the RoPE table (device positions are clamped to it)
 };
@@ -31,7 +33,7 @@ struct EpiParams {
 __device__ __forceinline__ void qkv_row(const EpiParams &p, int m, int &b, int &t, int &ps) {
     b = m / p.T;
     t = m - b * p.T;
-    ps = p.pos ? p.pos[b] : p.start + t;
+    ps = p.pos ? p.pos[b] : (p.starts ? p.starts[b] : p.start) + t;
 }
 
 // Store the pair of output columns (c, c+1), c even, of row m.
@@ -83,6 +85,7 @@ __device__ __forceinline__ void epi_store_pair(const EpiParams &p, int m, int c,
             Elem<T>::store(q, iq + 1, v1);
         } else {
             if (ps < 0 || ps >= p.t_max) return;  // never write outside the cache
+            if (p.lens && t >= p.lens[b]) return;  // padding rows leave the cache alone
             int cc = c - qd;
             T *dst = (T *)p.kc;
             if (cc >= kvd) { cc -= kvd; dst = (T *)p.vc; }

@@ -47,6 +47,7 @@ struct AttnCall {
     const void *kc, *vc;  // [B, Hkv, t_max, dh]
     void *o;              // [B, T, H*dh]
     const int32_t *pos;   // decode positions or NULL
+    const int32_t *starts, *lens;  // varlen prefill: [B] first position, valid rows (NULL: start, T)
     int B, T, H, Hkv, dh, t_max, start;
     float scale;
     void *partials;       // split-KV scratch (decode), may be NULL
