@@ -106,6 +106,25 @@ typedef struct {
     const void *w_unembed;
 } tfb_model;
 
+/* A paged KV cache (tirogla "Transformer block", Implementation notes: a
+ * cache allocated in fixed-size blocks per sequence rather than one T_max
+ * buffer per request).  k, v: pools [n_blocks, Hkv, block_size, dh] in the
+ * config's storage type, device; post-RoPE keys and values as in
+ * tfb_kv_cache.  block_table: [batch, max_blocks] int32, device, read-only:
+ * row (position) p of sequence b is row p % block_size of pool block
+ * block_table[b][p / block_size].  block_size is a power of two in
+ * [8, 65536]; a sequence holds up to max_blocks * block_size positions.
+ * Table entries must lie in [0, n_blocks) and the blocks of different live
+ * sequences must not overlap (device data, not checked on the host: an
+ * entry outside the range is clamped into it, so no access leaves the
+ * pool).  The caller owns the pools and the table and may hand blocks out
+ * and back in any order. */
+typedef struct {
+    void *k, *v;
+    const int32_t *block_table;
+    int32_t batch, block_size, max_blocks, n_blocks;
+} tfb_paged_kv_cache;
+
 /* Bytes of workspace the calls below need for batch B, sequence T (T = 1 for
  * decode) and, for tfb_model_forward, vocabulary `vocab` (0 = block calls
  * only).  Returns 0 for an invalid config. */
@@ -161,6 +180,20 @@ tfb_status tfb_block_prefill_varlen(const tfb_block_config *cfg, const tfb_block
 tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
                             int32_t t_max_table, const void *x, void *out, int32_t B, tfb_kv_cache *cache,
                             const int32_t *pos, int32_t h_max_pos, void *ws, size_t ws_bytes, void *stream);
+
+/* tfb_block_prefill and tfb_block_decode on a paged cache: the same
+ * computation, with cache rows found through the block table (positions and
+ * bounds as in the contiguous calls, with t_max = max_blocks * block_size).
+ * Prefill writes rows start_pos..start_pos+T-1 of every sequence; decode
+ * writes row pos[b] and attends over rows 0..pos[b] (or the window). */
+tfb_status tfb_block_prefill_paged(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                   int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T,
+                                   int32_t start_pos, const tfb_paged_kv_cache *cache, void *ws, size_t ws_bytes,
+                                   void *stream);
+tfb_status tfb_block_decode_paged(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                  int32_t t_max_table, const void *x, void *out, int32_t B,
+                                  const tfb_paged_kv_cache *cache, const int32_t *pos, int32_t h_max_pos, void *ws,
+                                  size_t ws_bytes, void *stream);
 
 /* Append n_new rows per sequence: k_new, v_new [B, n_new, Hkv, dh] (already
  * rotated) are written to cache rows start[b] .. start[b]+n_new-1.

@@ -113,6 +113,34 @@ def test_prefill_rejects_invalid_arguments():
     assert _prefill(neg) == -2                      # a window is a key count >= 0
 
 
+def test_paged_calls_reject_invalid_arguments():
+    lib = tfb.lib()
+    cfg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()
+    w = _weights()
+
+    def pc(bs=64, max_blocks=4, n_blocks=8, batch=2, table=FAKE, k=FAKE):
+        return tfb.PagedKVCache(ctypes.c_void_p(k), ctypes.c_void_p(FAKE + 4096), ctypes.c_void_p(table), batch, bs,
+                                max_blocks, n_blocks)
+
+    def pre(c, T=8, start=0, t_tab=1024):
+        return lib.tfb_block_prefill_paged(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(FAKE), t_tab,
+                                           ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 2, T, start, ctypes.byref(c),
+                                           ctypes.c_void_p(FAKE), 1 << 40, None)
+
+    def dec(c, h_max=5, t_tab=1024):
+        return lib.tfb_block_decode_paged(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(FAKE), t_tab,
+                                          ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 2, ctypes.byref(c),
+                                          ctypes.c_void_p(FAKE), h_max, ctypes.c_void_p(FAKE), 1 << 40, None)
+    assert pre(pc(bs=48)) == -2 and pre(pc(bs=4)) == -2       # block size: a power of two >= 8
+    assert pre(pc(batch=3)) == -2 and pre(pc(n_blocks=0)) == -2
+    assert pre(pc(table=0)) == -1 and pre(pc(k=0)) == -1
+    assert pre(pc(k=FAKE + 2)) == -4
+    assert pre(pc(), T=200, start=60) == -6                   # 4 blocks of 64 rows hold 256 positions
+    assert pre(pc(), T=8, t_tab=7) == -6
+    assert dec(pc(), h_max=256) == -6
+    assert dec(pc(bs=100)) == -2
+
+
 def test_varlen_prefill_rejects_invalid_arguments():
     lib = tfb.lib()
     cfg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024).c()

@@ -473,3 +473,64 @@ def test_varlen_prefill_matches_per_sequence(oracle, dtype, d, H, Hkv, W):
         # padding rows write nothing; earlier rows are untouched
         assert np.isnan(gk[b, :, int(starts[b] + lens[b]):]).all()
         assert np.array_equal(gk[b, :, :int(starts[b])], okc[b, :, :int(starts[b])])
+
+
+# ---- paged KV cache (tirogla "Transformer block", Implementation notes: a
+# cache allocated in fixed-size blocks per sequence)
+@pytest.mark.parametrize("dtype,bs,W", [("bf16", 16, 0), ("bf16", 64, 0), ("bf16", 256, 40), ("f32", 8, 0)])
+def test_paged_cache_matches_contiguous_bitwise(oracle, dtype, bs, W):
+    """Prefill in two chunks, then decode steps, through a block table that
+    scatters each sequence over a shuffled pool: outputs and cached rows must
+    equal the contiguous cache's bit for bit (only the addressing differs)."""
+    torch = _torch()
+    d, H, Hkv = (64, 4, 2) if dtype == "f32" else (256, 4, 2)
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype=dtype, number=130, window=W)
+    tc = tfb.Config.of(cfg)
+    w32, w = dev_weights(cfg)
+    B, T1, T2, steps = 2, 100, 50, 3
+    T = T1 + T2 + steps
+    x32, x = dev_x(cfg, B, T)
+    max_blocks = (T + bs - 1) // bs + 1
+    t_max = max_blocks * bs
+    n_blocks = B * max_blocks + 3
+    perm = np.random.default_rng(bs).permutation(n_blocks)[:B * max_blocks].reshape(B, max_blocks)
+    table = torch.from_numpy(perm.astype(np.int32)).cuda()
+    dh = d // H
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kp = torch.full((n_blocks, Hkv, bs, dh), float("nan"), dtype=tdt, device="cuda")
+    vp = kp.clone()
+    kc, vc = new_cache(cfg, B, t_max)
+    rope = tfb.rope_table_init(tc, t_max)
+    print("case: paged", dtype, bs, W, flush=True)
+    outs_c, outs_p = [], []
+    for s0, n in ((0, T1), (T1, T2)):
+        xi = x[:, s0:s0 + n].contiguous()
+        oc, op = torch.empty_like(xi), torch.empty_like(xi)
+        tfb.block_prefill(tc, w, rope, xi, oc, start_pos=s0, cache=(kc, vc))
+        tfb.block_prefill_paged(tc, w, rope, xi, op, (kp, vp, table, bs), start_pos=s0)
+        outs_c.append(oc)
+        outs_p.append(op)
+    for s in range(steps):
+        p = T1 + T2 + s
+        xi = x[:, p:p + 1].contiguous()
+        oc, op = torch.empty_like(xi), torch.empty_like(xi)
+        pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+        tfb.block_decode(tc, w, rope, xi, oc, (kc, vc), pos, p)
+        tfb.block_decode_paged(tc, w, rope, xi, op, (kp, vp, table, bs), pos, p)
+        outs_c.append(oc)
+        outs_p.append(op)
+    torch.cuda.synchronize()
+    got_c = np.concatenate([to_np(o) for o in outs_c], axis=1)
+    got_p = np.concatenate([to_np(o) for o in outs_p], axis=1)
+    assert np.array_equal(got_p, got_c)
+    ref = oracle.block_forward(cfg, w32, x32)
+    assert rel_err(got_p, ref) <= tol(cfg), rel_err(got_p, ref)
+    gk, gkp = widen_cache(kc), widen_cache(kp)
+    gv, gvp = widen_cache(vc), widen_cache(vp)
+    for b in range(B):
+        for p in range(T):
+            blk, r = perm[b, p // bs], p % bs
+            assert np.array_equal(gkp[blk, :, r], gk[b, :, p]) and np.array_equal(gvp[blk, :, r], gv[b, :, p])
+    # pool blocks no sequence owns are untouched
+    free = np.setdiff1d(np.arange(n_blocks), perm.ravel())
+    assert np.isnan(gkp[free]).all()

@@ -19,7 +19,8 @@ TFB_F32, TFB_BF16 = 0, 1
 STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTYPE", -4: "TFB_ERR_ALIGN",
           -5: "TFB_ERR_WORKSPACE", -6: "TFB_ERR_CACHE_OVERFLOW", -7: "TFB_ERR_HIP", -8: "TFB_ERR_UNSUPPORTED"}
 EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
-           "tfb_model_forward", "tfb_block_prefill_varlen", "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
+           "tfb_model_forward", "tfb_block_prefill_varlen", "tfb_block_prefill_paged", "tfb_block_decode_paged",
+           "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
            "tfb_profile_stages", "tfb_profile_stage_name")
 
 _VP = ctypes.c_void_p
@@ -37,6 +38,11 @@ class BlockWeights(ctypes.Structure):
 
 class KVCache(ctypes.Structure):
     _fields_ = [("k", _VP), ("v", _VP), ("batch", ctypes.c_int32), ("t_max", ctypes.c_int32)]
+
+
+class PagedKVCache(ctypes.Structure):
+    _fields_ = [("k", _VP), ("v", _VP), ("block_table", _VP), ("batch", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("n_blocks", ctypes.c_int32)]
 
 
 class Model(ctypes.Structure):
@@ -70,6 +76,12 @@ def lib():
         L.tfb_block_prefill.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.POINTER(KVCache), _VP, ctypes.c_size_t, _VP]
+        L.tfb_block_prefill_paged.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
+                                              ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.POINTER(PagedKVCache), _VP, ctypes.c_size_t, _VP]
+        L.tfb_block_decode_paged.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
+                                             ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.POINTER(PagedKVCache),
+                                             _VP, ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
         L.tfb_block_prefill_varlen.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
                                                ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP,
                                                ctypes.c_int32, ctypes.POINTER(KVCache), _VP, ctypes.c_size_t, _VP]
@@ -82,7 +94,8 @@ def lib():
                                         ctypes.c_int32, ctypes.POINTER(KVCache), _VP, ctypes.c_int32, _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_size_t, _VP]
         for f in ("tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
-                  "tfb_model_forward", "tfb_block_prefill_varlen"):
+                  "tfb_model_forward", "tfb_block_prefill_varlen", "tfb_block_prefill_paged",
+                  "tfb_block_decode_paged"):
             getattr(L, f).restype = ctypes.c_int
         L.tfb_status_string.argtypes = [ctypes.c_int]
         L.tfb_status_string.restype = ctypes.c_char_p
@@ -193,6 +206,37 @@ def block_prefill_varlen(cfg: Config, w: dict, rope, x, out, start, lens, max_en
     _check(lib().tfb_block_prefill_varlen(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
                                           rope.shape[0], _ptr(x), _ptr(out), B, T, _ptr(start), _ptr(lens), max_end,
                                           kv, _ptr(ws), ws_n, _stream()), "tfb_block_prefill_varlen")
+    return out
+
+
+def paged_cache_struct(k, v, table, block_size: int) -> PagedKVCache:
+    """k, v: pools [n_blocks, Hkv, block_size, dh]; table: int32 [B, max_blocks] device tensor."""
+    return PagedKVCache(_VP(k.data_ptr()), _VP(v.data_ptr()), _VP(table.data_ptr()), table.shape[0], block_size,
+                        table.shape[1], k.shape[0])
+
+
+def block_prefill_paged(cfg: Config, w: dict, rope, x, out, paged, start_pos: int = 0, ws=None):
+    """paged: (k_pool, v_pool, block_table, block_size)."""
+    B, T, _ = x.shape
+    if ws is None:
+        ws = workspace(cfg, B, T)
+    pc = paged_cache_struct(*paged)
+    ws_n = ws.numel() * ws.element_size()
+    _check(lib().tfb_block_prefill_paged(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
+                                         rope.shape[0], _ptr(x), _ptr(out), B, T, start_pos, ctypes.byref(pc),
+                                         _ptr(ws), ws_n, _stream()), "tfb_block_prefill_paged")
+    return out
+
+
+def block_decode_paged(cfg: Config, w: dict, rope, x, out, paged, pos, max_pos: int, ws=None):
+    B = x.shape[0]
+    if ws is None:
+        ws = workspace(cfg, B, 1)
+    pc = paged_cache_struct(*paged)
+    ws_n = ws.numel() * ws.element_size()
+    _check(lib().tfb_block_decode_paged(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
+                                        rope.shape[0], _ptr(x), _ptr(out), B, ctypes.byref(pc), _ptr(pos), max_pos,
+                                        _ptr(ws), ws_n, _stream()), "tfb_block_decode_paged")
     return out
 
 

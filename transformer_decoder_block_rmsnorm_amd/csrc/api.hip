@@ -2,6 +2,7 @@
 // the launch sequence of each call.  Page short names: [TIR] tirogla
 // "Transformer block", [PID] pidoku "The Transformer".
 #include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <algorithm>
@@ -159,7 +160,9 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
                      int max_pos, const void *x,
                      void *out, int B, int T, int start, const int32_t *pos, void *kc, void *vc, int t_max,
                      uint8_t *ws, const WsLayout &L, hipStream_t s, const int32_t *starts = nullptr,
-                     const int32_t *lens = nullptr) {
+                     const int32_t *lens = nullptr, const KvMap *paged = nullptr) {
+    // cache rows: contiguous [B, Hkv, t_max, dh], or a paged pool and block table
+    const KvMap kvm = paged ? *paged : KvMap{nullptr, t_max, 0, 0, 0};
     const int M = B * T, d = c.d, H = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, f = c.d_ff;
     const int qd = H * dh, kvd = Hkv * dh;
     void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
@@ -186,6 +189,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.ep.T = T; g.ep.H = H; g.ep.Hkv = Hkv; g.ep.dh = dh; g.ep.t_max = t_max; g.ep.start = start;
     g.ep.starts = starts;
     g.ep.lens = lens;
+    g.ep.kvm = kvm;
     g.scratch = L.skinny_bytes ? ws + L.skinny : nullptr;
     g.scratch_bytes = L.skinny_bytes;
     g.split_scratch = L.gsplit_bytes ? ws + L.gsplit : nullptr;
@@ -198,6 +202,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.dh = dh; a.t_max = t_max; a.start = start;
     a.starts = starts;
     a.lens = lens;
+    a.kvm = kvm;
     a.scale = 1.0f / sqrtf((float)dh);
     a.partials = ws + L.part;
     a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
@@ -383,6 +388,60 @@ tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights
                      L, (hipStream_t)stream);
 }
 
+// Paged cache: validated host fields, and the row map the kernels use.
+static tfb_status paged_map(const tfb_paged_kv_cache *pc, int B, KvMap &m) {
+    if (!pc->k || !pc->v || !pc->block_table) return TFB_ERR_NULL;
+    if (!aligned(pc->k) || !aligned(pc->v)) return TFB_ERR_ALIGN;
+    if (pc->batch != B || pc->max_blocks <= 0 || pc->n_blocks <= 0) return TFB_ERR_SHAPE;
+    const int bs = pc->block_size;
+    if (bs < 8 || bs > (1 << 16) || (bs & (bs - 1))) return TFB_ERR_SHAPE;
+    int shift = 0;
+    while ((1 << shift) < bs) ++shift;
+    if ((int64_t)pc->max_blocks * bs > INT32_MAX) return TFB_ERR_SHAPE;
+    m = KvMap{pc->block_table, pc->max_blocks * bs, shift, pc->max_blocks, pc->n_blocks};
+    return TFB_OK;
+}
+
+tfb_status tfb_block_prefill_paged(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                   int32_t t_max_table, const void *x, void *out, int32_t B, int32_t T,
+                                   int32_t start_pos, const tfb_paged_kv_cache *cache, void *ws, size_t ws_bytes,
+                                   void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if ((st = check_weights(w)) != TFB_OK) return st;
+    if (!rope_table || !x || !out || !cache) return TFB_ERR_NULL;
+    if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
+    if (B <= 0 || T <= 0 || start_pos < 0) return TFB_ERR_SHAPE;
+    KvMap m;
+    if ((st = paged_map(cache, B, m)) != TFB_OK) return st;
+    if ((int64_t)start_pos + T > m.t_max || (int64_t)start_pos + T > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    const WsLayout L = ws_layout(*cfg, B, T, 0);
+    if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
+    if (!aligned(ws)) return TFB_ERR_ALIGN;
+    return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, start_pos, nullptr, cache->k, cache->v,
+                     m.t_max, (uint8_t *)ws, L, (hipStream_t)stream, nullptr, nullptr, &m);
+}
+
+tfb_status tfb_block_decode_paged(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                  int32_t t_max_table, const void *x, void *out, int32_t B,
+                                  const tfb_paged_kv_cache *cache, const int32_t *pos, int32_t h_max_pos, void *ws,
+                                  size_t ws_bytes, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if ((st = check_weights(w)) != TFB_OK) return st;
+    if (!rope_table || !x || !out || !cache || !pos) return TFB_ERR_NULL;
+    if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
+    if (B <= 0 || h_max_pos < 0) return TFB_ERR_SHAPE;
+    KvMap m;
+    if ((st = paged_map(cache, B, m)) != TFB_OK) return st;
+    if (h_max_pos >= m.t_max || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    const WsLayout L = ws_layout(*cfg, B, 1, 0);
+    if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
+    if (!aligned(ws)) return TFB_ERR_ALIGN;
+    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v, m.t_max,
+                     (uint8_t *)ws, L, (hipStream_t)stream, nullptr, nullptr, &m);
+}
+
 tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const void *k_new, const void *v_new,
                          const int32_t *start, int32_t n_new, int32_t h_max_start, void *stream) {
     tfb_status st = check_cfg(cfg);
@@ -394,8 +453,9 @@ tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const
     if (n_new <= 0 || h_max_start < 0) return TFB_ERR_SHAPE;
     if ((int64_t)h_max_start + n_new > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
     hipStream_t s = (hipStream_t)stream;
+    const KvMap kvm{nullptr, cache->t_max, 0, 0, 0};
     TRY_HIP(STAGE(ST_KV_APPEND, kv_append_launch(cfg->dtype, cache->k, cache->v, k_new, v_new, start, cache->batch,
-                                                 n_new, cfg->n_kv_heads, cfg->head_dim, cache->t_max, s)));
+                                                 n_new, cfg->n_kv_heads, cfg->head_dim, kvm, s)));
     return TFB_OK;
 }
 

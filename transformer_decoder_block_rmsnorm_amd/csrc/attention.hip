@@ -41,8 +41,8 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
     if (p >= a.t_max) p = a.t_max - 1;  // never read past the cache
     const int n_keys = p + 1;
     const int kvh = h / (a.H / a.Hkv);
-    const T *K = (const T *)a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * a.dh;
-    const T *V = (const T *)a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * a.dh;
+    const T *K = (const T *)a.kc;
+    const T *V = (const T *)a.vc;
 
     // sliding window: keys from p - window + 1 ([PID] Sliding-window attention)
     const int k_first = a.window > 0 ? max(0, p - a.window + 1) : 0;
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
         const int j = j0 + lane;
         float s = -INFINITY;
         if (j < n_keys) {
-            const T *kj = K + (int64_t)j * a.dh;
+            const T *kj = K + kv_row(a.kvm, b, a.Hkv, kvh, j) * a.dh;
             float dot = 0.0f;
             for (int e = 0; e < a.dh; ++e) dot += qs[wave][e] * Elem<T>::load(kj, e);
             s = dot * a.scale;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
         const int cnt = min(64, n_keys - j0);
         for (int jj = 0; jj < cnt; ++jj) {
             const float pw = __shfl(pj, jj, 64);
-            const T *vj = V + (int64_t)(j0 + jj) * a.dh;
+            const T *vj = V + kv_row(a.kvm, b, a.Hkv, kvh, j0 + jj) * a.dh;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = lane + 64 * i;
@@ -110,6 +110,7 @@ struct FlashArgs {
     int B, T, H, Hkv, t_max, start;
     const int32_t *starts, *lens;  // varlen: [B] first position and valid rows (NULL: start, T)
     int window;  // keys per query (0: full causal)
+    KvMap kvm;   // cache row addressing
     int HG, PB, n_qblocks, n_hsub;
     float scale_log2e;
 };
@@ -119,7 +120,7 @@ struct FlashArgs {
 // the S^T accumulator: {4h..4h+3, 8+4h..8+4h+3}.
 __device__ __forceinline__ int v_slot(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <int DH>
+template <int DH, bool PAGED>
 __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     constexpr int BKV = 64;          // keys per tile
     constexpr int NS = DH / 16;      // 16-wide dh slices of q.k
@@ -173,25 +174,27 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
         }
     }
     const int qpos = start + t0 + lr;
-    const bf16_t *Kg = a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
-    const bf16_t *Vg = a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
-
+    // cache row j of this sequence and KV head (a contiguous slab unless paged)
+    const int64_t slab = ((int64_t)b * a.Hkv + kvh) * a.t_max;
+    auto row = [&](int j) -> int64_t { return PAGED ? kv_row(a.kvm, b, a.Hkv, kvh, j) : slab + j; };
     u32x4 rk[K_PER], rv[8];
     auto load_tile = [&](int it) {
         const int j0 = it * BKV;
 #pragma unroll
         for (int i = 0; i < K_PER; ++i) {
             const int c = tid + 256 * i, key = c / KCH, ch = c % KCH, j = j0 + key;
-            rk[i] = (j < kv_len && j >= key_floor) ? *(const u32x4 *)(Kg + (int64_t)j * DH + ch * 8)
-                                                   : u32x4{0, 0, 0, 0};
+            rk[i] = (j < kv_len && j >= key_floor)
+                        ? *(const u32x4 *)(a.kc + row(j) * DH + ch * 8)
+                        : u32x4{0, 0, 0, 0};
         }
         if (tid < NVB) {
             const int kb = tid / (DH / 8), eb = tid % (DH / 8);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const int j = j0 + kb * 8 + r;
-                rv[r] = (j < kv_len && j >= key_floor) ? *(const u32x4 *)(Vg + (int64_t)j * DH + eb * 8)
-                                                       : u32x4{0, 0, 0, 0};
+                rv[r] = (j < kv_len && j >= key_floor)
+                            ? *(const u32x4 *)(a.vc + row(j) * DH + eb * 8)
+                            : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -337,6 +340,7 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     a.starts = c.starts;
     a.lens = c.lens;
     a.window = c.window;
+    a.kvm = c.kvm;
     const int G = c.H / c.Hkv;
     a.HG = G >= 4 ? 4 : (G >= 2 ? 2 : 1);
     if (G % a.HG) a.HG = 1;
@@ -345,10 +349,15 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     a.n_qblocks = (c.T + a.PB - 1) / a.PB;
     a.scale_log2e = c.scale * 1.4426950408889634f;
     const int blocks = a.n_qblocks * c.B * c.Hkv * a.n_hsub;
-    if (c.dh == 128)
-        hipLaunchKernelGGL(flash_prefill_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+    const bool paged = a.kvm.table != nullptr;
+    if (c.dh == 128 && paged)
+        hipLaunchKernelGGL((flash_prefill_kernel<128, true>), dim3(blocks), dim3(256), 0, s, a);
+    else if (c.dh == 128)
+        hipLaunchKernelGGL((flash_prefill_kernel<128, false>), dim3(blocks), dim3(256), 0, s, a);
+    else if (paged)
+        hipLaunchKernelGGL((flash_prefill_kernel<64, true>), dim3(blocks), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL(flash_prefill_kernel<64>, dim3(blocks), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((flash_prefill_kernel<64, false>), dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -371,6 +380,7 @@ struct DecArgs {
     float *part;      // [B][H][max_chunks][DH + 4]
     int B, H, Hkv, t_max, max_chunks, chunk_keys;
     int window;       // keys per query (0: full causal)
+    KvMap kvm;        // cache row addressing
     float scale_log2e;
 };
 
@@ -410,8 +420,6 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
         if (ln < G) v = *(const u32x4 *)(a.q + ((int64_t)b * a.H + h0 + ln) * DH + (4 * s + g4) * 8);
         qf[s] = as_bf16x8(v);
     }
-    const bf16_t *Kg = a.kc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
-    const bf16_t *Vg = a.vc + ((int64_t)b * a.Hkv + kvh) * a.t_max * DH;
     const bool v_lane = ln < NCH;  // dh = 64 uses half the output columns
 
     float m_run = -INFINITY, l_run = 0.0f;  // for head ln
@@ -426,7 +434,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
             const int j = base + 16 * t + ln;
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-                kr[t][s] = (j < k_end) ? ld_stream(Kg + (int64_t)j * DH + (4 * s + g4) * 8) : u32x4{0, 0, 0, 0};
+                kr[t][s] = (j < k_end) ? ld_stream(a.kc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + (4 * s + g4) * 8)
+                                       : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -434,7 +443,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
             for (int r = 0; r < 8; ++r) {
                 // slots 0-3: keys 32u + 4g + v; slots 4-7: keys 32u + 16 + 4g + v
                 const int j = base + 32 * u + 16 * (r >> 2) + 4 * g4 + (r & 3);
-                vr[u][r] = (v_lane && j < k_end) ? ld_stream(Vg + (int64_t)j * DH + ln * 8) : u32x4{0, 0, 0, 0};
+                vr[u][r] = (v_lane && j < k_end) ? ld_stream(a.vc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + ln * 8)
+                                                 : u32x4{0, 0, 0, 0};
             }
         f32x4 sacc[4];
 #pragma unroll
@@ -600,6 +610,7 @@ static hipError_t split_decode_launch(const AttnCall &c, hipStream_t s) {
     }
     a.chunk_keys = chunk_keys;
     a.max_chunks = chunks;
+    a.kvm = c.kvm;
     a.scale_log2e = c.scale * 1.4426950408889634f;
     if (decode_part_bytes(c.B, c.H, c.dh, chunks) > c.partial_bytes) return hipErrorInvalidValue;
     return c.dh == 128 ? decode_launch_dh<128>(c, a, s) : decode_launch_dh<64>(c, a, s);

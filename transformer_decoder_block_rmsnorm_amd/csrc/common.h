@@ -104,4 +104,25 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Where row j (absolute position) of sequence b, KV head g lives in a KV
+// cache, as a row index (the element offset is row * dh).
+//  - contiguous cache [B, Hkv, t_max, dh] (table == NULL);
+//  - paged cache: a pool [n_blocks, Hkv, 2^bs_shift, dh] of fixed-size
+//    blocks, and a block table [B, max_blocks] giving the pool block of each
+//    logical block j >> bs_shift of a sequence (tirogla "Transformer block",
+//    Implementation notes: a KV cache allocated in fixed blocks per
+//    sequence).  A table entry outside [0, n_blocks) is clamped into it, so a
+//    bad table can give wrong values but never an access outside the pool.
+struct KvMap {
+    const int32_t *table;
+    int t_max;        // rows per sequence (paged: max_blocks << bs_shift)
+    int bs_shift, max_blocks, n_blocks;
+};
+__device__ __forceinline__ int64_t kv_row(const KvMap &m, int b, int Hkv, int g, int j) {
+    if (!m.table) return ((int64_t)b * Hkv + g) * m.t_max + j;
+    int blk = m.table[(int64_t)b * m.max_blocks + (j >> m.bs_shift)];
+    blk = min(max(blk, 0), m.n_blocks - 1);
+    return (((int64_t)blk * Hkv + g) << m.bs_shift) + (j & ((1 << m.bs_shift) - 1));
+}
+
 }  // namespace tfb

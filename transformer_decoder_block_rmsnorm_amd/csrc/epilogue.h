@@ -26,6 +26,7 @@ struct EpiParams {
     const int32_t *starts;   // varlen prefill: [B] position of row 0 (NULL: start)
     const int32_t *lens;     // varlen prefill: [B] valid rows; later rows are padding (NULL: all T)
     int T, H, Hkv, dh, t_max, start;
+    KvMap kvm;               // cache row addressing (contiguous or paged)
     int rope_rows;           // rows of the RoPE table (device positions are clamped to it)
 };
 
@@ -90,7 +91,7 @@ __device__ __forceinline__ void epi_store_pair(const EpiParams &p, int m, int c,
             T *dst = (T *)p.kc;
             if (cc >= kvd) { cc -= kvd; dst = (T *)p.vc; }
             int g = cc / p.dh, e = cc - g * p.dh;
-            int64_t ic = (((int64_t)b * p.Hkv + g) * p.t_max + ps) * p.dh + e;
+            int64_t ic = kv_row(p.kvm, b, p.Hkv, g, ps) * p.dh + e;
             Elem<T>::store(dst, ic, v0);
             Elem<T>::store(dst, ic + 1, v1);
         }

@@ -55,13 +55,14 @@ struct AttnCall {
     int max_keys;         // host bound on keys per query (for work sizing)
     int max_splits;       // chunks per (b, h) the partial buffer holds
     int window;           // sliding window: keys per query (0: full causal)
+    KvMap kvm;            // cache row addressing (contiguous or paged)
 };
 hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
 size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_keys);
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
-                            int B, int n_new, int Hkv, int dh, int t_max, hipStream_t s);
+                            int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s);
 hipError_t embed_launch(int dtype, const int32_t *ids, const void *table, void *x, int64_t rows, int d, int vocab,
                         hipStream_t s);
 // Copy row (T-1) of each sequence of x [B, T, d] into y [B, d].

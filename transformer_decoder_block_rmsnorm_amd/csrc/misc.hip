@@ -91,7 +91,7 @@ hipError_t rope_table_launch(int t_max, int dh, double base, float *table, hipSt
 // start[b] + t.  One thread per 4 elements; rows outside [0, t_max) are skipped.
 template <typename T>
 __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const int32_t *start, int B, int n_new,
-                                 int Hkv, int dh, int t_max) {
+                                 int Hkv, int dh, KvMap kvm) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int per_row = dh / 4;
     const int64_t total = (int64_t)B * n_new * Hkv * per_row;
@@ -103,9 +103,9 @@ __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const i
     const int t = (int)(r % n_new);
     const int b = (int)(r / n_new);
     const int p = start[b] + t;
-    if (p < 0 || p >= t_max) return;
+    if (p < 0 || p >= kvm.t_max) return;
     const int64_t src = (((int64_t)b * n_new + t) * Hkv + g) * dh + e4 * 4;
-    const int64_t dst = (((int64_t)b * Hkv + g) * t_max + p) * dh + e4 * 4;
+    const int64_t dst = kv_row(kvm, b, Hkv, g, p) * dh + e4 * 4;
     if constexpr (sizeof(T) == 2) {
         *(u32x2 *)(kc + dst) = *(const u32x2 *)(kn + src);
         *(u32x2 *)(vc + dst) = *(const u32x2 *)(vn + src);
@@ -116,15 +116,15 @@ __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const i
 }
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
-                            int B, int n_new, int Hkv, int dh, int t_max, hipStream_t s) {
+                            int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s) {
     const int64_t total = (int64_t)B * n_new * Hkv * (dh / 4);
     dim3 grid((unsigned)((total + 255) / 256));
     if (dtype == TFB_BF16)
         hipLaunchKernelGGL(kv_append_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)kc, (bf16_t *)vc,
-                           (const bf16_t *)k_new, (const bf16_t *)v_new, start, B, n_new, Hkv, dh, t_max);
+                           (const bf16_t *)k_new, (const bf16_t *)v_new, start, B, n_new, Hkv, dh, kvm);
     else
         hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, (float *)kc, (float *)vc,
-                           (const float *)k_new, (const float *)v_new, start, B, n_new, Hkv, dh, t_max);
+                           (const float *)k_new, (const float *)v_new, start, B, n_new, Hkv, dh, kvm);
     return hipGetLastError();
 }
 
