@@ -403,7 +403,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
-    const int ch = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    // grid (Hkv, B, chunks): consecutive workgroups, which the hardware deals
+    // to the 8 XCDs in turn, are different (sequence, KV head) pairs of one
+    // chunk index, so every XCD gets the same mix of long and empty chunks
+    const int kvh = blockIdx.x, b = blockIdx.y, ch = blockIdx.z;
     const int n_keys = min(a.pos[b] + 1, a.t_max);
     // keys [k_first, n_keys): all of them, or the last `window` ones
     const int k_first = a.window > 0 ? max(0, n_keys - a.window) : 0;
@@ -574,7 +577,7 @@ size_t decode_part_bytes(int B, int H, int dh, int max_chunks) {
 template <int DH>
 static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s) {
     const int G = c.H / c.Hkv;
-    dim3 grid(a.max_chunks, c.Hkv, c.B);
+    dim3 grid(c.Hkv, c.B, a.max_chunks);
     switch (G) {
         case 1: hipLaunchKernelGGL((decode_attn_kernel<DH, 1>), grid, dim3(256), 0, s, a); break;
         case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2>), grid, dim3(256), 0, s, a); break;

@@ -80,19 +80,6 @@ __device__ __forceinline__ void wg_work(const GemmArgs &g, int bid, int &tile, i
     }
 }
 
-// ds_read_b64_tr_b16: within each 16-lane group, lane j receives element
-// (j % 4) of the 8-byte rows addressed by lanes j/4 + 4i, i = 0..3.  So when
-// lane s of a group points at B[kb + s/4][n0 + 4 (s % 4)], lane j receives
-// B[kb + 0..3][n0 + j]: four consecutive k values of column n0 + j, the
-// layout of an MFMA B fragment.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t *p) {
-    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(__attribute__((address_space(3))) void *)p);
-    return __builtin_bit_cast(u32x2, v);
-}
-
 // ---------------------------------------------------------------------------
 // bf16 GEMM: operands go from global memory straight into LDS
 // (global_load_lds_dwordx4: lane i of an instruction writes the i-th 16-byte
@@ -107,23 +94,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t *p) {
 // makes every wave's slots visible.  The MFMAs of one 16-wide k half run
 // while the fragments of the next half are read from LDS.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
-// Issued as inline assembly so that the compiler neither tracks the LDS write
-// nor inserts its own vmcnt waits; callers order it with wait_vmcnt and a
-// barrier.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte_addr), "v"(gptr)
-                 : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
-}
-
 template <int BM, int BN, int WM, int WN, int SRC, int EPI>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, EpiParams ep) {
     constexpr int NW = WM * WN, NT = NW * 64;
