@@ -210,6 +210,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.max_splits = kMaxSplits;
     a.window = c.window;
     TRY_HIP(STAGE(ST_ATTN, pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s)));
+    if (pos) TRY_HIP(STAGE(ST_ATTN_COMBINE, attention_decode_merge_launch(a, s)));
 
     GemmCall o{};
     o.dtype = c.dtype;

@@ -586,14 +586,11 @@ static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s)
         case 16: hipLaunchKernelGGL((decode_attn_kernel<DH, 16>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<DH>, dim3((c.B * c.H + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-static hipError_t split_decode_launch(const AttnCall &c, hipStream_t s) {
-    DecArgs a;
+// Arguments of the split decode kernels for one call.
+static bool split_decode_args(const AttnCall &c, DecArgs &a) {
     a.q = (const bf16_t *)c.q;
     a.kc = (const bf16_t *)c.kc;
     a.vc = (const bf16_t *)c.vc;
@@ -615,8 +612,12 @@ static hipError_t split_decode_launch(const AttnCall &c, hipStream_t s) {
     a.max_chunks = chunks;
     a.kvm = c.kvm;
     a.scale_log2e = c.scale * 1.4426950408889634f;
-    if (decode_part_bytes(c.B, c.H, c.dh, chunks) > c.partial_bytes) return hipErrorInvalidValue;
-    return c.dh == 128 ? decode_launch_dh<128>(c, a, s) : decode_launch_dh<64>(c, a, s);
+    return decode_part_bytes(c.B, c.H, c.dh, chunks) <= c.partial_bytes;
+}
+
+static bool split_decode_applies(const AttnCall &a) {
+    const int G = a.H / a.Hkv;
+    return a.dtype == TFB_BF16 && (a.dh == 128 || a.dh == 64) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
 static hipError_t rowwise_launch(const AttnCall &a, hipStream_t s) {
@@ -634,10 +635,22 @@ hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s) {
     return rowwise_launch(a, s);
 }
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s) {
-    const int G = a.H / a.Hkv;
-    if (a.dtype == TFB_BF16 && (a.dh == 128 || a.dh == 64) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16))
-        return split_decode_launch(a, s);
-    return rowwise_launch(a, s);
+    if (!split_decode_applies(a)) return rowwise_launch(a, s);
+    DecArgs d;
+    if (!split_decode_args(a, d)) return hipErrorInvalidValue;
+    return a.dh == 128 ? decode_launch_dh<128>(a, d, s) : decode_launch_dh<64>(a, d, s);
+}
+
+hipError_t attention_decode_merge_launch(const AttnCall &a, hipStream_t s) {
+    if (!split_decode_applies(a)) return hipSuccess;  // the row-wise kernel needs no merge
+    DecArgs d;
+    if (!split_decode_args(a, d)) return hipErrorInvalidValue;
+    const dim3 grid((a.B * a.H + 3) / 4);
+    if (a.dh == 128)
+        hipLaunchKernelGGL(decode_combine_kernel<128>, grid, dim3(256), 0, s, d);
+    else
+        hipLaunchKernelGGL(decode_combine_kernel<64>, grid, dim3(256), 0, s, d);
+    return hipGetLastError();
 }
 size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits) {
     return decode_part_bytes(B, H, dh, max_splits);

@@ -59,6 +59,8 @@ struct AttnCall {
 };
 hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
+// Merge of the split-KV chunk partials into o (after attention_decode_launch).
+hipError_t attention_decode_merge_launch(const AttnCall &a, hipStream_t s);
 size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_keys);
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
