@@ -33,7 +33,7 @@ PEAK_HBM_GBPS = 8000.0      # HBM3E
 # with the sources of the kernel it was taken on (stale counters give null)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gateup_gemm_7b_prefill_pmc.md")
 GEMM_SOURCES = [os.path.join(ROOT, "transformer_decoder_block_rmsnorm_amd", "csrc", n)
-                for n in ("gemm.hip", "epilogue.h", "common.h", "kernels.h")]
+                for n in ("gemm.hip", "epilogue.h", "common.h")]
 
 
 def gemm_source_digest() -> str:
