@@ -28,6 +28,7 @@ struct EpiParams {
     int T, H, Hkv, dh, t_max, start;
     KvMap kvm;               // cache row addressing (contiguous or paged)
     int rope_rows;           // rows of the RoPE table (device positions are clamped to it)
+    int vec8;                // set by the GEMM launcher: 8-column groups may use 16-byte accesses
 };
 
 // Position of output row m (token t of sequence b).
@@ -94,6 +95,103 @@ __device__ __forceinline__ void epi_store_pair(const EpiParams &p, int m, int c,
             int64_t ic = kv_row(p.kvm, b, p.Hkv, g, ps) * p.dh + e;
             Elem<T>::store(dst, ic, v0);
             Elem<T>::store(dst, ic + 1, v1);
+        }
+    }
+}
+
+// Eight consecutive bf16 values -> one 16-byte store.
+__device__ __forceinline__ void store_bf16x8(bf16_t *dst, const float (&v)[8]) {
+    u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    *(u32x4 *)dst = w;
+}
+__device__ __forceinline__ void load_bf16x8(const bf16_t *src, float (&v)[8]) {
+    const u32x4 w = *(const u32x4 *)src;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf16_lo(w[k]);
+        v[2 * k + 1] = bf16_hi(w[k]);
+    }
+}
+
+// Store output columns c .. c+7 (c a multiple of 8) of row m with 16-byte
+// accesses.  The launcher sets p.vec8 when every such group starts 16-byte
+// aligned in every tensor it touches (leading dimensions, head width); a
+// group that is not whole inside the output, or a launch without vec8, goes
+// through the pairwise path, which checks each column.  KIND == EPI_SWIGLU
+// takes the finished SiLU(gate) * up values.
+template <int KIND>
+__device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, const float (&v)[8]) {
+    if (!p.vec8 || c + 8 > p.N) {
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+            if constexpr (KIND == EPI_SWIGLU) {
+                if (m < p.M && c + k < p.N) Elem<bf16_t>::store((bf16_t *)p.out, (int64_t)m * p.ldo + c + k, v[k]);
+                if (m < p.M && c + k + 1 < p.N)
+                    Elem<bf16_t>::store((bf16_t *)p.out, (int64_t)m * p.ldo + c + k + 1, v[k + 1]);
+            } else {
+                epi_store_pair<KIND, bf16_t>(p, m, c + k, v[k], v[k + 1]);
+            }
+        }
+        return;
+    }
+    if (m >= p.M) return;
+    if constexpr (KIND == EPI_SWIGLU) {
+        store_bf16x8((bf16_t *)p.out + (int64_t)m * p.ldo + c, v);
+    } else if constexpr (KIND == EPI_RESID) {
+        const int64_t ir = (int64_t)m * p.ldr + c, io = (int64_t)m * p.ldo + c;
+        float r[8];
+        if (p.res_f32) {
+            const f32x4 a = *(const f32x4 *)((const float *)p.res + ir), b = *(const f32x4 *)((const float *)p.res + ir + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { r[k] = a[k]; r[k + 4] = b[k]; }
+        } else {
+            load_bf16x8((const bf16_t *)p.res + ir, r);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] += v[k];
+        if (p.out_f32) {
+            float *o = (float *)p.out + io;
+            *(f32x4 *)o = f32x4{r[0], r[1], r[2], r[3]};
+            *(f32x4 *)(o + 4) = f32x4{r[4], r[5], r[6], r[7]};
+        } else {
+            store_bf16x8((bf16_t *)p.out + io, r);
+        }
+    } else if constexpr (KIND == EPI_F32) {
+        float *o = (float *)p.out + (int64_t)m * p.ldo + c;
+        *(f32x4 *)o = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4 *)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else if constexpr (KIND == EPI_QKV) {
+        int b, t, ps;
+        qkv_row(p, m, b, t, ps);
+        const int qd = p.H * p.dh, kvd = p.Hkv * p.dh;
+        float w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = v[k];
+        if (c < qd + kvd) {
+            // RoPE on the four pairs (e, e+1) .. (e+6, e+7) of one head
+            const int e = c % p.dh;
+            const int pr = min(max(ps, 0), p.rope_rows - 1);
+            const f32x4 *cs = (const f32x4 *)(p.rope + ((int64_t)pr * (p.dh >> 1) + (e >> 1)) * 2);
+            const f32x4 t0 = cs[0], t1 = cs[1];
+            const float co[4] = {t0[0], t0[2], t1[0], t1[2]}, si[4] = {t0[1], t0[3], t1[1], t1[3]};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float a = v[2 * k], bb = v[2 * k + 1];
+                w[2 * k] = a * co[k] - bb * si[k];
+                w[2 * k + 1] = a * si[k] + bb * co[k];
+            }
+        }
+        if (c < qd) {
+            const int h = c / p.dh, e = c - h * p.dh;
+            store_bf16x8((bf16_t *)p.q + (((int64_t)b * p.H + h) * p.T + t) * p.dh + e, w);
+        } else {
+            if (ps < 0 || ps >= p.t_max) return;  // never write outside the cache
+            if (p.lens && t >= p.lens[b]) return;  // padding rows leave the cache alone
+            int cc = c - qd;
+            bf16_t *dst = (bf16_t *)p.kc;
+            if (cc >= kvd) { cc -= kvd; dst = (bf16_t *)p.vc; }
+            const int g = cc / p.dh, e = cc - g * p.dh;
+            store_bf16x8(dst + kv_row(p.kvm, b, p.Hkv, g, ps) * p.dh + e, w);
         }
     }
 }

@@ -106,7 +106,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     static_assert(A_INS * NW * 1024 == BM * BKD * 2 && B_INS * NW * 1024 == BKD * BN * 2, "tiles split in 1 KB blocks");
     static_assert(BN / 16 >= 8, "granule swizzle needs 8 granules per row");
     static_assert(SRC != SRC_DUAL || TN % 2 == 0, "dual source needs gate/up tile pairs");
-    static_assert(NW * 32 * WTN * 4 <= NST * STAGE * 2, "epilogue staging must fit");
+    static_assert(NW * 32 * (WTN + 4) * 4 <= NST * STAGE * 2, "epilogue staging must fit");
+    static_assert((32 * (EPI == EPI_SWIGLU ? WTN / 2 : WTN) / 8) % 64 == 0, "whole 8-column segments per lane");
 
     __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;  // LDS byte address of the ring
@@ -282,18 +283,45 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     wait_vmcnt<0>();
     __syncthreads();  // every wave is done with the ring before it is reused for staging
 
-    float *stage = (float *)lds + wave * (32 * WTN);
+    // Epilogue, one 32-row slab of the wave tile at a time: the accumulators
+    // go through LDS (row stride SW floats) so that each lane then holds 8
+    // consecutive columns of one row and the stores are 16 bytes wide.
+    // SwiGLU is applied before staging: the gate (j even) and up (j + 1)
+    // values of one output sit in the same register of the same lane.
+    constexpr int UW = (EPI == EPI_SWIGLU) ? WTN / 2 : WTN;  // output columns of the wave
+    constexpr int SW = WTN + 4;                               // staging row stride (floats)
+    float *stage = (float *)lds + wave * (32 * SW);
+    // 16-byte chunk pair of lane segment sg: segments 4..7 of a 64-wide row
+    // read their two chunks in the other order, so the eight lanes of one
+    // row fall in distinct banks.
+    auto read8 = [&](const float *src, int sg, float (&v)[8]) {
+        const int f = (sg >> 2) & 1;
+        const f32x4 a = *(const f32x4 *)(src + 4 * f), b = *(const f32x4 *)(src + 4 * (1 - f));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[4 * f + k] = a[k];
+            v[4 * (1 - f) + k] = b[k];
+        }
+    };
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+        const int row0 = m0 + wm * WTM + i * 32;
+        if (split >= 0 || EPI != EPI_SWIGLU) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * WTN + j * 32 + lr] = acc[i][j][v];
+                for (int v = 0; v < 16; ++v) stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * SW + j * 32 + lr] = acc[i][j][v];
+        } else {
+#pragma unroll
+            for (int jp = 0; jp < TN / 2; ++jp)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * SW + jp * 32 + lr] =
+                        silu_f(acc[i][2 * jp][v]) * acc[i][2 * jp + 1][v];
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int row0 = m0 + wm * WTM + i * 32;
         if (split >= 0) {
             // split tail: raw fp32 partial of this k range, tile-local layout
             float *dst = g.part + ((int64_t)(tile - g.full_tiles) * g.splits + split) * (BM * BN) +
@@ -301,24 +329,17 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
 #pragma unroll
             for (int r = 0; r < 32 * WTN / 4 / 64; ++r) {
                 const int p = r * 64 + lane, rl = p / (WTN / 4), c4 = p % (WTN / 4);
-                *(f32x4 *)(dst + rl * BN + 4 * c4) = *(const f32x4 *)(stage + rl * WTN + 4 * c4);
-            }
-        } else if constexpr (EPI == EPI_SWIGLU) {
-            constexpr int UW = WTN / 2;
-#pragma unroll
-            for (int r = 0; r < 32 * UW / 64; ++r) {
-                const int p = r * 64 + lane, rl = p / UW, u = p % UW;
-                const int cg = 64 * (u >> 5) + (u & 31);
-                epi_store_swiglu<bf16_t>(ep, row0 + rl, tn * (BN / 2) + wn * UW + u, stage[rl * WTN + cg],
-                                         stage[rl * WTN + cg + 32]);
+                *(f32x4 *)(dst + rl * BN + 4 * c4) = *(const f32x4 *)(stage + rl * SW + 4 * c4);
             }
         } else {
-            constexpr int PW = WTN / 2;
+            constexpr int SEGS = UW / 8;  // 8-column segments per row
+            const int c0 = (EPI == EPI_SWIGLU) ? tn * (BN / 2) + wn * UW : n0 + wn * WTN;
 #pragma unroll
-            for (int r = 0; r < 32 * PW / 64; ++r) {
-                const int p = r * 64 + lane, rl = p / PW, cp = p % PW;
-                const float2 v = *(const float2 *)(stage + rl * WTN + 2 * cp);
-                epi_store_pair<EPI, bf16_t>(ep, row0 + rl, n0 + wn * WTN + 2 * cp, v.x, v.y);
+            for (int r = 0; r < 32 * SEGS / 64; ++r) {
+                const int p = r * 64 + lane, rl = p / SEGS, sg = p % SEGS;
+                float v8[8];
+                read8(stage + rl * SW + 8 * sg, sg, v8);
+                epi_store8<EPI>(ep, row0 + rl, c0 + 8 * sg, v8);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -496,7 +517,16 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
     g.M = c.M;
     g.K = c.K;
     for (int i = 0; i < 3; ++i) { g.w[i] = c.w[i]; g.w_cols[i] = c.w_cols[i]; }
-    const EpiParams &ep = c.ep;
+    EpiParams ep = c.ep;
+    // 16-byte epilogue accesses need every 8-column group to start 16-byte
+    // aligned: leading dimensions in elements, and whole groups inside one head
+    switch (c.epi) {
+        case EPI_SWIGLU: ep.vec8 = ep.ldo % 8 == 0; break;
+        case EPI_RESID: ep.vec8 = ep.ldr % (ep.res_f32 ? 4 : 8) == 0 && ep.ldo % (ep.out_f32 ? 4 : 8) == 0; break;
+        case EPI_F32: ep.vec8 = ep.ldo % 4 == 0; break;
+        case EPI_QKV: ep.vec8 = ep.dh % 8 == 0; break;
+        default: ep.vec8 = 0;
+    }
     if (c.dtype == TFB_F32) {
         g.N = c.ep.N;
         dim3 grid((c.ep.N + 63) / 64, (c.M + 63) / 64);
