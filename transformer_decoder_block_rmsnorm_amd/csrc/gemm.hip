@@ -497,17 +497,46 @@ static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, void *part, size_t
     return hipGetLastError();
 }
 
-// Tile shape of a large-M bf16 GEMM: 256x256 on 8 waves when at least half
-// the compute units get a tile (a partial last round is split along k),
-// 128x128 on 4 waves otherwise.
-static bool big_tiles(int M, int N_virtual) {
-    return ((M + 255) / 256) * ((N_virtual + 255) / 256) * 2 >= device_cus();
+// Tile shape of a large-M bf16 GEMM (8 waves unless noted):
+//  T_256:     256x256, a partial last round of tiles split along k;
+//  T_256x128: 256x128, which needs no split partials and no fix-up pass but
+//             moves 1.5x the operand bytes per flop;
+//  T_128:     128x128 on 4 waves, when fewer than half the compute units
+//             would get a 256x256 tile.
+// Between the first two, a cost model in units of one 256x256 k step, with
+// constants measured on MI355X (7B-shaped block, K = 4096 and 11008): a
+// 256x128 k step costs 0.63 units plus 7 units of epilogue per round, and the
+// split tail costs 0.77 units per MB of fp32 partials written and re-read.
+enum TilePlan { T_256 = 0, T_256x128 = 1, T_128 = 2 };
+static TilePlan plan_tiles(int M, int N_virtual, int K) {
+    const int cus = device_cus();
+    const int tm = (M + 255) / 256, kt = K / 32;
+    const int t256 = tm * ((N_virtual + 255) / 256), t128 = tm * ((N_virtual + 127) / 128);
+    if (t256 * 2 < cus) return T_128;
+    const SplitPlan sp = plan_split(t256, kt, cus, 256 * 256);
+    double c256 = (double)(t256 / cus) * kt;
+    if (sp.splits > 1) c256 += (double)kt / sp.splits + 0.77 * sp.part_bytes / (1 << 20);
+    else if (t256 % cus) c256 += kt;
+    const double c128 = (double)((t128 + cus - 1) / cus) * (0.63 * kt + 7.0);
+    return c128 < c256 ? T_256x128 : T_256;
 }
 
 size_t gemm_split_bytes(int M, int N_virtual, int K) {
-    if (M <= kSkinnyMaxM || !big_tiles(M, N_virtual)) return 0;
+    if (M <= kSkinnyMaxM || plan_tiles(M, N_virtual, K) != T_256) return 0;
     const int tiles = ((M + 255) / 256) * ((N_virtual + 255) / 256);
     return plan_split(tiles, K / 32, device_cus(), 256 * 256).part_bytes;
+}
+
+template <int SRC, int EPI>
+static hipError_t launch_planned(const GemmArgs &g, const EpiParams &ep, void *part, size_t pb, hipStream_t s) {
+    switch (plan_tiles(g.M, g.N, g.K)) {
+        case T_256: return launch_dma<256, 256, 2, 4, SRC, EPI>(g, ep, part, pb, s);
+        case T_256x128:
+            // the gate-up pairing needs two 32-column blocks per wave
+            if constexpr (SRC == SRC_DUAL) return launch_dma<256, 128, 4, 2, SRC, EPI>(g, ep, nullptr, 0, s);
+            else return launch_dma<256, 128, 2, 4, SRC, EPI>(g, ep, nullptr, 0, s);
+        default: return launch_dma<128, 128, 2, 2, SRC, EPI>(g, ep, nullptr, 0, s);
+    }
 }
 
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
@@ -540,27 +569,21 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
         return hipGetLastError();
     }
     if (c.M <= kSkinnyMaxM && c.scratch) return skinny_gemm_launch(c, c.scratch, c.scratch_bytes, s);
-    const int nv = c.ep.N * (c.epi == EPI_SWIGLU ? 2 : 1);
-    const bool big = big_tiles(c.M, nv);
     void *part = c.split_scratch;
     const size_t pb = c.split_bytes;
     switch (c.epi) {
         case EPI_QKV:
             g.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2];
-            return big ? launch_dma<256, 256, 2, 4, SRC_CONCAT, EPI_QKV>(g, ep, part, pb, s)
-                       : launch_dma<128, 128, 2, 2, SRC_CONCAT, EPI_QKV>(g, ep, nullptr, 0, s);
+            return launch_planned<SRC_CONCAT, EPI_QKV>(g, ep, part, pb, s);
         case EPI_RESID:
             g.N = c.w_cols[0];
-            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_RESID>(g, ep, part, pb, s)
-                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_RESID>(g, ep, nullptr, 0, s);
+            return launch_planned<SRC_ONE, EPI_RESID>(g, ep, part, pb, s);
         case EPI_SWIGLU:
             g.N = 2 * c.w_cols[0];
-            return big ? launch_dma<256, 256, 2, 4, SRC_DUAL, EPI_SWIGLU>(g, ep, part, pb, s)
-                       : launch_dma<128, 128, 2, 2, SRC_DUAL, EPI_SWIGLU>(g, ep, nullptr, 0, s);
+            return launch_planned<SRC_DUAL, EPI_SWIGLU>(g, ep, part, pb, s);
         case EPI_F32:
             g.N = c.w_cols[0];
-            return big ? launch_dma<256, 256, 2, 4, SRC_ONE, EPI_F32>(g, ep, part, pb, s)
-                       : launch_dma<128, 128, 2, 2, SRC_ONE, EPI_F32>(g, ep, nullptr, 0, s);
+            return launch_planned<SRC_ONE, EPI_F32>(g, ep, part, pb, s);
         default: return hipErrorInvalidValue;
     }
 }
