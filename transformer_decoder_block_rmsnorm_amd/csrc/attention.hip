@@ -94,15 +94,18 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
 //   S^T[keys, queries] = K . Q^T : lane l holds query l%32, so the softmax of
 //                                  a query lives in one lane (plus lane l^32).
 //   O^T[e, queries]   += V^T . P^T : P^T comes straight from the S^T
-//                                  accumulators (converted to bf16); V is
-//                                  stored transposed in LDS with the keys of
-//                                  each 16-key slice permuted to the order in
-//                                  which the accumulator holds them.
+//                                  accumulators (converted to bf16).
+// K and V tiles of 64 keys go from global memory straight into a ring of LDS
+// stages (global_load_lds_dwordx4) in their cache layout, rows of dh values.
+// K rows are read as 16-byte fragments (chunks XOR-swizzled by key); the V^T
+// fragments come from the transpose read ds_read_b64_tr_b16 on rows of V
+// (32-byte granules swizzled by key), taking keys in the order in which the
+// S^T accumulator holds them, so nothing is transposed in registers.
 // Tiles entirely above the causal diagonal are skipped per wave; the
-// workgroups with the longest key ranges are scheduled first.  Keys at or
-// beyond start + T, and (sliding window) below the earliest window of the
-// workgroup, are zero-filled in LDS, so cache rows no query may read (even
-// NaN) never reach the result.
+// workgroups with the longest key ranges are scheduled first.  Rows a tile
+// holds beyond start + T, or (sliding window) below the earliest window of the
+// workgroup, are fetched from a clamped valid row and masked out of the
+// softmax, so cache rows no query may read (even NaN) never reach the result.
 // ---------------------------------------------------------------------------
 struct FlashArgs {
     const bf16_t *q, *kc, *vc;
@@ -115,22 +118,28 @@ struct FlashArgs {
     float scale_log2e;
 };
 
-// Slot of key k (0..15) inside its 16-key slice in the transposed V tile:
-// lane half h reads slots [8h, 8h+8) and must find there the keys it holds in
-// the S^T accumulator: {4h..4h+3, 8+4h..8+4h+3}.
-__device__ __forceinline__ int v_slot(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// 32-byte granule swizzle of V rows: the four rows one 16-lane group of a
+// transpose read touches fall in four different bank groups.
+template <int DH>
+__device__ __forceinline__ int v_granule_swz(int key) {
+    if constexpr (DH >= 128) return swz_tr(key);
+    else return key & 3;
+}
 
 template <int DH, bool PAGED>
-__global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
-    constexpr int BKV = 64;          // keys per tile
-    constexpr int NS = DH / 16;      // 16-wide dh slices of q.k
-    constexpr int NE = DH / 32;      // 32-row e tiles of O^T
-    constexpr int KCH = DH / 8;      // 16-byte chunks per K row
-    constexpr int K_PER = BKV * KCH / 256;
-    constexpr int NVB = (BKV / 8) * (DH / 8);  // 8x8 V blocks per tile
-    __shared__ __attribute__((aligned(16))) bf16_t lds[2 * 2 * BKV * DH];
-    auto Ks = [&](int bf) { return lds + bf * 2 * BKV * DH; };
-    auto Vs = [&](int bf) { return lds + bf * 2 * BKV * DH + BKV * DH; };
+__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
+    constexpr int BKV = 64;                    // keys per tile
+    constexpr int NS = DH / 16;                // 16-wide dh slices of q.k
+    constexpr int NE = DH / 32;                // 32-row e tiles of O^T
+    constexpr int KCH = DH / 8;                // 16-byte chunks per row
+    constexpr int TILE = BKV * DH;             // elements of one K (or V) tile
+    constexpr int NSTG = 2;                    // ring stages
+    constexpr int BLK = 2 * TILE * 2 / 1024;   // 1 KB blocks per stage (K then V)
+    constexpr int PER = BLK / 4;               // DMA instructions per wave per tile
+    constexpr int RPB = 1024 / (DH * 2);       // keys per 1 KB block
+    static_assert(PER * 4 == BLK && RPB * DH * 2 == 1024, "tile splits into 1 KB blocks per wave");
+    __shared__ __attribute__((aligned(1024))) bf16_t lds[NSTG * 2 * TILE];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lh = lane >> 5;
@@ -177,47 +186,29 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
     // cache row j of this sequence and KV head (a contiguous slab unless paged)
     const int64_t slab = ((int64_t)b * a.Hkv + kvh) * a.t_max;
     auto row = [&](int j) -> int64_t { return PAGED ? kv_row(a.kvm, b, a.Hkv, kvh, j) : slab + j; };
-    u32x4 rk[K_PER], rv[8];
-    auto load_tile = [&](int it) {
+
+    // Per-lane part of this wave's DMA blocks: block bi (K for bi < BLK/2,
+    // then V) holds keys RPB*(bi % (BLK/2)) .. +RPB-1; lane slot -> key and
+    // the element offset inside the row that belongs in that LDS slot.
+    int dkey[PER], doff[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int bi = wave * PER + i, isv = bi >= BLK / 2;
+        const int key = (bi % (BLK / 2)) * RPB + lane / KCH, pch = lane % KCH;
+        dkey[i] = key;
+        doff[i] = isv ? 16 * ((pch >> 1) ^ v_granule_swz<DH>(key)) + 8 * (pch & 1)  // V: granules
+                      : 8 * (pch ^ (key & (KCH - 1)));                              // K: chunks
+    }
+    auto issue = [&](int it, int stg) {
         const int j0 = it * BKV;
+        int64_t rows[PER];
 #pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int c = tid + 256 * i, key = c / KCH, ch = c % KCH, j = j0 + key;
-            rk[i] = (j < kv_len && j >= key_floor)
-                        ? *(const u32x4 *)(a.kc + row(j) * DH + ch * 8)
-                        : u32x4{0, 0, 0, 0};
-        }
-        if (tid < NVB) {
-            const int kb = tid / (DH / 8), eb = tid % (DH / 8);
+        for (int i = 0; i < PER; ++i) rows[i] = row(min(max(j0 + dkey[i], key_floor), kv_len - 1));
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + stg * (2 * TILE * 2) + wave * PER * 1024);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int j = j0 + kb * 8 + r;
-                rv[r] = (j < kv_len && j >= key_floor)
-                            ? *(const u32x4 *)(a.vc + row(j) * DH + eb * 8)
-                            : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&](int bf) {
-#pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int c = tid + 256 * i, key = c / KCH, ch = c % KCH;
-            *(u32x4 *)(Ks(bf) + key * DH + ((ch ^ (key & (KCH - 1))) * 8)) = rk[i];
-        }
-        if (tid < NVB) {
-            const int kb = tid / (DH / 8), eb = tid % (DH / 8);
-            u32x4 t[8];
-            transpose8x8_bf16(rv, t);
-            // keys kb*8 .. kb*8+7: first four go to slot v_slot(8*(kb&1)), last four to v_slot(8*(kb&1)+4)
-            const int base = (kb >> 1) * 16;
-            const int p_lo = base + v_slot(8 * (kb & 1)), p_hi = base + v_slot(8 * (kb & 1) + 4);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int e = eb * 8 + c;
-                bf16_t *row = Vs(bf) + e * BKV;
-                *(u32x2 *)(row + (((p_lo >> 3) ^ swz_row(e)) << 3) + (p_lo & 7)) = u32x2{t[c][0], t[c][1]};
-                *(u32x2 *)(row + (((p_hi >> 3) ^ swz_row(e)) << 3) + (p_hi & 7)) = u32x2{t[c][2], t[c][3]};
-            }
+        for (int i = 0; i < PER; ++i) {
+            const bf16_t *src = (wave * PER + i < BLK / 2 ? a.kc : a.vc) + rows[i] * DH + doff[i];
+            dma16(src, base + i * 1024);
         }
     };
 
@@ -228,13 +219,19 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
         for (int v = 0; v < 16; ++v) oacc[te][v] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    load_tile(first_tile);
-    store_tile(0);
-    __syncthreads();
+    // transpose-read geometry: 16-lane group q reads e columns 16(q&1)+..,
+    // keys 4(q>>1)+.. of each 8-key half of a 16-key slice
+    const int q4 = lane >> 4, sl = lane & 15;
+    const int v_row = 4 * (q4 >> 1) + (sl >> 2), v_in = (sl & 3) * 4;
+
+    issue(first_tile, 0);
     for (int it = first_tile; it < n_tiles; ++it) {
-        const int bf = (it - first_tile) & 1;
-        if (it + 1 < n_tiles) load_tile(it + 1);
+        const int stg = (it - first_tile) % NSTG;
+        wait_vmcnt<0>();                         // this wave's loads of tile it landed
+        asm volatile("s_barrier" ::: "memory");  // every wave's did; every wave is done with tile it-1
+        if (it + 1 < n_tiles) issue(it + 1, (stg + 1) % NSTG);
         if (it < wave_tiles && it >= wave_first_tile) {
+            const bf16_t *Ks = lds + stg * 2 * TILE, *Vs = Ks + TILE;
             const int j0 = it * BKV;
             f32x16 sacc[2];
 #pragma unroll
@@ -245,12 +242,17 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     const bf16x8 kf =
-                        as_bf16x8(*(const u32x4 *)(Ks(bf) + key * DH + (((2 * s + lh) ^ (key & (KCH - 1))) * 8)));
+                        as_bf16x8(*(const u32x4 *)(Ks + key * DH + (((2 * s + lh) ^ (key & (KCH - 1))) * 8)));
                     sacc[kt] = mfma32(kf, qf[s], sacc[kt]);
                 }
             }
-            // online softmax in the log2 domain
-            // the diagonal crosses this tile, or (window) its lower edge does
+            // Online softmax in the log2 domain.  The reference max of a
+            // query moves only when a tile raises it by more than 2^8 (in
+            // exponent units): until then the weights 2^(x - m) stay below
+            // 256 and the running sums stay exact up to rounding, so the
+            // output accumulators are rescaled only on those rare tiles.
+            // The diagonal crosses this tile, or (window) its lower edge
+            // does; rows past start + T sit above every real query's diagonal.
             const bool need_mask = (j0 + BKV - 1 > start + t0) || (W > 0 && j0 < start + t0 + 31 - W + 1);
             const int key_lo = W > 0 ? qpos - W + 1 : 0;
             float mx = -INFINITY;
@@ -258,34 +260,37 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    float x = sacc[kt][v] * a.scale_log2e;
                     if (need_mask) {
                         const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                        if (key > qpos || key < key_lo) x = -INFINITY;
+                        if (key > qpos || key < key_lo) sacc[kt][v] = -INFINITY;
                     }
-                    sacc[kt][v] = x;
-                    mx = fmaxf(mx, x);
+                    mx = fmaxf(mx, sacc[kt][v]);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            const float msub = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2e;
+            const bool grow = mx > m_run + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+                if (grow) m_run = mx;
+                l_run *= alpha;
+#pragma unroll
+                for (int te = 0; te < NE; ++te)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) oacc[te][v] *= alpha;
+            }
+            const float msub = m_run == -INFINITY ? 0.0f : m_run;
             float sum = 0.0f;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float p = __builtin_amdgcn_exp2f(sacc[kt][v] - msub);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], a.scale_log2e, -msub));
                     sacc[kt][v] = p;
                     sum += p;
                 }
             sum += __shfl_xor(sum, 32, 64);
-            l_run = l_run * alpha + sum;
-            m_run = m_new;
-#pragma unroll
-            for (int te = 0; te < NE; ++te)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) oacc[te][v] *= alpha;
+            l_run += sum;
+            // P^T fragment of 16-key slice s2: lane (query lr, half lh) holds
+            // keys 16 s2 + {4lh .. 4lh+3, 8+4lh .. 8+4lh+3}
             bf16x8 pf[4];
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
@@ -300,18 +305,18 @@ __global__ __launch_bounds__(256) void flash_prefill_kernel(FlashArgs a) {
             }
 #pragma unroll
             for (int te = 0; te < NE; ++te) {
-                const int e = te * 32 + lr;
+                const int gran = 2 * te + (q4 & 1);
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2) {
-                    const bf16x8 vf =
-                        as_bf16x8(*(const u32x4 *)(Vs(bf) + e * BKV + (((2 * s2 + lh) ^ swz_row(e)) * 8)));
-                    oacc[te] = mfma32(vf, pf[s2], oacc[te]);
+                    const int r0 = 16 * s2 + v_row, r1 = r0 + 8;
+                    const u32x2 lo = lds_read_tr16(Vs + r0 * DH + ((gran ^ v_granule_swz<DH>(r0)) * 16) + v_in);
+                    const u32x2 hi = lds_read_tr16(Vs + r1 * DH + ((gran ^ v_granule_swz<DH>(r1)) * 16) + v_in);
+                    oacc[te] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[s2], oacc[te]);
                 }
             }
         }
-        if (it + 1 < n_tiles) store_tile(bf ^ 1);
-        __syncthreads();
     }
+    wait_vmcnt<0>();
 
     const int t = t0 + lr;
     if (wave_active && t < Tb) {
