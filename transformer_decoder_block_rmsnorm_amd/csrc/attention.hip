@@ -88,9 +88,15 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
 // entry and [MSA] 6: exact attention computed tile by tile with a running
 // softmax, never materialising the T x T score matrix).
 //
-// Workgroup = 4 waves = 128 query rows of one KV head's group: HG heads of the
-// group side by side times 128/HG positions, so every K/V tile loaded into LDS
-// serves all query heads that share it (GQA).  Each wave owns 32 queries.
+// Workgroup = NGRP groups of 4 waves over the same 128 query rows of one KV
+// head's group (HG heads of the group side by side times 128/HG positions),
+// so every K/V tile loaded into LDS serves all query heads that share it
+// (GQA).  Each wave owns 32 queries.  With NGRP = 2 the two groups take the
+// lower and the upper half of the workgroup's key tiles, each with its own
+// LDS ring and running softmax, and are merged through LDS at the end: used
+// when the whole grid is resident at once, where the longest causal key
+// range is the critical path.  Larger grids run NGRP = 1 at two workgroups
+// per CU, where one workgroup's start and end overlap the other's work.
 //   S^T[keys, queries] = K . Q^T : lane l holds query l%32, so the softmax of
 //                                  a query lives in one lane (plus lane l^32).
 //   O^T[e, queries]   += V^T . P^T : P^T comes straight from the S^T
@@ -126,8 +132,8 @@ __device__ __forceinline__ int v_granule_swz(int key) {
     else return key & 3;
 }
 
-template <int DH, bool PAGED>
-__global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
+template <int DH, bool PAGED, int NGRP>
+__global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(FlashArgs a) {
     constexpr int BKV = 64;                    // keys per tile
     constexpr int NS = DH / 16;                // 16-wide dh slices of q.k
     constexpr int NE = DH / 32;                // 32-row e tiles of O^T
@@ -138,10 +144,13 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     constexpr int PER = BLK / 4;               // DMA instructions per wave per tile
     constexpr int RPB = 1024 / (DH * 2);       // keys per 1 KB block
     static_assert(PER * 4 == BLK && RPB * DH * 2 == 1024, "tile splits into 1 KB blocks per wave");
-    __shared__ __attribute__((aligned(1024))) bf16_t lds[NSTG * 2 * TILE];
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;
+    __shared__ __attribute__((aligned(1024))) bf16_t lds[NGRP * NSTG * 2 * TILE];  // a ring per wave group
+    static_assert(NGRP == 1 || 2 * NSTG * 2 * TILE * 2 >= 4 * (NE * 16 + 2) * 64 * 4, "merge staging fits");
+    const int grp = NGRP == 2 ? (int)(threadIdx.x >> 8) : 0;  // wave group: lower / upper half of the key tiles
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds + grp * (NSTG * 2 * TILE * 2);
+    bf16_t *const ring = lds + grp * (NSTG * 2 * TILE);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, lh = lane >> 5;
     const int nbh = a.B * a.Hkv * a.n_hsub;
     const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / nbh);  // longest key ranges first
@@ -224,14 +233,18 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
     const int q4 = lane >> 4, sl = lane & 15;
     const int v_row = 4 * (q4 >> 1) + (sl >> 2), v_in = (sl & 3) * 4;
 
-    issue(first_tile, 0);
-    for (int it = first_tile; it < n_tiles; ++it) {
-        const int stg = (it - first_tile) % NSTG;
+    // key tiles of this wave group; both groups run n_lo steps (the upper
+    // half has at most as many tiles) so that their barriers pair up
+    const int n_lo = NGRP == 2 ? (n_tiles - first_tile + 1) / 2 : n_tiles - first_tile;
+    const int g_first = grp ? first_tile + n_lo : first_tile, g_end = grp ? n_tiles : first_tile + n_lo;
+    if (g_first < g_end) issue(g_first, 0);
+    for (int step = 0; step < n_lo; ++step) {
+        const int it = g_first + step, stg = step % NSTG;
         wait_vmcnt<0>();                         // this wave's loads of tile it landed
-        asm volatile("s_barrier" ::: "memory");  // every wave's did; every wave is done with tile it-1
-        if (it + 1 < n_tiles) issue(it + 1, (stg + 1) % NSTG);
-        if (it < wave_tiles && it >= wave_first_tile) {
-            const bf16_t *Ks = lds + stg * 2 * TILE, *Vs = Ks + TILE;
+        asm volatile("s_barrier" ::: "memory");  // every wave's did; every wave is done with the previous tile
+        if (it + 1 < g_end) issue(it + 1, (stg + 1) % NSTG);
+        if (it < g_end && it < wave_tiles && it >= wave_first_tile) {
+            const bf16_t *Ks = ring + stg * 2 * TILE, *Vs = Ks + TILE;
             const int j0 = it * BKV;
             f32x16 sacc[2];
 #pragma unroll
@@ -317,6 +330,35 @@ __global__ __launch_bounds__(256, 2) void flash_prefill_kernel(FlashArgs a) {
         }
     }
     wait_vmcnt<0>();
+    if constexpr (NGRP == 2) {
+        __syncthreads();  // both rings are free: they hold the merge staging now
+
+        // Merge the two groups' partial softmax states: (m, l, O) of the
+        // upper group go through LDS to the wave of the lower group that owns
+        // the same queries; both are relative to 2^m of their own group.
+        float *xs = (float *)lds + wave * ((NE * 16 + 2) * 64);
+        if (grp == 1) {
+#pragma unroll
+            for (int te = 0; te < NE; ++te)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xs[(te * 16 + v) * 64 + lane] = oacc[te][v];
+            xs[NE * 16 * 64 + lane] = m_run;
+            xs[(NE * 16 + 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        {
+            const float m1 = xs[NE * 16 * 64 + lane], l1 = xs[(NE * 16 + 1) * 64 + lane];
+            const float m = fmaxf(m_run, m1);
+            const float c0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+            const float c1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+            l_run = l_run * c0 + l1 * c1;
+#pragma unroll
+            for (int te = 0; te < NE; ++te)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[te][v] = oacc[te][v] * c0 + xs[(te * 16 + v) * 64 + lane] * c1;
+        }
+    }
 
     const int t = t0 + lr;
     if (wave_active && t < Tb) {
@@ -354,15 +396,31 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     a.n_qblocks = (c.T + a.PB - 1) / a.PB;
     a.scale_log2e = c.scale * 1.4426950408889634f;
     const int blocks = a.n_qblocks * c.B * c.Hkv * a.n_hsub;
+    // the whole grid resident at once (two single-group workgroups per CU):
+    // split each workgroup's key range over two wave groups
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const bool two = blocks <= 2 * cus;
     const bool paged = a.kvm.table != nullptr;
-    if (c.dh == 128 && paged)
-        hipLaunchKernelGGL((flash_prefill_kernel<128, true>), dim3(blocks), dim3(256), 0, s, a);
-    else if (c.dh == 128)
-        hipLaunchKernelGGL((flash_prefill_kernel<128, false>), dim3(blocks), dim3(256), 0, s, a);
-    else if (paged)
-        hipLaunchKernelGGL((flash_prefill_kernel<64, true>), dim3(blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((flash_prefill_kernel<64, false>), dim3(blocks), dim3(256), 0, s, a);
+    const dim3 g(blocks), b1(256), b2(512);
+    if (c.dh == 128) {
+        if (paged) {
+            if (two) hipLaunchKernelGGL((flash_prefill_kernel<128, true, 2>), g, b2, 0, s, a);
+            else hipLaunchKernelGGL((flash_prefill_kernel<128, true, 1>), g, b1, 0, s, a);
+        } else {
+            if (two) hipLaunchKernelGGL((flash_prefill_kernel<128, false, 2>), g, b2, 0, s, a);
+            else hipLaunchKernelGGL((flash_prefill_kernel<128, false, 1>), g, b1, 0, s, a);
+        }
+    } else {
+        if (paged) {
+            if (two) hipLaunchKernelGGL((flash_prefill_kernel<64, true, 2>), g, b2, 0, s, a);
+            else hipLaunchKernelGGL((flash_prefill_kernel<64, true, 1>), g, b1, 0, s, a);
+        } else {
+            if (two) hipLaunchKernelGGL((flash_prefill_kernel<64, false, 2>), g, b2, 0, s, a);
+            else hipLaunchKernelGGL((flash_prefill_kernel<64, false, 1>), g, b1, 0, s, a);
+        }
+    }
     return hipGetLastError();
 }
 
