@@ -150,6 +150,14 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_byte_addr) 
                  : "memory", "m0");
 }
 
+// The same for data streamed once (weights in decode GEMMs): the nontemporal
+// policy keeps it from displacing reused lines in the caches; measured on
+// MI355X it roughly doubles the rate of a weight stream over the plain form.
+__device__ __forceinline__ void dma16_stream(const void *gptr, uint32_t lds_byte_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_byte_addr), "v"(gptr)
+                 : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -4,16 +4,19 @@
 // Transformer" (6. Under the hood: a decode step reads every weight once and
 // is bandwidth bound).
 //
-// Work unit = one wave: a 128-column block of W times a K-slice.  Per 32-row
-// k step a lane loads 8 rows x 16 bytes of W (lanes l and l+16k read whole
-// 256-byte row segments, so each load instruction covers 4 full rows) with
-// the nontemporal hint, transposes the 8x8 block in registers and feeds it as
-// the B operand of eight MFMA 16x16x32 (output column n of MFMA c is
-// 8n + c of the block).  x fragments (the A operand) come through L1/L2.
-// Several k steps are in flight per wave.  Each wave writes an fp32 partial
-// [slice][M][N]; a second kernel adds the slices in a fixed order and applies
-// the fused epilogue (RoPE + KV append, residual, SwiGLU, fp32 store), so the
-// result is deterministic.
+// Work unit = one 4-wave workgroup: a BN-column block of W (BN = 64 or 128)
+// times a range of k, split only as far as needed to give every compute unit
+// a workgroup.  Stages of 64 k rows of the weight block, plus the same 64
+// columns of x (64 rows, rows past M clamped), go from global memory straight
+// into a ring of LDS stages (global_load_lds_dwordx4 with the nontemporal
+// policy), so the loads in flight cost no registers and the ring keeps
+// several stages of HBM reads outstanding.  Each wave owns BN/4 output columns: its weight fragments come
+// from the transpose read ds_read_b64_tr_b16 on the N-contiguous weight rows
+// (32-byte granules swizzled by row), the x fragments are 16-byte reads
+// (chunks swizzled by row), and the products run on MFMA 16x16x32.  Each
+// workgroup writes an fp32 partial [split][M][N]; a second kernel adds the
+// splits in a fixed order and applies the fused epilogue (RoPE + KV append,
+// residual, SwiGLU, fp32 store), so the result is deterministic.
 #include <algorithm>
 
 #include "epilogue.h"
@@ -25,90 +28,145 @@ struct SkinnyArgs {
     const bf16_t *x;  // [M, K]
     int64_t ldx;
     int M, K, N;      // N = columns of the virtual B
-    int slices, ks;   // K-slices and rows per slice (multiple of 32)
+    int splits;       // k ranges per column block
     const bf16_t *w[3];
     int w_cols[3];
     int src;          // 0: one matrix, 1: concat (wq|wk|wv), 2: two matrices side by side (w1|w3)
-    float *part;      // [slices][M][N]
+    float *part;      // [splits][M][N]
 };
 
 // Column c of the virtual B -> (matrix, column).  Concat: matrices side by
-// side; dual: w1 columns then w3 columns.
-__device__ __forceinline__ const bf16_t *b_column(const SkinnyArgs &a, int c, int &ld, bool &ok) {
+// side; dual: w1 columns then w3 columns.  Every matrix width is a multiple of
+// 64, so an 8-column chunk never straddles two matrices.
+__device__ __forceinline__ const bf16_t *b_column(const SkinnyArgs &a, int c, int &ld) {
     int s = 0;
     if (a.src != 0) {
         while (s < 2 && a.w[s + 1] && c >= a.w_cols[s]) { c -= a.w_cols[s]; ++s; }
     }
     ld = a.w_cols[s];
-    ok = c < ld;
-    return a.w[s] + (ok ? c : 0);
+    return a.w[s] + min(c, ld - 8);
 }
 
-template <int MT, int UNROLL>
-__global__ __launch_bounds__(64) void skinny_gemm_kernel(SkinnyArgs a) {
-    // one wave per workgroup, so the tasks spread over every CU
-    const int lane = threadIdx.x & 63;
-    const int ln = lane & 15, g4 = lane >> 4;
-    const int n_cb = (a.N + 127) / 128;
-    const int task = blockIdx.x;
-    if (task >= n_cb * a.slices) return;  // no barriers in this kernel
-    const int cb = task % n_cb, sl = task / n_cb;
-    const int c0 = cb * 128;
-    const int k_lo = sl * a.ks, k_hi = min(a.K, k_lo + a.ks);
+// 32-byte granule swizzle of a weight row in LDS: the four rows one 16-lane
+// group of a transpose read touches fall in distinct bank groups.
+template <int BN>
+__device__ __forceinline__ int skinny_gswz(int row) {
+    if constexpr (BN >= 128) return swz_tr(row);
+    else return row & 3;
+}
 
-    int ld;
-    bool col_ok;
-    const bf16_t *wcol = b_column(a, c0 + 8 * ln, ld, col_ok);
+template <int BN, int MT>
+__global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
+    constexpr int SK = 64;                     // k rows per stage
+    constexpr int WST = SK * BN;               // weight elements per stage
+    constexpr int XST = 64 * SK;               // x elements per stage (64 rows)
+    constexpr int STAGE = WST + XST;
+    constexpr int NST = (BN >= 128) ? 6 : 8;   // ring stages (144 / 128 KB)
+    constexpr int WBLK = WST * 2 / 1024, XBLK = XST * 2 / 1024;  // 1 KB blocks
+    constexpr int PW = WBLK / 4, PX = XBLK / 4, PER = PW + PX;   // DMAs per wave per stage
+    constexpr int WRPB = 1024 / (BN * 2);      // weight rows per 1 KB block
+    constexpr int CPR = BN / 8;                // 16-byte chunks per weight row
+    constexpr int NC = BN / 64;                // 16-column tiles per wave
+    static_assert(PW * 4 == WBLK && PX * 4 == XBLK, "stage splits into 1 KB blocks per wave");
+    __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;
 
-    f32x4 acc[MT][8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_cb = a.N / BN;
+    const int cb = (int)blockIdx.x % n_cb, sp = (int)blockIdx.x / n_cb;
+    const int c0 = cb * BN;
+    const int n_st_all = a.K / SK;
+    const int st_lo = sp * n_st_all / a.splits, st_hi = (sp + 1) * n_st_all / a.splits;
+    const int n_st = st_hi - st_lo;
+
+    // per-lane DMA sources (stage 0 of this range; later stages step by SK rows)
+    const bf16_t *wsrc[PW];
+    int wld[PW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+        const int row = (wave * PW + i) * WRPB + lane / CPR, p = lane % CPR;
+        const int col = c0 + 16 * ((p >> 1) ^ skinny_gswz<BN>(row)) + 8 * (p & 1);
+        int ld;
+        const bf16_t *base = b_column(a, col, ld);
+        wld[i] = ld;
+        wsrc[i] = base + (int64_t)(st_lo * SK + row) * ld;
+    }
+    const bf16_t *xsrc[PX];
+#pragma unroll
+    for (int i = 0; i < PX; ++i) {
+        const int row = (wave * PX + i) * 8 + lane / 8, p = lane % 8;  // x rows of 128 bytes
+        xsrc[i] = a.x + (int64_t)min(row, a.M - 1) * a.ldx + st_lo * SK + 8 * (p ^ (row & 7));
+    }
+    auto issue = [&](int st, int slot) {
+        const uint32_t wb = __builtin_amdgcn_readfirstlane(lds_base + slot * STAGE * 2 + wave * PW * 1024);
+        const uint32_t xb = __builtin_amdgcn_readfirstlane(lds_base + slot * STAGE * 2 + WST * 2 + wave * PX * 1024);
+#pragma unroll
+        for (int i = 0; i < PW; ++i) dma16_stream(wsrc[i] + (int64_t)st * SK * wld[i], wb + i * 1024);
+#pragma unroll
+        for (int i = 0; i < PX; ++i) dma16_stream(xsrc[i] + st * SK, xb + i * 1024);
+    };
+    auto wait_stages = [&](int n) {  // at most n later stages of this wave still in flight
+        switch (n) {
+            case 0: wait_vmcnt<0>(); break;
+            case 1: wait_vmcnt<PER>(); break;
+            case 2: wait_vmcnt<2 * PER>(); break;
+            case 3: wait_vmcnt<3 * PER>(); break;
+            case 4: wait_vmcnt<4 * PER>(); break;
+            case 5: wait_vmcnt<5 * PER>(); break;
+            case 6: wait_vmcnt<6 * PER>(); break;
+            default: wait_vmcnt<7 * PER>(); break;
+        }
+    };
+
+    f32x4 acc[MT][NC];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[mt][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < NC; ++t) acc[mt][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int k0 = k_lo; k0 < k_hi; k0 += 32 * UNROLL) {
-        u32x4 wr[UNROLL][8];
+    // fragment geometry: 16-lane group g4 holds k 8 g4 .. 8 g4 + 7 of a 32-k step
+    const int g4 = lane >> 4, ln = lane & 15;
+    const int b_row = 8 * g4 + (ln >> 2), b_in = 4 * (ln & 3);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int kb = k0 + 32 * u + 8 * g4;
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < n_st) issue(s, s);
+    for (int st = 0; st < n_st; ++st) {
+        wait_stages(min(NST - 2, n_st - 1 - st));  // stage st landed
+        asm volatile("s_barrier" ::: "memory");    // every wave's did; stage st-1's slot is free
+        if (st + NST - 1 < n_st) issue(st + NST - 1, (st + NST - 1) % NST);
+        const bf16_t *Ws = lds + (st % NST) * STAGE, *Xs = Ws + WST;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int k = kb + r;
-                wr[u][r] = (col_ok && k < k_hi) ? ld_stream(wcol + (int64_t)k * ld) : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < SK / 32; ++ks) {
+            bf16x8 bf[NC], af[MT];
+#pragma unroll
+            for (int t = 0; t < NC; ++t) {
+                const int gran = (wave * (BN / 4) + 16 * t) / 16;
+                const int r0 = 32 * ks + b_row, r1 = r0 + 4;
+                const u32x2 lo = lds_read_tr16(Ws + r0 * BN + ((gran ^ skinny_gswz<BN>(r0)) * 16) + b_in);
+                const u32x2 hi = lds_read_tr16(Ws + r1 * BN + ((gran ^ skinny_gswz<BN>(r1)) * 16) + b_in);
+                bf[t] = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int kb = k0 + 32 * u + 8 * g4;
-            bf16x8 af[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const int m = 16 * mt + ln;
-                u32x4 v = {0, 0, 0, 0};
-                if (m < a.M && kb < k_hi) v = *(const u32x4 *)(a.x + (int64_t)m * a.ldx + kb);
-                af[mt] = as_bf16x8(v);
+                const int row = 16 * mt + ln, ch = 4 * ks + g4;
+                af[mt] = as_bf16x8(*(const u32x4 *)(Xs + row * SK + 8 * (ch ^ (row & 7))));
             }
-            u32x4 wt[8];
-            transpose8x8_bf16(wr[u], wt);
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt][c] = mfma16(af[mt], as_bf16x8(wt[c]), acc[mt][c]);
+                for (int t = 0; t < NC; ++t) acc[mt][t] = mfma16(af[mt], bf[t], acc[mt][t]);
         }
     }
-    // partial: rows 16mt + 4*g4 + v, columns c0 + 8*ln + c (c = 0..7)
-    const int col = c0 + 8 * ln;
-    if (col >= a.N) return;
-    float *dst = a.part + (int64_t)sl * a.M * a.N;
+    // partial: rows 16 mt + 4 g4 + v, column c0 + wave * BN/4 + 16 t + ln
+    float *dst = a.part + (int64_t)sp * a.M * a.N;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = 16 * mt + 4 * g4 + v;
             if (m >= a.M) continue;
-            float *p = dst + (int64_t)m * a.N + col;
-            *(f32x4 *)p = f32x4{acc[mt][0][v], acc[mt][1][v], acc[mt][2][v], acc[mt][3][v]};
-            *(f32x4 *)(p + 4) = f32x4{acc[mt][4][v], acc[mt][5][v], acc[mt][6][v], acc[mt][7][v]};
+#pragma unroll
+            for (int t = 0; t < NC; ++t) dst[(int64_t)m * a.N + c0 + wave * (BN / 4) + 16 * t + ln] = acc[mt][t][v];
         }
 }
 
@@ -145,23 +203,32 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float *part, i
     }
 }
 
-// Splits of K for a skinny GEMM: enough waves to keep many loads in flight,
-// while the fp32 partials stay below half of the weight bytes.
-static void skinny_split(int M, int K, int N, int &slices, int &ks) {
-    const int n_cb = (N + 127) / 128;
-    const int mpad = ((M + 15) / 16) * 16;
-    int s_cap = (K * 2) / (2 * 4 * mpad);       // partial bytes <= weight bytes / 2
-    int s_want = (2048 + n_cb - 1) / n_cb;      // ~2048 waves
-    int s = std::max(1, std::min(s_cap, s_want));
-    s = std::min(s, K / 32);
-    ks = ((K + s - 1) / s + 31) / 32 * 32;
-    slices = (K + ks - 1) / ks;
+// Column block width and k splits of a skinny GEMM: 128-column blocks when N
+// allows (each workgroup also streams its x slice, 64/BN of its weight bytes),
+// then k is split so that the workgroups come close to one per compute unit
+// without exceeding it.
+static void skinny_plan(int K, int N, int &bn, int &splits) {
+    bn = N % 128 == 0 ? 128 : 64;
+    const int n_cb = N / bn;
+    splits = std::max(1, std::min(256 / n_cb, K / 64));
+    splits = std::min(splits, 16);
 }
 
 size_t skinny_part_bytes(int M, int K, int N) {
-    int slices, ks;
-    skinny_split(M, K, N, slices, ks);
-    return (size_t)slices * M * N * sizeof(float);
+    int bn, splits;
+    skinny_plan(K, N, bn, splits);
+    return (size_t)splits * M * N * sizeof(float);
+}
+
+template <int BN>
+static void skinny_launch_bn(const SkinnyArgs &a, int blocks, hipStream_t s) {
+    const int mt = (a.M + 15) / 16;
+    switch (mt) {
+        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 1>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 2>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 3>), dim3(blocks), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 4>), dim3(blocks), dim3(256), 0, s, a); break;
+    }
 }
 
 hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, hipStream_t s) {
@@ -175,28 +242,27 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     if (c.epi == EPI_QKV) { a.src = 1; a.N = c.w_cols[0] + c.w_cols[1] + c.w_cols[2]; }
     else if (c.epi == EPI_SWIGLU) { a.src = 2; a.N = 2 * c.w_cols[0]; a.w[2] = nullptr; }
     else { a.src = 0; a.N = c.w_cols[0]; a.w[1] = a.w[2] = nullptr; }
-    skinny_split(a.M, a.K, a.N, a.slices, a.ks);
-    if ((size_t)a.slices * a.M * a.N * sizeof(float) > part_bytes || a.M > 64) return hipErrorInvalidValue;
+    // the stage and block layout needs whole 64-row stages and 64-column
+    // blocks, 16-byte aligned rows of x, and every matrix a multiple of 64 wide
+    if (a.M < 1 || a.M > 64 || a.K % 64 || a.N % 64 || a.ldx % 8) return hipErrorInvalidValue;
+    for (int i = 0; i < 3; ++i)
+        if (a.w[i] && a.w_cols[i] % 64) return hipErrorInvalidValue;
+    int bn;
+    skinny_plan(a.K, a.N, bn, a.splits);
+    if ((size_t)a.splits * a.M * a.N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
     a.part = (float *)part;
-    const int n_cb = (a.N + 127) / 128;
-    const int waves = n_cb * a.slices;
-    dim3 grid(waves);
-    const int mt = (a.M + 15) / 16;
-    switch (mt) {
-        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<1, 4>), grid, dim3(64), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<2, 4>), grid, dim3(64), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<3, 2>), grid, dim3(64), 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_gemm_kernel<4, 2>), grid, dim3(64), 0, s, a); break;
-    }
+    const int blocks = (a.N / bn) * a.splits;
+    if (bn == 128) skinny_launch_bn<128>(a, blocks, s);
+    else skinny_launch_bn<64>(a, blocks, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)a.M * (n_out / 2);
     dim3 rg((unsigned)((threads + 255) / 256));
     switch (c.epi) {
-        case EPI_QKV: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_QKV>, rg, dim3(256), 0, s, a.part, a.slices, a.M, a.N, n_out, c.ep); break;
-        case EPI_RESID: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_RESID>, rg, dim3(256), 0, s, a.part, a.slices, a.M, a.N, n_out, c.ep); break;
-        case EPI_SWIGLU: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_SWIGLU>, rg, dim3(256), 0, s, a.part, a.slices, a.M, a.N, n_out, c.ep); break;
-        case EPI_F32: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_F32>, rg, dim3(256), 0, s, a.part, a.slices, a.M, a.N, n_out, c.ep); break;
+        case EPI_QKV: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_QKV>, rg, dim3(256), 0, s, a.part, a.splits, a.M, a.N, n_out, c.ep); break;
+        case EPI_RESID: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_RESID>, rg, dim3(256), 0, s, a.part, a.splits, a.M, a.N, n_out, c.ep); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_SWIGLU>, rg, dim3(256), 0, s, a.part, a.splits, a.M, a.N, n_out, c.ep); break;
+        case EPI_F32: hipLaunchKernelGGL(skinny_reduce_kernel<EPI_F32>, rg, dim3(256), 0, s, a.part, a.splits, a.M, a.N, n_out, c.ep); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
