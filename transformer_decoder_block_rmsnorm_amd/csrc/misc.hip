@@ -8,6 +8,58 @@ namespace tfb {
 
 // RMSNorm ([TIR] Code, rms_norm; [PID] Tiny example, rmsnorm): one wave per
 // row, fp32 sum of squares reduced across the wave, y = x * r * g.
+// Vector path (bf16 output): each lane owns NCH 16-byte chunks of the row
+// (chunk i of lane l holds elements 64 EPC i + EPC l ..), loads them all at
+// once, keeps them in registers for the reduction and the scaled write, so a
+// row is read from memory once.  Other widths or fp32 output: a plain
+// two-pass loop.
+template <typename Tin, int NCH>
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const Tin *x, int64_t ldx, const bf16_t *g, bf16_t *y,
+                                                          int64_t ldy, int rows, float eps) {
+    constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
+    constexpr int D = 64 * EPC * NCH;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const Tin *xr = x + (int64_t)row * ldx;
+    u32x4 v[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) v[i] = *(const u32x4 *)(xr + 64 * EPC * i + EPC * lane);
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if constexpr (EPC == 8) {
+                const float a = bf16_lo(v[i][w]), b = bf16_hi(v[i][w]);
+                ss += a * a + b * b;
+            } else {
+                const float a = __uint_as_float(v[i][w]);
+                ss += a * a;
+            }
+        }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    bf16_t *yr = y + (int64_t)row * ldy;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int c = 64 * EPC * i + EPC * lane;
+        if constexpr (EPC == 8) {
+            const u32x4 gv = *(const u32x4 *)(g + c);
+            u32x4 o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                o[w] = pack_bf16x2(bf16_lo(v[i][w]) * r * bf16_lo(gv[w]), bf16_hi(v[i][w]) * r * bf16_hi(gv[w]));
+            *(u32x4 *)(yr + c) = o;
+        } else {
+            const u32x2 gv = *(const u32x2 *)(g + c);
+            u32x2 o;
+            o[0] = pack_bf16x2(__uint_as_float(v[i][0]) * r * bf16_lo(gv[0]), __uint_as_float(v[i][1]) * r * bf16_hi(gv[0]));
+            o[1] = pack_bf16x2(__uint_as_float(v[i][2]) * r * bf16_lo(gv[1]), __uint_as_float(v[i][3]) * r * bf16_hi(gv[1]));
+            *(u32x2 *)(yr + c) = o;
+        }
+    }
+}
+
 template <typename Tin, typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const Tin *x, int64_t ldx, const T *g, T *y, int64_t ldy,
                                                       int rows, int d, float eps) {
@@ -16,55 +68,45 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const Tin *x, int64_t ldx,
     const Tin *xr = x + (int64_t)row * ldx;
     T *yr = y + (int64_t)row * ldy;
     float ss = 0.0f;
-    if constexpr (sizeof(Tin) == 2) {
-        for (int c = lane * 8; c < d; c += 512) {
-            u32x4 v = *(const u32x4 *)(xr + c);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float a = bf16_lo(v[w]), b = bf16_hi(v[w]);
-                ss += a * a + b * b;
-            }
-        }
-    } else {
-        for (int c = lane; c < d; c += 64) ss += xr[c] * xr[c];
+    for (int c = lane; c < d; c += 64) {
+        const float a = Elem<Tin>::load(xr, c);
+        ss += a * a;
     }
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)d + eps);
-    if constexpr (sizeof(T) == 2 && sizeof(Tin) == 2) {
-        for (int c = lane * 8; c < d; c += 512) {
-            u32x4 v = *(const u32x4 *)(xr + c), gv = *(const u32x4 *)(g + c), o;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                o[w] = pack_bf16x2(bf16_lo(v[w]) * r * bf16_lo(gv[w]), bf16_hi(v[w]) * r * bf16_hi(gv[w]));
-            *(u32x4 *)(yr + c) = o;
-        }
-    } else if constexpr (sizeof(T) == 2) {
-        for (int c = lane * 8; c < d; c += 512) {
-            f32x4 v0 = *(const f32x4 *)(xr + c), v1 = *(const f32x4 *)(xr + c + 4);
-            u32x4 gv = *(const u32x4 *)(g + c), o;
-            o[0] = pack_bf16x2(v0[0] * r * bf16_lo(gv[0]), v0[1] * r * bf16_hi(gv[0]));
-            o[1] = pack_bf16x2(v0[2] * r * bf16_lo(gv[1]), v0[3] * r * bf16_hi(gv[1]));
-            o[2] = pack_bf16x2(v1[0] * r * bf16_lo(gv[2]), v1[1] * r * bf16_hi(gv[2]));
-            o[3] = pack_bf16x2(v1[2] * r * bf16_lo(gv[3]), v1[3] * r * bf16_hi(gv[3]));
-            *(u32x4 *)(yr + c) = o;
-        }
-    } else {
-        for (int c = lane; c < d; c += 64) yr[c] = xr[c] * r * g[c];
+    for (int c = lane; c < d; c += 64) Elem<T>::store(yr, c, Elem<Tin>::load(xr, c) * r * Elem<T>::load(g, c));
+}
+
+template <typename Tin>
+static bool rmsnorm_vec_launch(dim3 grid, const Tin *x, int64_t ldx, const bf16_t *g, bf16_t *y, int64_t ldy,
+                               int rows, int d, float eps, hipStream_t s) {
+    constexpr int EPC = 16 / sizeof(Tin);
+    if (d % (64 * EPC) || ldx % EPC || ldy % 8) return false;
+    switch (d / (64 * EPC)) {
+        case 1: hipLaunchKernelGGL((rmsnorm_vec_kernel<Tin, 1>), grid, dim3(256), 0, s, x, ldx, g, y, ldy, rows, eps); return true;
+        case 2: hipLaunchKernelGGL((rmsnorm_vec_kernel<Tin, 2>), grid, dim3(256), 0, s, x, ldx, g, y, ldy, rows, eps); return true;
+        case 4: hipLaunchKernelGGL((rmsnorm_vec_kernel<Tin, 4>), grid, dim3(256), 0, s, x, ldx, g, y, ldy, rows, eps); return true;
+        case 8: hipLaunchKernelGGL((rmsnorm_vec_kernel<Tin, 8>), grid, dim3(256), 0, s, x, ldx, g, y, ldy, rows, eps); return true;
+        case 16: hipLaunchKernelGGL((rmsnorm_vec_kernel<Tin, 16>), grid, dim3(256), 0, s, x, ldx, g, y, ldy, rows, eps); return true;
+        default: return false;
     }
 }
 
 hipError_t rmsnorm_launch(int dtype, const void *x, int64_t ldx, const void *g, void *y, int64_t ldy, int rows, int d,
                           float eps, hipStream_t s, bool x_f32) {
     dim3 grid((rows + 3) / 4);
-    if (dtype == TFB_BF16 && !x_f32)
-        hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, (const bf16_t *)x, ldx,
-                           (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps);
-    else if (dtype == TFB_BF16)
-        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t>), grid, dim3(256), 0, s, (const float *)x, ldx,
-                           (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps);
-    else
+    if (dtype == TFB_BF16 && !x_f32) {
+        if (!rmsnorm_vec_launch<bf16_t>(grid, (const bf16_t *)x, ldx, (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps, s))
+            hipLaunchKernelGGL((rmsnorm_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, (const bf16_t *)x, ldx,
+                               (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps);
+    } else if (dtype == TFB_BF16) {
+        if (!rmsnorm_vec_launch<float>(grid, (const float *)x, ldx, (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps, s))
+            hipLaunchKernelGGL((rmsnorm_kernel<float, bf16_t>), grid, dim3(256), 0, s, (const float *)x, ldx,
+                               (const bf16_t *)g, (bf16_t *)y, ldy, rows, d, eps);
+    } else {
         hipLaunchKernelGGL((rmsnorm_kernel<float, float>), grid, dim3(256), 0, s, (const float *)x, ldx,
                            (const float *)g, (float *)y, ldy, rows, d, eps);
+    }
     return hipGetLastError();
 }
 
