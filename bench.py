@@ -3,12 +3,16 @@
 Headline (`value`): block prefill TFLOP/s on the Llama-2-7B-shaped block
 (d=4096, H=Hkv=32, dh=128, f=11008, B=1, T=2048, bf16 storage, fp32
 accumulation, KV cache written), algorithmic causal FLOP count.  In the same
-run: the GQA decode step (d=4096, H=32, Hkv=8, f=14336, B=64 sequences with
-cache lengths uniform in [1024, 4096]) in tokens/s, with the decode-attention
-kernel's achieved HBM bandwidth.  Inputs are synthetic and seeded, resident
-in HBM before timing starts.
+run:
+  - the GQA decode step (d=4096, H=32, Hkv=8, f=14336, B=64 sequences with
+    cache lengths uniform in [1024, 4096]) in tokens/s, with the
+    decode-attention kernel's achieved HBM bandwidth;
+  - the GQA long-context block prefill (B=2, T=8192) in TFLOP/s;
+  - the 32-layer model (B=4, prompt T=1024, V=32000): prefill TFLOP/s and
+    128 greedy decode steps in tokens/s.
+Inputs are synthetic and seeded, resident in HBM before timing starts.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long] [--no-model]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
                                              scaling the HBM byte counters)
 """
@@ -34,6 +38,26 @@ PEAK_HBM_GBPS = 8000.0      # HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gateup_gemm_7b_prefill_pmc.md")
 GEMM_SOURCES = [os.path.join(ROOT, "transformer_decoder_block_rmsnorm_amd", "csrc", n)
                 for n in ("gemm.hip", "epilogue.h", "common.h")]
+
+
+# Algorithmic counts (2 FLOPs per multiply-add: tirogla "Transformer block",
+# How it works; kirito-excalibur "The Transformer", 4. FLOP counting).
+def block_matrix_params(d, H, Hkv, f):
+    """Wq, Wk, Wv, Wo and the three SwiGLU matrices of one block."""
+    dh = d // H
+    return d * H * dh + 2 * d * Hkv * dh + H * dh * d + 3 * d * f
+
+
+def prefill_flops(B, T, d, H, Hkv, f):
+    """Weight products for every token plus causal attention: q.k and p.v over
+    the T(T+1)/2 visible (query, key) pairs of each head."""
+    dh = d // H
+    return 2 * B * T * block_matrix_params(d, H, Hkv, f) + 4 * dh * H * B * T * (T + 1) // 2
+
+
+def decode_attention_bytes(lens, Hkv, dh):
+    """bf16 K and V rows 0..len_b (the new row included) of every sequence."""
+    return sum((int(n) + 1) * Hkv * dh * 2 * 2 for n in lens)
 
 
 def gemm_source_digest() -> str:
@@ -67,7 +91,7 @@ def _dev_tensor(f32, bits):
 
 
 def block_inputs(cfg, B, T):
-    from tests.inputs import activations, block_weights
+    from synth.inputs import activations, block_weights
     w32, bits = block_weights(cfg)
     w = {k: _dev_tensor(v, None if bits is None else bits[k]) for k, v in w32.items()}
     x32, xb = activations(cfg, B, T)
@@ -77,7 +101,6 @@ def block_inputs(cfg, B, T):
 def time_prefill(cfg, steps, warmup):
     import torch
     import transformer_decoder_block_rmsnorm_amd as tfb
-    from oracle import formulas as FM
     tc = tfb.Config.of(cfg)
     B, T = cfg.B, cfg.T
     w32, w, x32, x = block_inputs(cfg, B, T)
@@ -120,7 +143,7 @@ def time_prefill(cfg, steps, warmup):
     tfb.profile_enable(False)
     ms_all_events = e0.elapsed_time(e1) / steps
     stages = tfb.profile_read()
-    flops = FM.block_prefill_flops_causal(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    flops = prefill_flops(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
     return dict(ms=ms, ms_all_events=ms_all_events, flops=flops, stages=stages, dominant=dominant, w32=w32,
                 x32=x32)
 
@@ -130,7 +153,6 @@ def time_decode(cfg, steps, warmup):
     import torch
     import synth
     import transformer_decoder_block_rmsnorm_amd as tfb
-    from oracle import formulas as FM
     from synth.configs import tensor_id
     tc = tfb.Config.of(cfg)
     B, dh = cfg.B, cfg.d // cfg.n_heads
@@ -180,20 +202,140 @@ def time_decode(cfg, steps, warmup):
     torch.cuda.synchronize()
     tfb.profile_enable(False)
     stages = tfb.profile_read()
-    attn_bytes = FM.decode_attention_bytes(lens, cfg.n_kv_heads, dh) + 2 * B * cfg.d * 2
-    wbytes = 2 * FM.block_matrix_params(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    attn_bytes = decode_attention_bytes(lens, cfg.n_kv_heads, dh) + 2 * B * cfg.d * 2
+    wbytes = 2 * block_matrix_params(cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
     return dict(ms=ms, stages=stages, dominant=dominant, attn_bytes=attn_bytes, weight_bytes=wbytes, lens=lens)
+
+
+def time_long_prefill(cfg, steps, warmup):
+    """The GQA long-context block prefill: whole-step time, then one pass with
+    every stage bracketed by events for the breakdown."""
+    import torch
+    import transformer_decoder_block_rmsnorm_amd as tfb
+    tc = tfb.Config.of(cfg)
+    B, T = cfg.B, cfg.T
+    _, w, _, x = block_inputs(cfg, B, T)
+    rope = tfb.rope_table_init(tc, cfg.t_max)
+    kc = torch.zeros((B, cfg.n_kv_heads, cfg.t_max, tc.head_dim), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    out = torch.empty_like(x)
+    ws = tfb.workspace(tc, B, T)
+
+    def step():
+        tfb.block_prefill(tc, w, rope, x, out, cache=(kc, vc), ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tfb.profile_read()
+    tfb.profile_stages(None)
+    tfb.profile_enable(True)
+    step()
+    torch.cuda.synchronize()
+    tfb.profile_enable(False)
+    stages = {k: round(v[0] / v[1], 4) for k, v in tfb.profile_read().items()}
+    flops = prefill_flops(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    attn = 4 * (cfg.d // cfg.n_heads) * cfg.n_heads * B * T * (T + 1) // 2
+    return {"workload": "GQA long-context block prefill: d=4096 H=32 Hkv=8 dh=128 f=14336 B=2 T=8192, "
+                        "KV cache written",
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
+                                                                                PEAK_BF16_TFLOPS, 4),
+            "ms_per_step": round(ms, 4), "steps": steps, "flops_per_step": flops, "stage_ms": stages,
+            "attention_tflops": round(attn / (stages["attention"] * 1e-3) / 1e12, 2)}
+
+
+def time_model(cfg, decode_steps, reps):
+    """The 32-layer model: prefill of the prompts (logits of the last rows,
+    greedy next token), then decode_steps greedy steps with the growing cache.
+    Weights are drawn N(0, 0.02) on the GPU (torch generator, seeded); the
+    gains are 1."""
+    import torch
+    import transformer_decoder_block_rmsnorm_amd as tfb
+    from synth.inputs import weight_shapes
+    tc = tfb.Config.of(cfg)
+    B, T, L, V, d = cfg.B, cfg.T, cfg.n_layers, cfg.vocab, cfg.d
+    dh = d // cfg.n_heads
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+
+    def randn(shape):
+        return (torch.randn(shape, generator=g, device="cuda") * cfg.w_sigma).to(torch.bfloat16)
+
+    layers = []
+    for _ in range(L):
+        layers.append({n: (torch.ones(s, dtype=torch.bfloat16, device="cuda") if n.startswith("g_") else randn(s))
+                       for n, s in weight_shapes(d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff).items()})
+    embed, w_un = randn((V, d)), randn((d, V))
+    g_final = torch.ones(d, dtype=torch.bfloat16, device="cuda")
+    h = tfb.ModelHandle(tc, layers, embed, g_final, w_un)
+    caches = [(torch.zeros((B, cfg.n_kv_heads, cfg.t_max, dh), dtype=torch.bfloat16, device="cuda"),
+               torch.zeros((B, cfg.n_kv_heads, cfg.t_max, dh), dtype=torch.bfloat16, device="cuda"))
+              for _ in range(L)]
+    rope = tfb.rope_table_init(tc, cfg.t_max)
+    ids = torch.randint(0, V, (B, T), generator=g, device="cuda", dtype=torch.int32)
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nxt = torch.empty((B, 1), dtype=torch.int32, device="cuda")
+    ws_pre = tfb.workspace(tc, B, T, V)
+    ws_dec = tfb.workspace(tc, B, 1, V)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def prefill():
+        lens.zero_()
+        tfb.model_forward(h, rope, ids, caches, lens, 0, last_only=True, next_ids=nxt.view(B), ws=ws_pre)
+
+    def decode():
+        for s in range(decode_steps):
+            tfb.model_forward(h, rope, nxt, caches, lens, T + s, last_only=True, next_ids=nxt.view(B), ws=ws_dec)
+
+    prefill()
+    decode()
+    torch.cuda.synchronize()
+    pre_ms, dec_ms = [], []
+    for _ in range(reps):
+        flush.fill_(1)
+        torch.cuda.synchronize()
+        e0.record()
+        prefill()
+        e1.record()
+        torch.cuda.synchronize()
+        pre_ms.append(e0.elapsed_time(e1))
+        e0.record()
+        decode()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms.append(e0.elapsed_time(e1))
+    pre, dec = min(pre_ms), min(dec_ms)
+    flops = L * prefill_flops(B, T, d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff) + 2 * B * d * V
+    wbytes = 2 * (L * block_matrix_params(d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff) + d * V)
+    kv = sum(L * decode_attention_bytes([T + s] * B, cfg.n_kv_heads, dh) for s in range(decode_steps))
+    step_ms = dec / decode_steps
+    return {"workload": "32-layer GQA model: d=4096 H=32 Hkv=8 f=14336 V=32000 untied, B=4, prompt T=1024 "
+                        "token ids uniform in [0, V), then %d greedy decode steps" % decode_steps,
+            "prefill_ms": round(pre, 3), "prefill_tflops": round(flops / (pre * 1e-3) / 1e12, 2),
+            "prefill_mfma_frac": round(flops / (pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "decode_ms_per_step": round(step_ms, 4), "decode_tok_per_s": round(B / (step_ms * 1e-3), 1),
+            "decode_hbm_frac": round((wbytes + kv / decode_steps) / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "decode_bytes_per_step": int(wbytes + kv / decode_steps), "reps": reps,
+            "note": "minimum over reps; the caches are flushed before each prefill; each decode step is one "
+                    "tfb_model_forward call over all 32 layers"}
 
 
 def cpu_baseline(cfg, w32, x32, rows):
     """The CPU oracle on a bounded prefix of the same block prefill."""
     import oracle as O
-    from oracle import formulas as FM
     orc = O.Oracle()
     t0 = time.time()
     orc.block_forward(cfg, w32, x32[:, :rows])
     dt = time.time() - t0
-    flops = FM.block_prefill_flops_causal(cfg.B, rows, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+    flops = prefill_flops(cfg.B, rows, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": orc.threads(), "kind": "oracle",
             "sample": "first %d of %d tokens of the same block prefill (B=%d, full widths), %.1f s wall"
                       % (rows, cfg.T, cfg.B, dt)}
@@ -206,6 +348,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-model", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -215,7 +359,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from synth.configs import C2, C4
+    from synth.configs import C2, C3, C4, C5
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.backends.cuda.matmul.allow_tf32 = False
     if args.copy_calibration:
@@ -274,6 +418,10 @@ def main():
                                    PEAK_HBM_GBPS, 4),
             "stage_ms": {k: round(v[0] / v[1], 4) for k, v in dec["stages"].items()},
         }
+    if not args.no_long:
+        result["long_prefill"] = time_long_prefill(C3, max(2, args.steps // 6), max(1, args.warmup // 10))
+    if not args.no_model:
+        result["model"] = time_model(C5, C5.decode_steps, 3)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(C2, pre["w32"], pre["x32"], args.cpu_rows)
     print(json.dumps(result), flush=True)
