@@ -293,6 +293,45 @@ def test_decode_long_cache_chunks(oracle, lens, d, H, Hkv):
     assert rel_err(got, ref) <= 2e-2
 
 
+@pytest.mark.parametrize("B,d,H,Hkv,f", [
+    (20, 512, 4, 2, 1024),     # 17-32 rows per weight stream: two 16-row tiles
+    (40, 512, 8, 2, 1536),     # 33-48 rows: three 16-row tiles, dh = 64
+    (64, 1024, 8, 8, 2048),    # the full 64 rows, 128-column weight blocks split along k
+])
+def test_decode_batch_sizes(oracle, B, d, H, Hkv, f):
+    """Decode of B sequences at spread positions: the weight-streaming GEMMs
+    take B rows (every row-tile count of the kernel) against the oracle."""
+    torch = _torch()
+    import synth
+    from tests.gpu_util import to_dev
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=f, dtype="bf16", base=500000.0, number=93)
+    tc = tfb.Config.of(cfg)
+    dh = d // H
+    lens = [int(v) for v in synth.integers(cfg.seed, 13, (B,), 1, 200)]
+    t_max = max(lens) + 4
+    shape = (B, Hkv, t_max, dh)
+    kf, kb = synth.normal(cfg.seed, 11, shape, 1.0, True)
+    vf, vb = synth.normal(cfg.seed, 12, shape, 1.0, True)
+    kc, vc = to_dev(kf, kb), to_dev(vf, vb)
+    w32, w = dev_weights(cfg)
+    x32, x = dev_x(cfg, B, 1)
+    rope = tfb.rope_table_init(tc, t_max)
+    pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = torch.empty_like(x)
+    print("case: decode batch", B, d, H, Hkv, f, flush=True)
+    tfb.block_decode(tc, w, rope, x, o, (kc, vc), pos, max(lens))
+    torch.cuda.synchronize()
+    okc, ovc = kf.copy(), vf.copy()
+    ref = oracle.block_forward(cfg, w32, x32, start=np.array(lens, np.int32), kc=okc, vc=ovc)
+    got = to_np(o)
+    assert np.isfinite(got).all()
+    assert rel_err(got, ref) <= tol(cfg)
+    gk, gv = widen_cache(kc), widen_cache(vc)
+    for b in range(B):
+        assert cache_ok(cfg, gk[b, :, lens[b]], okc[b, :, lens[b]])
+        assert cache_ok(cfg, gv[b, :, lens[b]], ovc[b, :, lens[b]])
+
+
 @pytest.mark.parametrize("dtype,chunks", [("f32", [5, 7, 4]), ("bf16", [100, 37, 129, 1]), ("bf16", [64, 64, 64])])
 def test_chunked_prefill_matches_full_prefill(oracle, dtype, chunks):
     """Prefill in chunks at start positions 0, c0, c0+c1, ... into one cache
