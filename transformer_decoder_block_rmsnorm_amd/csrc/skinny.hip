@@ -55,19 +55,22 @@ __device__ __forceinline__ int skinny_gswz(int row) {
     else return row & 3;
 }
 
-template <int BN, int MT>
+template <int BN, int SK, int MT>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
-    constexpr int SK = 64;                     // k rows per stage
+    // SK: k rows per stage
     constexpr int WST = SK * BN;               // weight elements per stage
     constexpr int XST = 64 * SK;               // x elements per stage (64 rows)
     constexpr int STAGE = WST + XST;
-    constexpr int NST = (BN >= 128) ? 6 : 8;   // ring stages (144 / 128 KB)
+    constexpr int NST = (144 * 1024) / (STAGE * 2) < 16 ? (144 * 1024) / (STAGE * 2) : 16;  // ring stages
     constexpr int WBLK = WST * 2 / 1024, XBLK = XST * 2 / 1024;  // 1 KB blocks
     constexpr int PW = WBLK / 4, PX = XBLK / 4, PER = PW + PX;   // DMAs per wave per stage
     constexpr int WRPB = 1024 / (BN * 2);      // weight rows per 1 KB block
     constexpr int CPR = BN / 8;                // 16-byte chunks per weight row
     constexpr int NC = BN / 64;                // 16-column tiles per wave
-    static_assert(PW * 4 == WBLK && PX * 4 == XBLK, "stage splits into 1 KB blocks per wave");
+    constexpr int XCH = SK / 8;                // 16-byte chunks per x row
+    constexpr int XRPL = 8 / XCH;              // x rows per 128 bytes
+    static_assert(PW * 4 == WBLK && PX * 4 == XBLK && WRPB >= 1, "stage splits into 1 KB blocks per wave");
+    static_assert(NST >= 3 && (SK == 32 || SK == 64), "ring depth and x row layout");
     __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;
 
@@ -94,8 +97,9 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     const bf16_t *xsrc[PX];
 #pragma unroll
     for (int i = 0; i < PX; ++i) {
-        const int row = (wave * PX + i) * 8 + lane / 8, p = lane % 8;  // x rows of 128 bytes
-        xsrc[i] = a.x + (int64_t)min(row, a.M - 1) * a.ldx + st_lo * SK + 8 * (p ^ (row & 7));
+        // x rows of 2 SK bytes; chunk XOR (row / XRPL) keeps the 16-lane fragment reads conflict free
+        const int row = (wave * PX + i) * (64 / XCH) + lane / XCH, p = lane % XCH;
+        xsrc[i] = a.x + (int64_t)min(row, a.M - 1) * a.ldx + st_lo * SK + 8 * (p ^ ((row / XRPL) & (XCH - 1)));
     }
     auto issue = [&](int st, int slot) {
         const uint32_t wb = __builtin_amdgcn_readfirstlane(lds_base + slot * STAGE * 2 + wave * PW * 1024);
@@ -106,18 +110,19 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
         for (int i = 0; i < PX; ++i) dma16_stream(xsrc[i] + st * SK, xb + i * 1024);
     };
     auto wait_stages = [&](int n) {  // at most n later stages of this wave still in flight
+        static_assert((NST - 2) * PER < 64, "vmcnt range");
+#define TFB_WAIT_CASE(k) \
+    case k:                                   \
+        wait_vmcnt<(k <= NST - 2 ? k : 0) * PER>(); \
+        break;
         switch (n) {
-            case 0: wait_vmcnt<0>(); break;
-            case 1: wait_vmcnt<PER>(); break;
-            case 2: wait_vmcnt<2 * PER>(); break;
-            case 3: wait_vmcnt<3 * PER>(); break;
-            case 4: wait_vmcnt<4 * PER>(); break;
-            case 5: wait_vmcnt<5 * PER>(); break;
-            case 6: wait_vmcnt<6 * PER>(); break;
-            default: wait_vmcnt<7 * PER>(); break;
+            TFB_WAIT_CASE(1) TFB_WAIT_CASE(2) TFB_WAIT_CASE(3) TFB_WAIT_CASE(4) TFB_WAIT_CASE(5)
+            TFB_WAIT_CASE(6) TFB_WAIT_CASE(7) TFB_WAIT_CASE(8) TFB_WAIT_CASE(9) TFB_WAIT_CASE(10)
+            TFB_WAIT_CASE(11) TFB_WAIT_CASE(12) TFB_WAIT_CASE(13) TFB_WAIT_CASE(14)
+            default: wait_vmcnt<0>(); break;
         }
+#undef TFB_WAIT_CASE
     };
-
     f32x4 acc[MT][NC];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int row = 16 * mt + ln, ch = 4 * ks + g4;
-                af[mt] = as_bf16x8(*(const u32x4 *)(Xs + row * SK + 8 * (ch ^ (row & 7))));
+                af[mt] = as_bf16x8(*(const u32x4 *)(Xs + row * SK + 8 * (ch ^ ((row / XRPL) & (XCH - 1)))));
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -220,14 +225,14 @@ size_t skinny_part_bytes(int M, int K, int N) {
     return (size_t)splits * M * N * sizeof(float);
 }
 
-template <int BN>
+template <int BN, int SK>
 static void skinny_launch_bn(const SkinnyArgs &a, int blocks, hipStream_t s) {
     const int mt = (a.M + 15) / 16;
     switch (mt) {
-        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 1>), dim3(blocks), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 2>), dim3(blocks), dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 3>), dim3(blocks), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, 4>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 1>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 2>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 3>), dim3(blocks), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 4>), dim3(blocks), dim3(256), 0, s, a); break;
     }
 }
 
@@ -252,8 +257,8 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     if ((size_t)a.splits * a.M * a.N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
     a.part = (float *)part;
     const int blocks = (a.N / bn) * a.splits;
-    if (bn == 128) skinny_launch_bn<128>(a, blocks, s);
-    else skinny_launch_bn<64>(a, blocks, s);
+    if (bn == 128) skinny_launch_bn<128, 64>(a, blocks, s);
+    else skinny_launch_bn<64, 64>(a, blocks, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)a.M * (n_out / 2);
