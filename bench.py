@@ -328,6 +328,42 @@ def time_model(cfg, decode_steps, reps):
                     "tfb_model_forward call over all 32 layers"}
 
 
+def time_tiny(cfg, reps):
+    """The tiny fp32 block: prefill of T rows then single-token decode steps
+    (launch-latency bound; microseconds only)."""
+    import torch
+    import transformer_decoder_block_rmsnorm_amd as tfb
+    tc = tfb.Config.of(cfg)
+    B, T, steps = cfg.B, cfg.T, cfg.decode_steps
+    _, w, _, x = block_inputs(cfg, B, T + steps)
+    rope = tfb.rope_table_init(tc, cfg.t_max)
+    kc = torch.zeros((B, cfg.n_kv_heads, cfg.t_max, tc.head_dim), dtype=torch.float32, device="cuda")
+    vc = torch.zeros_like(kc)
+    xp = x[:, :T].contiguous()
+    xd = [x[:, T + s:T + s + 1].contiguous() for s in range(steps)]
+    out_p, out_d = torch.empty_like(xp), torch.empty_like(xd[0])
+    pos = [torch.full((B,), T + s, dtype=torch.int32, device="cuda") for s in range(steps)]
+    ws = tfb.workspace(tc, B, T)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    pre, dec = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0.record()
+        tfb.block_prefill(tc, w, rope, xp, out_p, cache=(kc, vc), ws=ws)
+        e1.record()
+        for s in range(steps):
+            tfb.block_decode(tc, w, rope, xd[s], out_d, (kc, vc), pos[s], T + s, ws=ws)
+        e2.record()
+        torch.cuda.synchronize()
+        pre.append(e0.elapsed_time(e1) * 1e3)
+        dec.append(e1.elapsed_time(e2) * 1e3 / steps)
+    pre.sort()
+    dec.sort()
+    return {"workload": "tiny fp32 block: d=64 H=4 Hkv=2 f=192, prefill T=16 then 4 decode steps",
+            "prefill_us": round(pre[len(pre) // 2], 1), "decode_us_per_step": round(dec[len(dec) // 2], 1),
+            "reps": reps, "note": "median; launch-latency bound, no roofline claim"}
+
+
 def cpu_baseline(cfg, w32, x32, rows):
     """The CPU oracle on a bounded prefix of the same block prefill."""
     import oracle as O
@@ -349,6 +385,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the GQA decode step (for counter runs); prints the decode fields alone")
     ap.add_argument("--no-model", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -359,7 +397,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from synth.configs import C2, C3, C4, C5
+    from synth.configs import C1, C2, C3, C4, C5
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.backends.cuda.matmul.allow_tf32 = False
     if args.copy_calibration:
@@ -373,6 +411,12 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
         return
 
+    if args.decode_only:
+        dec = time_decode(C4, args.steps, args.warmup)
+        print(json.dumps({"decode_only": True, "tok_per_s": round(C4.B / (dec["ms"] * 1e-3), 1),
+                          "ms_per_step": round(dec["ms"], 4), "attention_bytes": dec["attn_bytes"],
+                          "weight_bytes": dec["weight_bytes"]}), flush=True)
+        return
     pre = time_prefill(C2, args.steps, args.warmup)
     tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
     gms, gcalls = pre["dominant"]["gateup_gemm"]
@@ -422,6 +466,7 @@ def main():
         result["long_prefill"] = time_long_prefill(C3, max(2, args.steps // 6), max(1, args.warmup // 10))
     if not args.no_model:
         result["model"] = time_model(C5, C5.decode_steps, 3)
+        result["tiny"] = time_tiny(C1, 21)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(C2, pre["w32"], pre["x32"], args.cpu_rows)
     print(json.dumps(result), flush=True)
