@@ -451,8 +451,12 @@ template <int DH, int G>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     // Per wave, 64 keys at a time on MFMA 16x16x32 (lane l: column l%16,
     // k group g = l/16):
-    //   S^T[keys, heads] = K . Q^T   K rows from global, 16 rows x 64
-    //                                 contiguous bytes per load;
+    //   S^T[keys, heads] = K . Q^T   K loaded as whole rows (each load
+    //                                 instruction covers 1 KB of consecutive
+    //                                 rows, the fastest streaming pattern),
+    //                                 written to a wave-private LDS slot
+    //                                 (16-byte chunks swizzled by row) and
+    //                                 read back as MFMA fragments;
     //   O[heads, e]     += P . V     V loaded 8 rows x 16 bytes per lane
     //                                 (whole rows per instruction) and
     //                                 transposed 8x8 in registers; output
@@ -463,6 +467,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     constexpr int NCH = DH / 8;        // 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) float red_o[4][G][DH];
     __shared__ float red_ml[4][G][2];
+    __shared__ __attribute__((aligned(16))) bf16_t kst[4][64 * DH];  // per wave: 64 K rows
+    constexpr int RPI = 64 / NCH;  // K rows per whole-row load instruction
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, g4 = lane >> 4;
@@ -494,14 +500,12 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     for (int c = 0; c < 8; ++c) oacc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int base = k_begin + wave * 64; base < k_end; base += 256) {
-        u32x4 kr[4][NS], vr[2][8];
+        u32x4 kw[NCH], vr[2][8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int j = base + 16 * t + ln;
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-                kr[t][s] = (j < k_end) ? ld_stream(a.kc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + (4 * s + g4) * 8)
-                                       : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < NCH; ++i) {
+            const int r = RPI * i + lane / NCH, j = base + r;
+            kw[i] = (j < k_end) ? ld_stream(a.kc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + (lane % NCH) * 8)
+                                : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -512,13 +516,30 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
                 vr[u][r] = (v_lane && j < k_end) ? ld_stream(a.vc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + ln * 8)
                                                  : u32x4{0, 0, 0, 0};
             }
+        bf16_t *ks = kst[wave];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int r = RPI * i + lane / NCH, c = lane % NCH;
+            *(u32x4 *)(ks + r * DH + ((c ^ (r & (NCH - 1))) * 8)) = kw[i];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         f32x4 sacc[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             sacc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int r = 16 * t + ln;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) sacc[t] = mfma16(as_bf16x8(kr[t][s]), qf[s], sacc[t]);
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 kf = *(const u32x4 *)(ks + r * DH + (((4 * s + g4) ^ (r & (NCH - 1))) * 8));
+                sacc[t] = mfma16(as_bf16x8(kf), qf[s], sacc[t]);
+            }
         }
+        // the slot is rewritten by the next iteration: its reads come first
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // online softmax for head ln over keys 16t + 4g + v
         float mx = -INFINITY;
 #pragma unroll
