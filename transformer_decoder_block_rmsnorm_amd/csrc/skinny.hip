@@ -16,7 +16,10 @@
 // (chunks swizzled by row), and the products run on MFMA 16x16x32.  Each
 // workgroup writes an fp32 partial [split][M][N]; a second kernel adds the
 // splits in a fixed order and applies the fused epilogue (RoPE + KV append,
-// residual, SwiGLU, fp32 store), so the result is deterministic.
+// residual, SwiGLU, fp32 store), so the result is deterministic.  The
+// gate-up GEMM in a single k range skips that pass: W1 and W3 are
+// interleaved in 16-column groups, so each wave holds the gate and the up
+// value of the same outputs and writes SiLU(gate) * up itself.
 #include <algorithm>
 
 #include "epilogue.h"
@@ -31,16 +34,24 @@ struct SkinnyArgs {
     int splits;       // k ranges per column block
     const bf16_t *w[3];
     int w_cols[3];
-    int src;          // 0: one matrix, 1: concat (wq|wk|wv), 2: two matrices side by side (w1|w3)
+    int src;          // 0: one matrix, 1: concat (wq|wk|wv), 2: w1 and w3 interleaved in 16-column groups
     float *part;      // [splits][M][N]
+    bf16_t *act;      // src 2 with one k range: SiLU(gate) * up written here directly, row stride ld_act
+    int64_t ld_act;
 };
 
 // Column c of the virtual B -> (matrix, column).  Concat: matrices side by
-// side; dual: w1 columns then w3 columns.  Every matrix width is a multiple of
-// 64, so an 8-column chunk never straddles two matrices.
+// side.  Dual: w1 and w3 interleaved in 16-column groups (virtual columns
+// 32 g .. 32 g + 15 are w1 columns 16 g .., the next 16 the same w3 columns),
+// so one wave's two 16-column tiles hold the gate and the up value of the same
+// outputs.  Every matrix width is a multiple of 64, so an 8-column chunk never
+// straddles two matrices or groups.
 __device__ __forceinline__ const bf16_t *b_column(const SkinnyArgs &a, int c, int &ld) {
     int s = 0;
-    if (a.src != 0) {
+    if (a.src == 2) {
+        s = (c >> 4) & 1;
+        c = 16 * (c >> 5) + (c & 15);
+    } else if (a.src != 0) {
         while (s < 2 && a.w[s + 1] && c >= a.w_cols[s]) { c -= a.w_cols[s]; ++s; }
     }
     ld = a.w_cols[s];
@@ -162,6 +173,22 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
                 for (int t = 0; t < NC; ++t) acc[mt][t] = mfma16(af[mt], bf[t], acc[mt][t]);
         }
     }
+    if (a.act) {
+        // gate-up with one k range: tile 0 holds the gate and tile 1 the up
+        // value of output column 16 * (group) + ln, rows 16 mt + 4 g4 + v
+        static_assert(NC == 2 || BN != 128, "gate/up tile pair per wave");
+        if constexpr (NC == 2) {
+            const int lc = (c0 + wave * (BN / 4)) / 2 + ln;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 16 * mt + 4 * g4 + v;
+                    if (m < a.M) a.act[(int64_t)m * a.ld_act + lc] = f32_to_bf16(silu_f(acc[mt][0][v]) * acc[mt][1][v]);
+                }
+        }
+        return;
+    }
     // partial: rows 16 mt + 4 g4 + v, column c0 + wave * BN/4 + 16 t + ln
     float *dst = a.part + (int64_t)sp * a.M * a.N;
 #pragma unroll
@@ -186,12 +213,12 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float *part, i
     const int m = (int)(idx / pairs), c = 2 * (int)(idx % pairs);
     const int64_t stride = (int64_t)M * N;
     if constexpr (EPI == EPI_SWIGLU) {
-        // gate columns [0, n_out), up columns [n_out, 2 n_out)
+        // output column c: gate at virtual column 32 (c / 16) + c % 16, up 16 later
         float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
-        const float *p = part + (int64_t)m * N + c;
+        const float *p = part + (int64_t)m * N + 32 * (c >> 4) + (c & 15);
         for (int s = 0; s < slices; ++s) {
             const float2 gv = *(const float2 *)(p + s * stride);
-            const float2 uv = *(const float2 *)(p + s * stride + n_out);
+            const float2 uv = *(const float2 *)(p + s * stride + 16);
             g0 += gv.x; g1 += gv.y; u0 += uv.x; u1 += uv.y;
         }
         epi_store_swiglu<bf16_t>(ep, m, c, g0, u0);
@@ -256,11 +283,17 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     skinny_plan(a.K, a.N, bn, a.splits);
     if ((size_t)a.splits * a.M * a.N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
     a.part = (float *)part;
+    // gate-up in one k range: the kernel applies SiLU(gate) * up itself
+    const bool direct = c.epi == EPI_SWIGLU && a.splits == 1 && bn == 128;
+    if (direct) {
+        a.act = (bf16_t *)c.ep.out;
+        a.ld_act = c.ep.ldo;
+    }
     const int blocks = (a.N / bn) * a.splits;
     if (bn == 128) skinny_launch_bn<128, 64>(a, blocks, s);
     else skinny_launch_bn<64, 64>(a, blocks, s);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || direct) return e;
     const int64_t threads = (int64_t)a.M * (n_out / 2);
     dim3 rg((unsigned)((threads + 255) / 256));
     switch (c.epi) {
