@@ -156,18 +156,30 @@ hipError_t staged(int stage, hipStream_t s, F &&launch) {
 //   RMSNorm_1 -> fused QKV GEMM (+RoPE, q to workspace, k and v to the cache)
 //   -> causal GQA attention -> Wo GEMM + residual -> RMSNorm_2
 //   -> fused gate-up GEMM (+SiLU * up) -> W2 GEMM + residual.
+// The RMSNorms that follow a residual GEMM run inside its reduce pass: on the
+// skinny path (bf16, at most kSkinnyMaxM rows, with its partial buffer) and
+// for widths the fused kernel holds in registers.
+bool norms_fuse(const tfb_block_config &c, int M, const WsLayout &L) {
+    return c.dtype == TFB_BF16 && M <= kSkinnyMaxM && L.skinny_bytes > 0 && c.d <= kSkinnyNormMaxN && c.d % 8 == 0;
+}
+
 tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
                      int max_pos, const void *x,
                      void *out, int B, int T, int start, const int32_t *pos, void *kc, void *vc, int t_max,
                      uint8_t *ws, const WsLayout &L, hipStream_t s, const int32_t *starts = nullptr,
-                     const int32_t *lens = nullptr, const KvMap *paged = nullptr) {
+                     const int32_t *lens = nullptr, const KvMap *paged = nullptr, bool h_ready = false,
+                     const void *next_g = nullptr) {
+    // h_ready: h in the workspace already holds RMSNorm1(x) (written by the
+    // previous layer's W2 step).  next_g: on the skinny path, the W2 step also
+    // writes RMSNorm(out) with this gain into h for whoever reads h next.
     // cache rows: contiguous [B, Hkv, t_max, dh], or a paged pool and block table
     const KvMap kvm = paged ? *paged : KvMap{nullptr, t_max, 0, 0, 0};
     const int M = B * T, d = c.d, H = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, f = c.d_ff;
     const int qd = H * dh, kvd = Hkv * dh;
     void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
 
-    TRY_HIP(STAGE(ST_RMSNORM_ATTN, rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s)));
+    if (!h_ready) TRY_HIP(STAGE(ST_RMSNORM_ATTN, rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s)));
+    const bool fuse = norms_fuse(c, M, L);
 
     GemmCall g{};
     g.dtype = c.dtype;
@@ -222,9 +234,14 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     o.scratch_bytes = g.scratch_bytes;
     o.split_scratch = g.split_scratch;
     o.split_bytes = g.split_bytes;
+    if (fuse) {  // RMSNorm2 of the stored residual rows, in the Wo reduce
+        o.norm_g = w.g_mlp;
+        o.norm_out = h;
+        o.norm_eps = c.rms_eps;
+    }
     TRY_HIP(STAGE(ST_WO, gemm_launch(o, s)));
 
-    TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
+    if (!fuse) TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
 
     GemmCall gu{};
     gu.dtype = c.dtype;
@@ -248,6 +265,11 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     dn.scratch_bytes = g.scratch_bytes;
     dn.split_scratch = g.split_scratch;
     dn.split_bytes = g.split_bytes;
+    if (fuse && next_g) {
+        dn.norm_g = next_g;
+        dn.norm_out = h;
+        dn.norm_eps = c.rms_eps;
+    }
     TRY_HIP(STAGE(ST_W2, gemm_launch(dn, s)));
     return TFB_OK;
 }
@@ -494,13 +516,21 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     // Embed ([PID] Tiny example, forward), then the L blocks.
     TRY_HIP(STAGE(ST_EMBED, embed_launch(c.dtype, ids, model->embed, wsb + L.x0, M, d, V, s)));
     void *cur = wsb + L.x0, *nxt = wsb + L.x1;
+    // On the skinny path each layer's W2 step also writes the next layer's
+    // normed input, and the last one the final norm when the head reads
+    // every row.
+    const bool fuse = norms_fuse(c, M, L);
+    const bool final_fused = fuse && (logits || next_ids) && !(last_only && T > 1);
     for (int l = 0; l < model->n_layers; ++l) {
+        const bool last = l + 1 == model->n_layers;
+        const void *next_g = !fuse ? nullptr : (last ? (final_fused ? model->g_final : nullptr) : model->layers[l + 1].g_attn);
+        const bool h_ready = fuse && l > 0;
         if (T > 1)
             st = run_block(c, model->layers[l], rope_table, t_max_table, 0, cur, nxt, B, T, 0, nullptr, caches[l].k, caches[l].v,
-                           caches[l].t_max, wsb, L, s);
+                           caches[l].t_max, wsb, L, s, nullptr, nullptr, nullptr, h_ready, next_g);
         else
             st = run_block(c, model->layers[l], rope_table, t_max_table, h_max_len, cur, nxt, B, 1, 0, lens, caches[l].k, caches[l].v,
-                           caches[l].t_max, wsb, L, s);
+                           caches[l].t_max, wsb, L, s, nullptr, nullptr, nullptr, h_ready, next_g);
         if (st != TFB_OK) return st;
         void *tmp = cur; cur = nxt; nxt = tmp;
     }
@@ -514,7 +544,8 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     }
     if (logits || next_ids) {
         void *hn = wsb + L.h;
-        TRY_HIP(STAGE(ST_FINAL_NORM, rmsnorm_launch(c.dtype, fin, d, model->g_final, hn, d, rows, d, c.rms_eps, s)));
+        if (!final_fused)
+            TRY_HIP(STAGE(ST_FINAL_NORM, rmsnorm_launch(c.dtype, fin, d, model->g_final, hn, d, rows, d, c.rms_eps, s)));
         float *lg = logits;
         if (!lg) {
             if (rows != B) {  // next ids only: the head runs on the last rows

@@ -21,7 +21,14 @@ struct GemmCall {
     size_t scratch_bytes;
     void *split_scratch;   // large-M split-K tail partials (gemm_split_bytes), may be NULL
     size_t split_bytes;
+    // EPI_RESID on the skinny path only (see kSkinnyNormMaxN): after storing
+    // each output row, RMSNorm the stored row with gain norm_g and write the
+    // bf16 result to norm_out [M, N] (the next GEMM's normed input)
+    const void *norm_g;
+    void *norm_out;
+    float norm_eps;
 };
+constexpr int kSkinnyNormMaxN = 8192;
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s);
 // Scratch the large-M bf16 GEMM uses for its split-K tail (0: none); with
 // less, it runs without splitting.  N_virtual: B columns (gate-up: 2 f).

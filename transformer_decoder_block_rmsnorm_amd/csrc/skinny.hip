@@ -235,6 +235,70 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float *part, i
     }
 }
 
+// Reduce + residual + RMSNorm of one row per workgroup (EPI_RESID with a
+// norm): out = res + sum of the k-range partials in order (stored in out's
+// storage type), then the stored row is normalised, as the separate norm
+// kernel would read it back, and written to norm_out in bf16
+// ([TIR] Code, rms_norm: y = x / sqrt(mean(x^2) + eps) * g).
+template <int IT>
+__global__ __launch_bounds__(256) void skinny_reduce_norm_kernel(const float *part, int slices, int M, int N,
+                                                                 EpiParams ep, const bf16_t *g, bf16_t *hn, float eps) {
+    const int m = blockIdx.x, tid = threadIdx.x;
+    if (m >= M) return;
+    const int64_t stride = (int64_t)M * N;
+    float v[IT][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int c = (it * 256 + tid) * 8;
+        if (c >= N) continue;
+        const float *p = part + (int64_t)m * N + c;
+        f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+        for (int s = 1; s < slices; ++s) {
+            a += *(const f32x4 *)(p + s * stride);
+            b += *(const f32x4 *)(p + s * stride + 4);
+        }
+        float r[8];
+        if (ep.res_f32) {
+            const float *rr = (const float *)ep.res + (int64_t)m * ep.ldr + c;
+            const f32x4 x0 = *(const f32x4 *)rr, x1 = *(const f32x4 *)(rr + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { r[k] = x0[k]; r[k + 4] = x1[k]; }
+        } else {
+            load_bf16x8((const bf16_t *)ep.res + (int64_t)m * ep.ldr + c, r);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { v[it][k] = r[k] + a[k]; v[it][k + 4] = r[k + 4] + b[k]; }
+        if (ep.out_f32) {
+            float *o = (float *)ep.out + (int64_t)m * ep.ldo + c;
+            *(f32x4 *)o = f32x4{v[it][0], v[it][1], v[it][2], v[it][3]};
+            *(f32x4 *)(o + 4) = f32x4{v[it][4], v[it][5], v[it][6], v[it][7]};
+        } else {
+            store_bf16x8((bf16_t *)ep.out + (int64_t)m * ep.ldo + c, v[it]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[it][k] = bf16_to_f32(f32_to_bf16(v[it][k]));  // the stored value
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += v[it][k] * v[it][k];
+    }
+    __shared__ float red[4];
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    ss = red[0] + red[1] + red[2] + red[3];
+    const float rs = 1.0f / sqrtf(ss / (float)N + eps);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int c = (it * 256 + tid) * 8;
+        if (c >= N) continue;
+        float gv[8], o[8];
+        load_bf16x8(g + c, gv);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = v[it][k] * rs * gv[k];
+        store_bf16x8(hn + (int64_t)m * N + c, o);
+    }
+}
+
 // Column block width and k splits of a skinny GEMM: 128-column blocks when N
 // allows (each workgroup also streams its x slice, 64/BN of its weight bytes),
 // then k is split so that the workgroups come close to one per compute unit
@@ -294,6 +358,21 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     else skinny_launch_bn<64, 64>(a, blocks, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
+    if (c.norm_g) {
+        // the caller skips its own norm launch, so a norm that cannot be fused is an error
+        if (c.epi != EPI_RESID || n_out > kSkinnyNormMaxN || n_out % 8 || !c.norm_out) return hipErrorInvalidValue;
+        const dim3 ng(a.M);
+        if (n_out <= 2048)
+            hipLaunchKernelGGL(skinny_reduce_norm_kernel<1>, ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N, c.ep,
+                               (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
+        else if (n_out <= 4096)
+            hipLaunchKernelGGL(skinny_reduce_norm_kernel<2>, ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N, c.ep,
+                               (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
+        else
+            hipLaunchKernelGGL(skinny_reduce_norm_kernel<4>, ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N, c.ep,
+                               (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
+        return hipGetLastError();
+    }
     const int64_t threads = (int64_t)a.M * (n_out / 2);
     dim3 rg((unsigned)((threads + 255) / 256));
     switch (c.epi) {
