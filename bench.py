@@ -385,6 +385,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--model-reps", type=int, default=3)
     ap.add_argument("--decode-only", action="store_true",
                     help="only the GQA decode step (for counter runs); prints the decode fields alone")
     ap.add_argument("--no-model", action="store_true")
@@ -465,7 +466,7 @@ def main():
     if not args.no_long:
         result["long_prefill"] = time_long_prefill(C3, max(2, args.steps // 6), max(1, args.warmup // 10))
     if not args.no_model:
-        result["model"] = time_model(C5, C5.decode_steps, 3)
+        result["model"] = time_model(C5, C5.decode_steps, max(1, args.model_reps))
         result["tiny"] = time_tiny(C1, 21)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(C2, pre["w32"], pre["x32"], args.cpu_rows)
