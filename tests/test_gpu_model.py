@@ -120,3 +120,64 @@ def test_model_last_only_and_next_ids_only(oracle):
         margin = (top2[:, 1] - top2[:, 0]) / np.sqrt(np.mean(ref ** 2))
         agree = nxt.cpu().numpy() == ref_next
         assert np.all(agree | (margin < 0.05))
+
+
+def test_decode_step_replays_from_a_hip_graph():
+    """One decode step of the model recorded into a HIP graph and replayed:
+    the library allocates nothing and never synchronises inside the call, and
+    the position of each sequence lives in the device-side lens, so each
+    replay is the next decode step.  Every replay (with eager work and a
+    synchronisation between replays) must give the eager step's logits and
+    greedy token bit for bit.  The eager steps use the same host bound; at
+    this size it yields the same launches as the per-step bound that the
+    oracle-checked decode test uses."""
+    import torch
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=97)
+    L, V, B, T, steps = 2, 1024, 3, 37, 4
+    print("case: graph replay of a decode step", L, V, B, T, steps, flush=True)
+    _, (ld, ed, gd, ud) = model_inputs(cfg, L, V)
+    tc = tfb.Config.of(cfg)
+    h = tfb.ModelHandle(tc, ld, ed, gd, ud)
+    t_max = T + steps + 3
+    bound = t_max - 2  # a host bound of max(lens) valid for every step
+    dh = cfg.d // cfg.n_heads
+    caches = [(torch.zeros((B, cfg.n_kv_heads, t_max, dh), dtype=torch.bfloat16, device="cuda"),
+               torch.zeros((B, cfg.n_kv_heads, t_max, dh), dtype=torch.bfloat16, device="cuda")) for _ in range(L)]
+    rope = tfb.rope_table_init(tc, t_max)
+    ids = torch.from_numpy(synth.integers(cfg.seed, tensor_id("ids"), (B, T), 0, V - 1)).cuda()
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    lg = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
+    ws_pre = tfb.workspace(tc, B, T, V)
+    ws_dec = tfb.workspace(tc, B, 1, V)
+
+    def prefill():
+        lens.zero_()
+        tfb.model_forward(h, rope, ids, caches, lens, 0, last_only=True, next_ids=nxt, ws=ws_pre)
+
+    def step():
+        tfb.model_forward(h, rope, nxt.view(B, 1), caches, lens, bound, logits=lg, last_only=True, next_ids=nxt,
+                          ws=ws_dec)
+
+    prefill()
+    ref = []
+    for _ in range(steps):
+        step()
+        ref.append((lg.clone(), nxt.clone()))
+    torch.cuda.synchronize()
+
+    prefill()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    prefill()  # capture ran nothing; start again from the prompt all the same
+    torch.cuda.synchronize()
+    for s in range(steps):
+        graph.replay()
+        got_l, got_i = lg.clone(), nxt.clone()
+        _ = (got_l * 2.0).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got_l, ref[s][0]), s
+        assert torch.equal(got_i, ref[s][1]), s
+        assert lens.cpu().numpy().tolist() == [T + s + 1] * B
