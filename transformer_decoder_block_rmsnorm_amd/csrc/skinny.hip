@@ -202,6 +202,11 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
         }
 }
 
+// The reduce passes load every K-slice of their columns before adding them
+// (in slice order, so the sums are the same): with the slice count known
+// only at run time, a plain loop would wait for each slice's load in turn.
+constexpr int kSkinnyMaxSplits = 16;
+
 // Sum the K-slices in order and apply the epilogue.  One thread per pair of
 // logical output columns.
 template <int EPI>
@@ -214,23 +219,35 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float *part, i
     const int64_t stride = (int64_t)M * N;
     if constexpr (EPI == EPI_SWIGLU) {
         // output column c: gate at virtual column 32 (c / 16) + c % 16, up 16 later
-        float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
         const float *p = part + (int64_t)m * N + 32 * (c >> 4) + (c & 15);
-        for (int s = 0; s < slices; ++s) {
-            const float2 gv = *(const float2 *)(p + s * stride);
-            const float2 uv = *(const float2 *)(p + s * stride + 16);
-            g0 += gv.x; g1 += gv.y; u0 += uv.x; u1 += uv.y;
-        }
+        float2 gv[kSkinnyMaxSplits], uv[kSkinnyMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kSkinnyMaxSplits; ++s)
+            if (s < slices) {
+                gv[s] = *(const float2 *)(p + s * stride);
+                uv[s] = *(const float2 *)(p + s * stride + 16);
+            }
+        float g0 = 0.0f, g1 = 0.0f, u0 = 0.0f, u1 = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kSkinnyMaxSplits; ++s)
+            if (s < slices) {
+                g0 += gv[s].x; g1 += gv[s].y; u0 += uv[s].x; u1 += uv[s].y;
+            }
         epi_store_swiglu<bf16_t>(ep, m, c, g0, u0);
         epi_store_swiglu<bf16_t>(ep, m, c + 1, g1, u1);
     } else {
-        float v0 = 0.0f, v1 = 0.0f;
         const float *p = part + (int64_t)m * N + c;
-        for (int s = 0; s < slices; ++s) {
-            const float2 v = *(const float2 *)(p + s * stride);
-            v0 += v.x;
-            v1 += v.y;
-        }
+        float2 pv[kSkinnyMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kSkinnyMaxSplits; ++s)
+            if (s < slices) pv[s] = *(const float2 *)(p + s * stride);
+        float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kSkinnyMaxSplits; ++s)
+            if (s < slices) {
+                v0 += pv[s].x;
+                v1 += pv[s].y;
+            }
         epi_store_pair<EPI, bf16_t>(ep, m, c, v0, v1);
     }
 }
@@ -253,11 +270,20 @@ __global__ __launch_bounds__(256) void skinny_reduce_norm_kernel(const float *pa
         const int c = (it * 256 + tid) * 8;
         if (c >= N) continue;
         const float *p = part + (int64_t)m * N + c;
-        f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-        for (int s = 1; s < slices; ++s) {
-            a += *(const f32x4 *)(p + s * stride);
-            b += *(const f32x4 *)(p + s * stride + 4);
-        }
+        f32x4 pa[kSkinnyMaxSplits], pb[kSkinnyMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kSkinnyMaxSplits; ++s)
+            if (s < slices) {
+                pa[s] = *(const f32x4 *)(p + s * stride);
+                pb[s] = *(const f32x4 *)(p + s * stride + 4);
+            }
+        f32x4 a = pa[0], b = pb[0];
+#pragma unroll
+        for (int s = 1; s < kSkinnyMaxSplits; ++s)
+            if (s < slices) {
+                a += pa[s];
+                b += pb[s];
+            }
         float r[8];
         if (ep.res_f32) {
             const float *rr = (const float *)ep.res + (int64_t)m * ep.ldr + c;
@@ -307,7 +333,7 @@ static void skinny_plan(int K, int N, int &bn, int &splits) {
     bn = N % 128 == 0 ? 128 : 64;
     const int n_cb = N / bn;
     splits = std::max(1, std::min(256 / n_cb, K / 64));
-    splits = std::min(splits, 16);
+    splits = std::min(splits, kSkinnyMaxSplits);
 }
 
 size_t skinny_part_bytes(int M, int K, int N) {
@@ -345,6 +371,7 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
         if (a.w[i] && a.w_cols[i] % 64) return hipErrorInvalidValue;
     int bn;
     skinny_plan(a.K, a.N, bn, a.splits);
+    if (a.splits > kSkinnyMaxSplits) return hipErrorInvalidValue;  // the reduce passes hold at most this many
     if ((size_t)a.splits * a.M * a.N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
     a.part = (float *)part;
     // gate-up in one k range: the kernel applies SiLU(gate) * up itself
