@@ -257,9 +257,9 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float *part, i
 // storage type), then the stored row is normalised, as the separate norm
 // kernel would read it back, and written to norm_out in bf16
 // ([TIR] Code, rms_norm: y = x / sqrt(mean(x^2) + eps) * g).
-template <int IT>
-__global__ __launch_bounds__(256) void skinny_reduce_norm_kernel(const float *part, int slices, int M, int N,
-                                                                 EpiParams ep, const bf16_t *g, bf16_t *hn, float eps) {
+template <int IT, int NT>
+__global__ __launch_bounds__(NT) void skinny_reduce_norm_kernel(const float *part, int slices, int M, int N,
+                                                                EpiParams ep, const bf16_t *g, bf16_t *hn, float eps) {
     const int m = blockIdx.x, tid = threadIdx.x;
     if (m >= M) return;
     const int64_t stride = (int64_t)M * N;
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_norm_kernel(const float *pa
     float ss = 0.0f;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int c = (it * 256 + tid) * 8;
+        const int c = (it * NT + tid) * 8;
         if (c >= N) continue;
         const float *p = part + (int64_t)m * N + c;
         f32x4 pa[kSkinnyMaxSplits], pb[kSkinnyMaxSplits];
@@ -307,15 +307,17 @@ __global__ __launch_bounds__(256) void skinny_reduce_norm_kernel(const float *pa
 #pragma unroll
         for (int k = 0; k < 8; ++k) ss += v[it][k] * v[it][k];
     }
-    __shared__ float red[4];
+    __shared__ float red[NT / 64];
     ss = wave_sum(ss);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    ss = red[0] + red[1] + red[2] + red[3];
+    ss = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) ss += red[w];
     const float rs = 1.0f / sqrtf(ss / (float)N + eps);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int c = (it * 256 + tid) * 8;
+        const int c = (it * NT + tid) * 8;
         if (c >= N) continue;
         float gv[8], o[8];
         load_bf16x8(g + c, gv);
@@ -388,16 +390,18 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     if (c.norm_g) {
         // the caller skips its own norm launch, so a norm that cannot be fused is an error
         if (c.epi != EPI_RESID || n_out > kSkinnyNormMaxN || n_out % 8 || !c.norm_out) return hipErrorInvalidValue;
+        // one workgroup per row (a decode batch has few rows): 8 columns per
+        // thread, so that each thread's slice loads go out in one round
         const dim3 ng(a.M);
         if (n_out <= 2048)
-            hipLaunchKernelGGL(skinny_reduce_norm_kernel<1>, ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N, c.ep,
-                               (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
+            hipLaunchKernelGGL((skinny_reduce_norm_kernel<1, 256>), ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N,
+                               c.ep, (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
         else if (n_out <= 4096)
-            hipLaunchKernelGGL(skinny_reduce_norm_kernel<2>, ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N, c.ep,
-                               (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
+            hipLaunchKernelGGL((skinny_reduce_norm_kernel<1, 512>), ng, dim3(512), 0, s, a.part, a.splits, a.M, a.N,
+                               c.ep, (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
         else
-            hipLaunchKernelGGL(skinny_reduce_norm_kernel<4>, ng, dim3(256), 0, s, a.part, a.splits, a.M, a.N, c.ep,
-                               (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
+            hipLaunchKernelGGL((skinny_reduce_norm_kernel<2, 512>), ng, dim3(512), 0, s, a.part, a.splits, a.M, a.N,
+                               c.ep, (const bf16_t *)c.norm_g, (bf16_t *)c.norm_out, c.norm_eps);
         return hipGetLastError();
     }
     const int64_t threads = (int64_t)a.M * (n_out / 2);
