@@ -15,6 +15,14 @@
 
 namespace tfb {
 
+// Compute units of the current device (256 on MI355X if the query fails).
+static int device_cus() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return cus;
+}
+
 // One wave per (b, h, t): lanes take 64 keys at a time, online softmax over
 // the chunks, each lane accumulates dh/64 output dimensions.  Serves the fp32
 // storage path and decode.
@@ -398,10 +406,7 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     const int blocks = a.n_qblocks * c.B * c.Hkv * a.n_hsub;
     // the whole grid resident at once (two single-group workgroups per CU):
     // split each workgroup's key range over two wave groups
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const bool two = blocks <= 2 * cus;
+    const bool two = blocks <= 2 * device_cus();
     const bool paged = a.kvm.table != nullptr;
     const dim3 g(blocks), b1(256), b2(512);
     if (c.dh == 128) {
@@ -682,12 +687,18 @@ static bool split_decode_args(const AttnCall &c, DecArgs &a) {
     a.pos = c.pos;
     a.part = (float *)c.partials;
     a.B = c.B; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max;
-    // chunk size: kDecChunk keys, grown in steps of kDecChunk when the longest
-    // sequence would need more chunks than the partial buffer holds
+    // chunk size: kDecChunk keys; half of that when (sequence, KV head)
+    // pairs are few, so that a small batch still spreads over the CUs; grown
+    // in steps of kDecChunk when the longest sequence would need more chunks
+    // than the partial buffer holds
     const int max_keys = c.window > 0 ? std::min(c.max_keys, c.window) : c.max_keys;
     a.window = c.window;
     int chunks = (max_keys + kDecChunk - 1) / kDecChunk;
     int chunk_keys = kDecChunk;
+    if ((int64_t)c.B * c.Hkv * chunks < 2 * (int64_t)device_cus()) {
+        chunk_keys = kDecChunk / 2;
+        chunks = (max_keys + chunk_keys - 1) / chunk_keys;
+    }
     if (chunks > c.max_splits) {
         chunk_keys = kDecChunk * ((chunks + c.max_splits - 1) / c.max_splits);
         chunks = (max_keys + chunk_keys - 1) / chunk_keys;
