@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds + grp * (NSTG * 2 * TILE * 2);
     bf16_t *const ring = lds + grp * (NSTG * 2 * TILE);
 
-    const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x & 255, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 31, lh = lane >> 5;
     const int nbh = a.B * a.Hkv * a.n_hsub;
     const int qb = a.n_qblocks - 1 - (int)(blockIdx.x / nbh);  // longest key ranges first
@@ -276,18 +276,26 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
             // does; rows past start + T sit above every real query's diagonal.
             const bool need_mask = (j0 + BKV - 1 > start + t0) || (W > 0 && j0 < start + t0 + 31 - W + 1);
             const int key_lo = W > 0 ? qpos - W + 1 : 0;
+            // one wave-uniform branch around the masking selects (a test
+            // per element would put a branch in front of every score; the
+            // empty asm keeps the compiler from executing the selects on
+            // every tile instead of branching)
+            if (need_mask) {
+                asm volatile("");
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                        sacc[kt][v] = (key > qpos || key < key_lo) ? -INFINITY : sacc[kt][v];
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    if (need_mask) {
-                        const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                        if (key > qpos || key < key_lo) sacc[kt][v] = -INFINITY;
-                    }
-                    mx = fmaxf(mx, sacc[kt][v]);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * a.scale_log2e;
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
+            mx = max_halves(mx) * a.scale_log2e;  // lane l holds keys 4lh.. of its query, l ^ 32 the rest
             const bool grow = mx > m_run + 8.0f;
             if (__builtin_amdgcn_ballot_w64(grow)) {
                 const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
@@ -299,7 +307,7 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
                     for (int v = 0; v < 16; ++v) oacc[te][v] *= alpha;
             }
             const float msub = m_run == -INFINITY ? 0.0f : m_run;
-            float sum = 0.0f;
+            float sum = -0.0f;  // the additive identity: the first add folds away
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -308,8 +316,7 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
                     sacc[kt][v] = p;
                     sum += p;
                 }
-            sum += __shfl_xor(sum, 32, 64);
-            l_run += sum;
+            l_run += sum_halves(sum);
             // P^T fragment of 16-key slice s2: lane (query lr, half lh) holds
             // keys 16 s2 + {4lh .. 4lh+3, 8+4lh .. 8+4lh+3}
             bf16x8 pf[4];

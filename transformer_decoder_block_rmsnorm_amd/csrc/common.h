@@ -91,6 +91,28 @@ __device__ __forceinline__ float swap_lane_pair(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
 
+// The values of lanes l % 32 and l % 32 + 32, in that order on both halves
+// of the wave: v_permlane32_swap (gfx950) exchanges the halves of two
+// registers in one instruction, where a shuffle goes through LDS
+// (ds_bpermute, with a wait that also drains the wave's other LDS reads).
+__device__ __forceinline__ void halves_of(float x, float &lo, float &hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+// max / sum of a value over lanes l and l ^ 32 (same result on both lanes;
+// max of values that are never NaN)
+__device__ __forceinline__ float max_halves(float x) {
+    float lo, hi;
+    halves_of(x, lo, hi);
+    return lo > hi ? lo : hi;
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    float lo, hi;
+    halves_of(x, lo, hi);
+    return lo + hi;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
