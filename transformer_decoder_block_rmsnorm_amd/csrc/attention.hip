@@ -154,7 +154,8 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     static_assert(PER * 4 == BLK && RPB * DH * 2 == 1024, "tile splits into 1 KB blocks per wave");
     __shared__ __attribute__((aligned(1024))) bf16_t lds[NGRP * NSTG * 2 * TILE];  // a ring per wave group
     static_assert(NGRP == 1 || 2 * NSTG * 2 * TILE * 2 >= 4 * (NE * 16 + 2) * 64 * 4, "merge staging fits");
-    const int grp = NGRP == 2 ? (int)(threadIdx.x >> 8) : 0;  // wave group: lower / upper half of the key tiles
+    // wave group: lower / upper half of the key tiles
+    const int grp = NGRP == 2 ? (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 8) : 0;
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds + grp * (NSTG * 2 * TILE * 2);
     bf16_t *const ring = lds + grp * (NSTG * 2 * TILE);
 
@@ -216,17 +217,28 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
         doff[i] = isv ? 16 * ((pch >> 1) ^ v_granule_swz<DH>(key)) + 8 * (pch & 1)  // V: granules
                       : 8 * (pch ^ (key & (KCH - 1)));                              // K: chunks
     }
+    // a wave's blocks are all K or all V; byte offset of each lane's chunk
+    // from the tile's first cache row (contiguous cache)
+    static_assert((BLK / 2) % PER == 0, "a wave fills K blocks or V blocks only");
+    const bf16_t *const kv_src = wave * PER < BLK / 2 ? a.kc : a.vc;
+    uint32_t voff[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) voff[i] = (uint32_t)(dkey[i] * DH + doff[i]) * 2u;
     auto issue = [&](int it, int stg) {
         const int j0 = it * BKV;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + stg * (2 * TILE * 2) + wave * PER * 1024);
+        if (!PAGED && j0 >= key_floor && j0 + BKV <= kv_len) {
+            // every row of the tile is a valid row: scalar base + fixed lane offsets
+            const bf16_t *src = kv_src + (slab + j0) * DH;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) dma16_sbase(src, voff[i], base + i * 1024);
+            return;
+        }
         int64_t rows[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) rows[i] = row(min(max(j0 + dkey[i], key_floor), kv_len - 1));
-        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + stg * (2 * TILE * 2) + wave * PER * 1024);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const bf16_t *src = (wave * PER + i < BLK / 2 ? a.kc : a.vc) + rows[i] * DH + doff[i];
-            dma16(src, base + i * 1024);
-        }
+        for (int i = 0; i < PER; ++i) dma16(kv_src + rows[i] * DH + doff[i], base + i * 1024);
     };
 
     f32x16 oacc[NE];

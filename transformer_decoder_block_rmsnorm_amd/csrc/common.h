@@ -172,6 +172,19 @@ __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_byte_addr) 
                  : "memory", "m0");
 }
 
+// The same with the address split into a wave-uniform base (SGPR pair) and
+// a 32-bit per-lane byte offset: a loop that walks a fixed per-lane pattern
+// over consecutive tiles then moves only the scalar base.
+// (The base must be the same on every lane; it is read from the first one.)
+__device__ __forceinline__ void dma16_sbase(const void *sbase, uint32_t voff, uint32_t lds_byte_addr) {
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_byte_addr), "v"(voff),
+                 "s"((const void *)(uintptr_t)ub)
+                 : "memory", "m0");
+}
+
 // The same for data streamed once (weights in decode GEMMs): the nontemporal
 // policy keeps it from displacing reused lines in the caches; measured on
 // MI355X it roughly doubles the rate of a weight stream over the plain form.
