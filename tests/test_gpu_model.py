@@ -181,3 +181,43 @@ def test_decode_step_replays_from_a_hip_graph():
         assert torch.equal(got_l, ref[s][0]), s
         assert torch.equal(got_i, ref[s][1]), s
         assert lens.cpu().numpy().tolist() == [T + s + 1] * B
+
+
+@pytest.mark.parametrize("V,cols,expected", [
+    (9024, [6001, 37, 4100, 9023], 37),   # tied columns in different threads, waves and 4-column groups
+    (9024, [9023, 9020, 9022], 9020),     # a tie inside one 4-column group of one thread
+    (128, [127, 64, 65], 64),
+])
+def test_greedy_next_token_ties_take_lowest_index(V, cols, expected):
+    """Greedy decoding breaks ties toward the lowest index (the oracle pin of
+    the same rule builds the same model).  Zero Wo and W2 make the block the
+    identity on its input, an embedding of ones and unit gains then give the
+    final hidden row of ones, and W_U has identical dominant columns: those
+    logits are exactly d, every other one is 0."""
+    import torch
+    cfg = small_cfg(d=256, H=2, Hkv=1, f=512, dtype="bf16", number=98)
+    B, T = 2, 3
+    print("case: argmax ties", V, cols, flush=True)
+    _, w = dev_weights(cfg, layer=0, gains="ones")
+    w = dict(w, wo=torch.zeros_like(w["wo"]), w2=torch.zeros_like(w["w2"]))
+    emb = torch.ones((V, cfg.d), dtype=torch.bfloat16, device="cuda")
+    wu = torch.zeros((cfg.d, V), dtype=torch.bfloat16, device="cuda")
+    for c in cols:
+        wu[:, c] = 1.0
+    gf = torch.ones(cfg.d, dtype=torch.bfloat16, device="cuda")
+    tc = tfb.Config.of(cfg)
+    h = tfb.ModelHandle(tc, [w], emb, gf, wu)
+    dh = cfg.d // cfg.n_heads
+    caches = [(torch.zeros((B, cfg.n_kv_heads, T, dh), dtype=torch.bfloat16, device="cuda"),
+               torch.zeros((B, cfg.n_kv_heads, T, dh), dtype=torch.bfloat16, device="cuda"))]
+    rope = tfb.rope_table_init(tc, T)
+    ids = torch.randint(0, V, (B, T), dtype=torch.int32, device="cuda")
+    lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nxt = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    lg = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
+    tfb.model_forward(h, rope, ids, caches, lens, 0, logits=lg, last_only=True, next_ids=nxt)
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy()[:, 0]
+    assert np.all(got[:, cols] == float(cfg.d)), got[:, cols]
+    assert np.count_nonzero(got) == B * len(cols)
+    assert nxt.cpu().numpy().tolist() == [expected] * B

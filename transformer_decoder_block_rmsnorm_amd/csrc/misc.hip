@@ -212,35 +212,57 @@ hipError_t gather_last_launch(int dtype, const void *x, void *y, int B, int T, i
 }
 
 // Greedy next token: argmax of each row, lowest index among equal maxima.
-__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int64_t ld, int n, int32_t *out) {
+// One 1024-thread workgroup per row (a decode batch has few rows): 16-byte
+// loads, unrolled so that a thread's loads are in flight together; each
+// thread visits its elements in increasing index order and keeps the first
+// maximum, then the threads' (value, index) pairs are merged, preferring the
+// lower index on equal values.
+__device__ __forceinline__ void argmax_merge(float &bv, int &bi, float ov, int oi) {
+    if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+}
+__global__ __launch_bounds__(1024) void argmax_kernel(const float *logits, int64_t ld, int n, int32_t *out) {
     const float *row = logits + (int64_t)blockIdx.x * ld;
+    const int tid = threadIdx.x;
     float best = -INFINITY;
     int idx = 0x7FFFFFFF;
-    for (int j = threadIdx.x; j < n; j += 256) {
-        float v = row[j];
-        if (v > best || (v == best && j < idx)) { best = v; idx = j; }
-    }
-    __shared__ float sv[256];
-    __shared__ int si[256];
-    sv[threadIdx.x] = best;
-    si[threadIdx.x] = idx;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (threadIdx.x < w) {
-            float ov = sv[threadIdx.x + w];
-            int oi = si[threadIdx.x + w];
-            if (ov > sv[threadIdx.x] || (ov == sv[threadIdx.x] && oi < si[threadIdx.x])) {
-                sv[threadIdx.x] = ov;
-                si[threadIdx.x] = oi;
-            }
+    if ((ld % 4) == 0 && ((uintptr_t)logits % 16) == 0) {
+        const int n4 = n / 4;
+#pragma unroll 8
+        for (int i = tid; i < n4; i += 1024) {
+            const f32x4 v = *(const f32x4 *)(row + 4 * i);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (v[k] > best) { best = v[k]; idx = 4 * i + k; }
         }
-        __syncthreads();
+        for (int j = 4 * n4 + tid; j < n; j += 1024) {  // tail: indices above every vector element
+            const float v = row[j];
+            if (v > best) { best = v; idx = j; }
+        }
+    } else {
+        for (int j = tid; j < n; j += 1024) {
+            const float v = row[j];
+            if (v > best) { best = v; idx = j; }
+        }
     }
-    if (threadIdx.x == 0) out[blockIdx.x] = si[0] == 0x7FFFFFFF ? 0 : si[0];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        argmax_merge(best, idx, __shfl_xor(best, o, 64), __shfl_xor(idx, o, 64));
+    __shared__ float sv[16];
+    __shared__ int si[16];
+    if ((tid & 63) == 0) { sv[tid >> 6] = best; si[tid >> 6] = idx; }
+    __syncthreads();
+    if (tid < 64) {
+        best = tid < 16 ? sv[tid] : -INFINITY;
+        idx = tid < 16 ? si[tid] : 0x7FFFFFFF;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1)
+            argmax_merge(best, idx, __shfl_xor(best, o, 64), __shfl_xor(idx, o, 64));
+        if (tid == 0) out[blockIdx.x] = idx == 0x7FFFFFFF ? 0 : idx;
+    }
 }
 
 hipError_t argmax_launch(const float *logits, int64_t ld, int rows, int n, int32_t *out, hipStream_t s) {
-    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(256), 0, s, logits, ld, n, out);
+    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(1024), 0, s, logits, ld, n, out);
     return hipGetLastError();
 }
 
