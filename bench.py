@@ -399,7 +399,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

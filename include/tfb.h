@@ -55,7 +55,7 @@ typedef enum {
     TFB_ERR_WORKSPACE = -5,      /* workspace NULL or smaller than required */
     TFB_ERR_CACHE_OVERFLOW = -6, /* a position bound is not below the cache (or RoPE table) length */
     TFB_ERR_HIP = -7,            /* a kernel launch failed */
-    TFB_ERR_UNSUPPORTED = -8     /* valid request this build does not implement */
+    TFB_ERR_UNSUPPORTED = -8     /* valid request the library does not implement */
 } tfb_status;
 
 typedef enum { TFB_F32 = 0, TFB_BF16 = 1 } tfb_dtype;
