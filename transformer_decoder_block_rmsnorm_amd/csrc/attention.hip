@@ -227,9 +227,11 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     auto issue = [&](int it, int stg) {
         const int j0 = it * BKV;
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + stg * (2 * TILE * 2) + wave * PER * 1024);
-        if (!PAGED && j0 >= key_floor && j0 + BKV <= kv_len) {
-            // every row of the tile is a valid row: scalar base + fixed lane offsets
-            const bf16_t *src = kv_src + (slab + j0) * DH;
+        // every row of the tile is a valid row, and (paged cache) the tile
+        // lies in one pool block of at least BKV rows, whose rows for this KV
+        // head are consecutive: scalar base + fixed lane offsets
+        if ((!PAGED || (1 << a.kvm.bs_shift) >= BKV) && j0 >= key_floor && j0 + BKV <= kv_len) {
+            const bf16_t *src = kv_src + row(j0) * DH;
 #pragma unroll
             for (int i = 0; i < PER; ++i) dma16_sbase(src, voff[i], base + i * 1024);
             return;
