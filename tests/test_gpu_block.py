@@ -84,6 +84,22 @@ def test_bf16_block_prefill_then_decode(oracle, shape):
     check_against_oracle(oracle, cfg, shape["B"], shape["T0"], shape["steps"], shape["T0"] + shape["steps"] + 5)
 
 
+@pytest.mark.parametrize("d,H,Hkv,B,T0,W", [
+    (256, 4, 2, 80, 200, 0),    # dh 64, two heads per KV head: 4 x 80 x 2 = 640 blocks of 64 rows
+    (256, 4, 2, 80, 200, 70),   # the same with a window
+    (256, 2, 1, 160, 200, 0),   # dh 128: 4 x 160 = 640 blocks
+    (512, 8, 2, 40, 201, 0),    # four heads per KV head: blocks of 32 rows, 7 x 40 x 2 = 560
+])
+def test_large_grid_prefill_one_wave_group_per_workgroup(oracle, d, H, Hkv, B, T0, W):
+    """Grids larger than two workgroups per CU run the flash kernel with one
+    wave group per workgroup (the long-context form, whose full-size test
+    only checks sampled rows): every output row and cache row against the
+    oracle, at ragged lengths, then one decode step."""
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype="bf16", number=112, window=W)
+    print("case: large-grid prefill", d, H, Hkv, B, T0, W, flush=True)
+    check_against_oracle(oracle, cfg, B, T0, 1, T0 + 8)
+
+
 def test_bf16_random_gains_rope_base_500k(oracle):
     cfg = small_cfg(d=512, H=4, Hkv=1, f=1536, dtype="bf16", base=500000.0, number=83)
     print("case: bf16 random gains base 5e5", flush=True)
