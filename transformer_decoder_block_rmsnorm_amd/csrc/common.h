@@ -86,11 +86,6 @@ __device__ __forceinline__ void transpose8x8_bf16(const u32x4 in[8], u32x4 out[8
 __device__ __forceinline__ int swz_row(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz_tr(int k) { return (0x6530 >> (4 * (k & 3))) & 0xF; }  // 0, 3, 5, 6
 
-// Swap with the neighbouring lane (l ^ 1) through DPP quad_perm [1,0,3,2].
-__device__ __forceinline__ float swap_lane_pair(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-}
-
 // The values of lanes l % 32 and l % 32 + 32, in that order on both halves
 // of the wave: v_permlane32_swap (gfx950) exchanges the halves of two
 // registers in one instruction, where a shuffle goes through LDS
