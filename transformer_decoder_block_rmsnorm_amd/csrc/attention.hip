@@ -15,14 +15,6 @@
 
 namespace tfb {
 
-// Compute units of the current device (256 on MI355X if the query fails).
-static int device_cus() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    return cus;
-}
-
 // One wave per (b, h, t): lanes take 64 keys at a time, online softmax over
 // the chunks, each lane accumulates dh/64 output dimensions.  Serves the fp32
 // storage path and decode.

@@ -444,19 +444,6 @@ __global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiPa
     }
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cache[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
 // Split-K plan for the last, partial round of tiles: with `rem` tiles left
 // over after whole rounds on `cus` compute units, split each of them `splits`
 // ways so that rem * splits <= cus (at least 8 k steps per split, at most 4).

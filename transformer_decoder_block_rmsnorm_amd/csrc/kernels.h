@@ -29,6 +29,9 @@ struct GemmCall {
     float norm_eps;
 };
 constexpr int kSkinnyNormMaxN = 8192;
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
+int device_cus();
 hipError_t gemm_launch(const GemmCall &c, hipStream_t s);
 // Scratch the large-M bf16 GEMM uses for its split-K tail (0: none); with
 // less, it runs without splitting.  N_virtual: B columns (gate-up: 2 f).

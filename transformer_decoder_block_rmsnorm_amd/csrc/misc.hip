@@ -2,9 +2,22 @@
 // embedding gather, last-row gather, greedy argmax, position updates.
 // Page short names: [TIR] tirogla "Transformer block", [PID] pidoku "The
 // Transformer".
+#include <atomic>
+
 #include "kernels.h"
 
 namespace tfb {
+
+int device_cus() {
+    static std::atomic<int> cache[64];  // zero-initialised: not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 // RMSNorm ([TIR] Code, rms_norm; [PID] Tiny example, rmsnorm): one wave per
 // row, fp32 sum of squares reduced across the wave, y = x * r * g.

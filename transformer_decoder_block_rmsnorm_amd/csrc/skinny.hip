@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NT) void skinny_reduce_norm_kernel(const float *par
 static void skinny_plan(int K, int N, int &bn, int &splits) {
     bn = N % 128 == 0 ? 128 : 64;
     const int n_cb = N / bn;
-    splits = std::max(1, std::min(256 / n_cb, K / 64));
+    splits = std::max(1, std::min(device_cus() / n_cb, K / 64));
     splits = std::min(splits, kSkinnyMaxSplits);
 }
 
