@@ -313,10 +313,14 @@ def test_decode_long_cache_chunks(oracle, lens, d, H, Hkv):
     (20, 512, 4, 2, 1024),     # 17-32 rows per weight stream: two 16-row tiles
     (40, 512, 8, 2, 1536),     # 33-48 rows: three 16-row tiles, dh = 64
     (64, 1024, 8, 8, 2048),    # the full 64 rows, 128-column weight blocks split along k
+    (80, 512, 4, 2, 1024),     # more rows than a weight stream takes: the tiled GEMMs, one ragged 128-row tile
+    (130, 256, 2, 1, 512),     # two row tiles, the second holding 2 rows; dh = 128, MQA
 ])
 def test_decode_batch_sizes(oracle, B, d, H, Hkv, f):
-    """Decode of B sequences at spread positions: the weight-streaming GEMMs
-    take B rows (every row-tile count of the kernel) against the oracle."""
+    """Decode of B sequences at spread positions: up to 64 rows the
+    weight-streaming GEMMs take B rows (every row-tile count of the kernel),
+    beyond that the tiled GEMMs with a ragged last row tile; all against the
+    oracle."""
     torch = _torch()
     import synth
     from tests.gpu_util import to_dev
