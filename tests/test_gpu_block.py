@@ -72,6 +72,18 @@ def test_fp32_random_gains_and_batch(oracle):
     check_against_oracle(oracle, cfg, 3, 37, 3, 48, gains="random")
 
 
+@pytest.mark.parametrize("d,H,Hkv,f", [
+    (512, 2, 1, 256),   # dh = 256, the widest head the fp32 path takes
+    (96, 4, 2, 64),     # dh = 24: not a multiple of the 64 lanes
+])
+def test_fp32_head_widths(oracle, d, H, Hkv, f):
+    """fp32 storage runs the row-wise attention for any even head width up
+    to 256: prefill then decode steps against the oracle."""
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=f, number=84)
+    print("case: fp32 head width", d // H, flush=True)
+    check_against_oracle(oracle, cfg, 2, 70, 3, 80)
+
+
 @pytest.mark.parametrize("shape", [
     dict(d=512, H=4, Hkv=2, f=1024, B=2, T0=300, steps=2),   # GQA, ragged rows (300 = 2*128 + 44)
     dict(d=256, H=2, Hkv=2, f=768, B=1, T0=129, steps=2),    # MHA, one row past a tile
