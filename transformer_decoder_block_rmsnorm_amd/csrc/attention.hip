@@ -642,6 +642,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
 }
 
 // Merge the chunk partials of each (b, h): one wave per pair.
+// Chunk count up to which the merge loads every chunk's partial at once.
+constexpr int kCombineBatch = 16;
+
 template <int DH>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -652,16 +655,41 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
     const int n_range = a.window > 0 ? min(n_keys, a.window) : n_keys;
     const int n_ch = min((n_range + a.chunk_keys - 1) / a.chunk_keys, a.max_chunks);
     const float *base = a.part + (int64_t)bh * a.max_chunks * (DH + 4);
-    float M = -INFINITY;
-    for (int c = 0; c < n_ch; ++c) M = fmaxf(M, base[c * (DH + 4)]);
     constexpr int EPL = DH / 64;
-    float L = 0.0f, O[EPL] = {};
-    for (int c = 0; c < n_ch; ++c) {
-        const float *p = base + c * (DH + 4);
-        const float sc = __builtin_amdgcn_exp2f(p[0] - M);
-        L += sc * p[1];
+    float M = -INFINITY, L = 0.0f, O[EPL] = {};
+    if (n_ch <= kCombineBatch) {
+        // every chunk's (m, l, o) loaded at once, then combined in chunk
+        // order: a loop over a run-time count would wait for each load in turn
+        float pm[kCombineBatch], pl[kCombineBatch], po[kCombineBatch][EPL];
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) O[i] += sc * p[4 + lane * EPL + i];
+        for (int c = 0; c < kCombineBatch; ++c) {
+            const float *p = base + c * (DH + 4);
+            const bool in = c < n_ch;
+            pm[c] = in ? p[0] : -INFINITY;
+            pl[c] = in ? p[1] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) po[c][i] = in ? p[4 + lane * EPL + i] : 0.0f;
+        }
+#pragma unroll
+        for (int c = 0; c < kCombineBatch; ++c) M = fmaxf(M, pm[c]);
+#pragma unroll
+        for (int c = 0; c < kCombineBatch; ++c) {
+            if (c < n_ch) {
+                const float sc = __builtin_amdgcn_exp2f(pm[c] - M);
+                L += sc * pl[c];
+#pragma unroll
+                for (int i = 0; i < EPL; ++i) O[i] += sc * po[c][i];
+            }
+        }
+    } else {
+        for (int c = 0; c < n_ch; ++c) M = fmaxf(M, base[c * (DH + 4)]);
+        for (int c = 0; c < n_ch; ++c) {
+            const float *p = base + c * (DH + 4);
+            const float sc = __builtin_amdgcn_exp2f(p[0] - M);
+            L += sc * p[1];
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) O[i] += sc * p[4 + lane * EPL + i];
+        }
     }
     const float inv = 1.0f / L;
     bf16_t *out = a.o + (int64_t)bh * DH + lane * EPL;
