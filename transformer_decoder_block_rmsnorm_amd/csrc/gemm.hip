@@ -31,6 +31,9 @@ namespace tfb {
 //              logical output has N/2 columns.
 enum SrcKind { SRC_ONE = 0, SRC_CONCAT = 1, SRC_DUAL = 2 };
 
+// Most k ranges a tile of the split-K tail is divided into.
+constexpr int kMaxSplitK = 4;
+
 struct GemmArgs {
     const void *A;
     int64_t lda;
@@ -416,8 +419,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams ep)
 // epilogue.  One thread per 4 tile-local columns of a row.
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiParams ep) {
+    // SwiGLU: 4 gate columns (and their up columns) per thread; otherwise 8
+    // columns, stored through the 16-byte epilogue
+    constexpr int EPT = EPI == EPI_SWIGLU ? 4 : 8;
     const int pt = blockIdx.y;
-    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * EPT;
     if (e >= BM * BN) return;
     int tm, tn;
     tile_coords(g, g.full_tiles + pt, tm, tn);
@@ -425,13 +431,29 @@ __global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiPa
     if constexpr (EPI == EPI_SWIGLU) {
         if ((col & 63) >= 32) return;  // up columns are read by the gate's thread
     }
+    // every split's partial is loaded before any is added (at most
+    // kMaxSplitK; a loop over the run-time count would wait for each load in
+    // turn), then they are summed in split order
     const float *src = g.part + (int64_t)pt * g.splits * (BM * BN) + row * BN + col;
-    f32x4 v = *(const f32x4 *)src;
-    f32x4 u = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (EPI == EPI_SWIGLU) u = *(const f32x4 *)(src + 32);
-    for (int s = 1; s < g.splits; ++s) {
-        v += *(const f32x4 *)(src + (int64_t)s * (BM * BN));
-        if constexpr (EPI == EPI_SWIGLU) u += *(const f32x4 *)(src + (int64_t)s * (BM * BN) + 32);
+    const int o2 = EPI == EPI_SWIGLU ? 32 : 4;  // second vector: the up columns, or columns 4..7
+    f32x4 pa[kMaxSplitK], pb[kMaxSplitK];
+#pragma unroll
+    for (int s = 0; s < kMaxSplitK; ++s) {
+        if (s < g.splits) {
+            pa[s] = *(const f32x4 *)(src + (int64_t)s * (BM * BN));
+            pb[s] = *(const f32x4 *)(src + (int64_t)s * (BM * BN) + o2);
+        } else {
+            pa[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            pb[s] = pa[s];
+        }
+    }
+    f32x4 v = pa[0], u = pb[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplitK; ++s) {
+        if (s < g.splits) {
+            v += pa[s];
+            u += pb[s];
+        }
     }
     const int m = tm * BM + row;
     if constexpr (EPI == EPI_SWIGLU) {
@@ -439,8 +461,8 @@ __global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiPa
 #pragma unroll
         for (int k = 0; k < 4; ++k) epi_store_swiglu<bf16_t>(ep, m, lc + k, v[k], u[k]);
     } else {
-        epi_store_pair<EPI, bf16_t>(ep, m, tn * BN + col, v[0], v[1]);
-        epi_store_pair<EPI, bf16_t>(ep, m, tn * BN + col + 2, v[2], v[3]);
+        const float v8[8] = {v[0], v[1], v[2], v[3], u[0], u[1], u[2], u[3]};
+        epi_store8<EPI>(ep, m, tn * BN + col, v8);
     }
 }
 
@@ -455,7 +477,7 @@ static SplitPlan plan_split(int tiles, int k_steps, int cus, int tile_elems) {
     SplitPlan p{tiles, 1, 0};
     const int rem = tiles % cus;
     if (rem == 0) return p;
-    int s = std::min(std::min(cus / rem, k_steps / 8), 4);
+    int s = std::min(std::min(cus / rem, k_steps / 8), kMaxSplitK);
     if (s < 2) return p;
     p.full_tiles = tiles - rem;
     p.splits = s;
@@ -479,7 +501,7 @@ static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, void *part, size_t
                        g, ep);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sp.splits == 1) return e;
-    dim3 fg((BM * BN / 4 + 255) / 256, tiles - sp.full_tiles);
+    dim3 fg((BM * BN / (EPI == EPI_SWIGLU ? 4 : 8) + 255) / 256, tiles - sp.full_tiles);
     hipLaunchKernelGGL((gemm_split_fixup_kernel<BM, BN, EPI>), fg, dim3(256), 0, s, g, ep);
     return hipGetLastError();
 }
