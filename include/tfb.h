@@ -130,6 +130,21 @@ typedef struct {
  * only).  Returns 0 for an invalid config. */
 size_t tfb_workspace_bytes(const tfb_block_config *cfg, int32_t B, int32_t T, int32_t vocab);
 
+/* Where the block calls leave their intermediate tensors in the workspace,
+ * for inspection after a call returns (tests and tools; the contents stay
+ * valid until the next call that uses the workspace).  `which` selects one:
+ *   TFB_VIEW_Q   q after RoPE, [B, H, T, dh], storage type;
+ *   TFB_VIEW_ATT the concatenated head outputs, [B, T, H*dh], storage type;
+ *   TFB_VIEW_R   the first residual r = x + att Wo, [B, T, d], fp32;
+ *   TFB_VIEW_ACT the SwiGLU product SiLU(h2 W1) * (h2 W3), [B, T, f],
+ *                storage type
+ * (the names of the tirogla page, How it works steps 2-3).  Sizes as for
+ * tfb_workspace_bytes.  *offset receives the byte offset from the start of
+ * the workspace.  Returns TFB_ERR_SHAPE for an invalid config or `which`. */
+enum { TFB_VIEW_Q = 0, TFB_VIEW_ATT = 1, TFB_VIEW_R = 2, TFB_VIEW_ACT = 3 };
+tfb_status tfb_workspace_view(const tfb_block_config *cfg, int32_t B, int32_t T, int32_t vocab, int32_t which,
+                              size_t *offset);
+
 /* Fill the RoPE table: table[t][i] = (cos, sin) of t * base^(-2i/dh) for
  * t < t_max, i < dh/2, angle computed in fp64 and stored as fp32
  * ([t_max, dh/2, 2] fp32, device).  The tirogla page's Implementation notes
@@ -195,11 +210,15 @@ tfb_status tfb_block_decode_paged(const tfb_block_config *cfg, const tfb_block_w
                                   const tfb_paged_kv_cache *cache, const int32_t *pos, int32_t h_max_pos, void *ws,
                                   size_t ws_bytes, void *stream);
 
-/* Append n_new rows per sequence: k_new, v_new [B, n_new, Hkv, dh] (already
- * rotated) are written to cache rows start[b] .. start[b]+n_new-1.
- * start: [B] int32 device; h_max_start is a host upper bound of max(start)
- * with h_max_start + n_new <= t_max.  Rows outside that range are never
- * touched. */
+/* Append n_new rows per sequence to the cache: the tirogla page, How it
+ * works, KV cache paragraph (the keys, after RoPE, and the values of every
+ * past token are stored so that a decode step computes only the new token's).
+ * k_new, v_new: [B, n_new, Hkv, dh] device, storage type, already rotated;
+ * row t of sequence b, KV head g goes to cache row start[b] + t of that
+ * sequence and head.  start: [B] int32 device, read-only; h_max_start is a
+ * host upper bound of max(start) with h_max_start + n_new <= t_max (checked;
+ * device code also skips any row outside [0, t_max)).  Rows outside the
+ * written range are never touched.  Any even dh is accepted for fp32 storage. */
 tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const void *k_new, const void *v_new,
                          const int32_t *start, int32_t n_new, int32_t h_max_start, void *stream);
 

@@ -49,8 +49,11 @@ class Counters(ctypes.Structure):
                 ("cache_values", ctypes.c_int64)]
 
 
+INTER_NAMES = ("q", "att", "r", "act", "q_pre", "att_pre", "act_pre", "k_pre", "v_pre")
+
+
 class _Inter(ctypes.Structure):
-    _fields_ = [("q", ctypes.c_void_p), ("att", ctypes.c_void_p), ("r", ctypes.c_void_p), ("act", ctypes.c_void_p)]
+    _fields_ = [(n, ctypes.c_void_p) for n in INTER_NAMES]
 
 
 WEIGHT_NAMES = ("g_attn", "g_mlp", "wq", "wk", "wv", "wo", "w1", "w3", "w2")
@@ -84,7 +87,7 @@ def load(path: str | None = None):
     lib.o_model_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.c_int, ctypes.c_int, _VP, ctypes.POINTER(_W), _VP,
                                     _VP, _VP, _VP, ctypes.c_int, _VP, ctypes.c_int, ctypes.c_int, _VP,
                                     ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.c_int, _VP, ctypes.c_int, _VP,
-                                    _VP, ctypes.POINTER(Counters)]
+                                    _VP, _VP, _VP, ctypes.POINTER(Counters)]
     lib.o_model_forward.restype = ctypes.c_int
     lib.o_omp_threads.restype = ctypes.c_int
     if path is None:
@@ -189,10 +192,15 @@ class Oracle:
         inter = _Inter()
         got = {}
         if intermediates:
-            qd = cfg.n_heads * dh
-            got = {"q": np.empty((B, R, qd), np.float32), "att": np.empty((B, R, qd), np.float32),
-                   "r": np.empty((B, R, d), np.float32), "act": np.empty((B, R, cfg.d_ff), np.float32)}
-            inter = _Inter(*[self._p(got[k]) for k in ("q", "att", "r", "act")])
+            # q, att, act: the operands as handed on; *_pre: the same values
+            # before bf16 rounding; k_pre, v_pre: every row, [B, T, Hkv*dh]
+            qd, kvd = cfg.n_heads * dh, cfg.n_kv_heads * dh
+            shapes = {"q": (B, R, qd), "att": (B, R, qd), "r": (B, R, d), "act": (B, R, cfg.d_ff),
+                      "k_pre": (B, T, kvd), "v_pre": (B, T, kvd)}
+            for k in ("q", "att", "act"):
+                shapes[k + "_pre"] = shapes[k]
+            got = {k: np.empty(shapes[k], np.float32) for k in INTER_NAMES}
+            inter = _Inter(*[self._p(got[k]) for k in INTER_NAMES])
         cw, keep = self._weights(w)
         cnt = counters if counters is not None else Counters()
         rc = self.lib.o_block_forward(ctypes.byref(self._cfg(cfg)), ctypes.byref(cw), self._p(cos_tab),
@@ -216,8 +224,9 @@ class Oracle:
 
     # ---- model ---------------------------------------------------------
     def model_forward(self, cfg, n_layers, vocab, embed, layers: list, g_final, w_unembed, ids, kcs, vcs,
-                      start=None, rows=None, rope=None, counters: Counters | None = None):
-        """Returns (logits [B, R, V], next_ids [B])."""
+                      start=None, rows=None, rope=None, counters: Counters | None = None, kv_pre=False):
+        """Returns (logits [B, R, V], next_ids [B]); with kv_pre also the lists
+        of each layer's k and v before bf16 storage ([B, T, Hkv*dh] each)."""
         ids = np.ascontiguousarray(ids, np.int32)
         B, T = ids.shape
         t_max = kcs[0].shape[2]
@@ -240,10 +249,18 @@ class Oracle:
         nxt = np.empty(B, np.int32)
         st = None if start is None else np.ascontiguousarray(start, np.int32)
         cnt = counters if counters is not None else Counters()
+        kpre = vpre = None
+        kpp = vpp = None
+        if kv_pre:
+            kvd = cfg.n_kv_heads * dh
+            kpre = [np.empty((B, T, kvd), np.float32) for _ in range(n_layers)]
+            vpre = [np.empty((B, T, kvd), np.float32) for _ in range(n_layers)]
+            kpp = (_VP * n_layers)(*[self._p(a) for a in kpre])
+            vpp = (_VP * n_layers)(*[self._p(a) for a in vpre])
         rc = self.lib.o_model_forward(ctypes.byref(self._cfg(cfg)), n_layers, vocab, self._p(embed), lw,
                                       self._p(g_final), self._p(w_unembed), self._p(cos_tab), self._p(sin_tab),
                                       cos_tab.shape[0], self._p(ids), B, T, self._p(st), kp, vp, t_max,
-                                      self._p(rows_a), R, self._p(logits), self._p(nxt), ctypes.byref(cnt))
+                                      self._p(rows_a), R, self._p(logits), self._p(nxt), kpp, vpp, ctypes.byref(cnt))
         if rc != 0:
             raise ValueError("oracle model_forward failed with %d" % rc)
-        return logits, nxt
+        return (logits, nxt, kpre, vpre) if kv_pre else (logits, nxt)

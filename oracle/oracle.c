@@ -82,12 +82,17 @@ typedef struct {
     int64_t cache_values;  /* K and V values appended to the cache */
 } o_counters;
 
-/* Optional intermediates for the selected rows (each nullable). */
+/* Optional intermediates for the selected rows (each nullable).  q, att and
+ * act are the operands as handed on (bf16 values with gemm_bf16); the *_pre
+ * arrays hold the same values as computed in fp32, before that rounding (equal
+ * to the operands when gemm_bf16 is 0).  k_pre, v_pre cover every row. */
 typedef struct {
     float *q;    /* [B, R, H*dh] after RoPE */
     float *att;  /* [B, R, H*dh] concatenated head outputs */
     float *r;    /* [B, R, d] first residual */
     float *act;  /* [B, R, f] SiLU(gate) * up */
+    float *q_pre, *att_pre, *act_pre; /* as q, att, act */
+    float *k_pre, *v_pre;             /* [B, T, Hkv*dh], k after RoPE */
 } o_intermediates;
 
 /* RMSNorm, one row: [TIR] Code (rms_norm) and How it works step 2;
@@ -292,6 +297,9 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
     /* RoPE on q and k only, never on v ([TIR] Pitfalls). */
     o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);
     o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);
+    if (inter && inter->q_pre) memcpy(inter->q_pre, q, sizeof(float) * R * qd);
+    if (inter && inter->k_pre) memcpy(inter->k_pre, k, sizeof(float) * M * kvd);
+    if (inter && inter->v_pre) memcpy(inter->v_pre, v, sizeof(float) * M * kvd);
     operand_round(cfg, q, R * qd);
     operand_round(cfg, k, M * kvd);
     operand_round(cfg, v, M * kvd);
@@ -343,6 +351,7 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
 
     /* Wo and the first residual: r = x + att.Wo ([TIR] How it works step 2). */
     float *a = (float *)malloc(sizeof(float) * R * d);
+    if (inter && inter->att_pre) memcpy(inter->att_pre, att, sizeof(float) * R * qd);
     operand_round(cfg, att, R * qd);
     o_matmul(att, w->wo, R, qd, d, a, cnt);
     if (inter && inter->att) memcpy(inter->att, att, sizeof(float) * R * qd);
@@ -365,6 +374,7 @@ int o_block_forward(const o_config *cfg, const o_weights *w, const float *cos_ta
     free(h2);
     for (int64_t i = 0; i < R * f; ++i) gate[i] = silu(gate[i]) * up[i];
     free(up);
+    if (inter && inter->act_pre) memcpy(inter->act_pre, gate, sizeof(float) * R * f);
     operand_round(cfg, gate, R * f);
     if (inter && inter->act) memcpy(inter->act, gate, sizeof(float) * R * f);
     float *m = (float *)malloc(sizeof(float) * R * d);
@@ -412,12 +422,14 @@ static int32_t argmax_row(const float *v, int n) {
  * layers: host array [L]; kcs, vcs: host arrays [L] of [B, Hkv, t_max, dh].
  * logits: [B, n_rows, V] for the selected rows (rows NULL = all T rows).
  * next_ids (nullable): [B] argmax of the last selected row of each sequence.
+ * k_pre, v_pre (nullable host arrays [L] of [B, T, Hkv*dh]): each layer's k
+ * (after RoPE) and v as computed, before bf16 storage.
  */
 int o_model_forward(const o_config *cfg, int n_layers, int vocab, const float *embed, const o_weights *layers,
                     const float *g_final, const float *w_unembed, const float *cos_tab, const float *sin_tab,
                     int t_max_table, const int32_t *ids, int B, int T, const int32_t *start, float **kcs,
                     float **vcs, int t_max, const int32_t *rows, int n_rows, float *logits, int32_t *next_ids,
-                    o_counters *cnt) {
+                    float **k_pre, float **v_pre, o_counters *cnt) {
     const int d = cfg->d;
     const int64_t M = (int64_t)B * T;
     if (!rows) n_rows = T;
@@ -432,8 +444,11 @@ int o_model_forward(const o_config *cfg, int n_layers, int vocab, const float *e
         int last = (l == n_layers - 1);
         /* Only the last layer may restrict its rows: earlier layers feed the
          * keys and values of every row to the next. */
+        o_intermediates kv = {0};
+        if (k_pre) kv.k_pre = k_pre[l];
+        if (v_pre) kv.v_pre = v_pre[l];
         rc = o_block_forward(cfg, &layers[l], cos_tab, sin_tab, t_max_table, x, B, T, start, kcs[l], vcs[l], t_max,
-                             last ? rows : NULL, last ? n_rows : T, y, NULL, cnt);
+                             last ? rows : NULL, last ? n_rows : T, y, &kv, cnt);
         /* the block output is the next block's input activation */
         operand_round(cfg, y, (last ? (int64_t)B * n_rows : M) * d);
         float *tmp = x; x = y; y = tmp;

@@ -38,10 +38,20 @@ MUTANTS = {
     "bf16_k_not_rounded": ("    operand_round(cfg, k, M * kvd);\n", ""),
     "bf16_act_not_rounded": ("    operand_round(cfg, gate, R * f);", ""),
     "bf16_q_rounded_before_rope": (
-        "    o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);\n    o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);\n"
-        "    operand_round(cfg, q, R * qd);\n",
+        "    o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);\n    o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);\n",
         "    operand_round(cfg, q, R * qd);\n    o_rope_apply(q, R, H, dh, pos_q, cos_tab, sin_tab);\n"
         "    o_rope_apply(k, M, Hkv, dh, pos_k, cos_tab, sin_tab);\n"),
+    # the value handed out as "before rounding" is taken after it
+    "bf16_pre_value_after_rounding": (
+        "    if (inter && inter->act_pre) memcpy(inter->act_pre, gate, sizeof(float) * R * f);\n"
+        "    operand_round(cfg, gate, R * f);",
+        "    operand_round(cfg, gate, R * f);\n"
+        "    if (inter && inter->act_pre) memcpy(inter->act_pre, gate, sizeof(float) * R * f);"),
+    # cache append
+    "kv_append_row_off_by_one": ("int64_t dst = (((int64_t)b * Hkv + g) * t_max + start[b] + t) * dh;",
+                                 "int64_t dst = (((int64_t)b * Hkv + g) * t_max + start[b] + t + 1) * dh;"),
+    "kv_append_source_heads_swapped": ("int64_t src = (((int64_t)b * n_new + t) * Hkv + g) * dh;",
+                                       "int64_t src = (((int64_t)b * Hkv + g) * n_new + t) * dh;"),
     "bf16_round_truncates": ("u += 0x7FFFu + ((u >> 16) & 1u);", "u += 0u;"),
     "bf16_layer_output_not_rounded": ("operand_round(cfg, y, (last ? (int64_t)B * n_rows : M) * d);", ""),
     "bf16_final_norm_not_rounded": ("operand_round(cfg, hn, R * d);", ""),
@@ -64,6 +74,9 @@ PINS = [
     P.test_rope_properties,
     P.test_attention_closed_forms,
     P.test_softmax_rows_sum_to_one,
+    P.test_values_before_rounding,
+    P.test_kv_append_places_every_value,
+    P.test_kv_append_equals_the_block_cache_write,
 ]
 
 

@@ -21,54 +21,7 @@ from tests.inputs import activations, block_weights, rel_err, small_cfg
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")
 
 
-# --------------------------------------------------------------------------
-# An independent fp64 composition out of PyTorch library routines (rms_norm,
-# matmul, complex rotation, scaled_dot_product_attention with is_causal, silu).
-# With bf16=True every GEMM operand is rounded to bf16 by torch's own
-# conversion where the pages' precision rule puts it ([TIR] Implementation
-# notes: bf16 GEMMs with fp32 accumulation, softmax and norms in fp32).
-# --------------------------------------------------------------------------
-def _bf16(a):
-    return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
-
-
-def torch_block_f64(cfg, w, x, start=0, bf16=False, window=0):
-    d, H, Hkv = cfg.d, cfg.n_heads, cfg.n_kv_heads
-    dh = d // H
-    rb = _bf16 if bf16 else (lambda a: a)
-    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
-    X = t(x)
-    B, T, _ = X.shape
-    h = rb(F.rms_norm(X, (d,), weight=t(w["g_attn"]), eps=cfg.rms_eps))
-    q = (h @ t(w["wq"])).reshape(B, T, H, dh)
-    k = (h @ t(w["wk"])).reshape(B, T, Hkv, dh)
-    v = (h @ t(w["wv"])).reshape(B, T, Hkv, dh)
-    pos = torch.arange(start, start + T, dtype=torch.float64)
-    theta = torch.tensor([cfg.rope_base ** (-2.0 * i / dh) for i in range(dh // 2)], dtype=torch.float64)
-    rot = torch.polar(torch.ones(T, dh // 2, dtype=torch.float64), pos[:, None] * theta[None, :])
-
-    def rope(a):
-        c = torch.view_as_complex(a.reshape(*a.shape[:-1], dh // 2, 2).contiguous())
-        return torch.view_as_real(c * rot[None, :, None, :]).reshape(a.shape)
-
-    q, k, v = rb(rope(q)), rb(rope(k)), rb(v)
-    g = H // Hkv
-    K = k.repeat_interleave(g, dim=2).transpose(1, 2)
-    V = v.repeat_interleave(g, dim=2).transpose(1, 2)
-    if window:
-        # band mask: key j visible to query i iff i - window < j <= i
-        i = torch.arange(T)[:, None]
-        j = torch.arange(T)[None, :]
-        band = (j <= i) & (j > i - window)
-        o = F.scaled_dot_product_attention(q.transpose(1, 2), K, V, attn_mask=band)
-    else:
-        o = F.scaled_dot_product_attention(q.transpose(1, 2), K, V, is_causal=True)
-    o = rb(o.transpose(1, 2).reshape(B, T, H * dh))
-    r = X + o @ t(w["wo"])
-    h2 = rb(F.rms_norm(r, (d,), weight=t(w["g_mlp"]), eps=cfg.rms_eps))
-    act = rb(F.silu(h2 @ t(w["w1"])) * (h2 @ t(w["w3"])))
-    return (r + act @ t(w["w2"])).numpy(), {"q": q.reshape(B, T, H * dh).numpy(), "att": o.numpy(),
-                                            "r": r.numpy(), "act": act.numpy()}
+from tests.exact import _bf16, torch_block_f64  # noqa: E402  (the fp64 library composition)
 
 
 TINY_SHAPES = [
@@ -132,6 +85,81 @@ def test_bf16_operands_match_fp64_composition(oracle):
             for key in ("q", "att", "act"):
                 gap, n = _bf16_gap(inter[key], rint[key])
                 assert gap <= 1 and n <= max(2, inter[key].size // 500), (key, gap, n)
+
+
+def test_values_before_rounding(oracle):
+    """The oracle's *_pre intermediates are the operands before their bf16
+    rounding: torch's own fp32 -> bf16 conversion of each gives the operand the
+    oracle handed on bit for bit, with fp32 storage they are the operands, and
+    they follow the fp64 composition's unrounded values (q and k after RoPE,
+    v, the attention output, the SwiGLU product)."""
+    for i, s in enumerate(TINY_SHAPES[:3]):
+        for dtype in ("f32", "bf16"):
+            cfg = small_cfg(d=s["d"], H=s["H"], Hkv=s["Hkv"], f=s["f"], number=60 + i, dtype=dtype)
+            w, _ = block_weights(cfg, gains="random")
+            x, _ = activations(cfg, 2, s["T"])
+            _, inter = oracle.block_forward(cfg, w, x, intermediates=True)
+            _, rint = torch_block_f64(cfg, w, x, bf16=dtype == "bf16")
+            for key in ("q", "att", "act"):
+                pre = inter[key + "_pre"]
+                if dtype == "f32":
+                    assert np.array_equal(pre, inter[key]), key
+                else:
+                    rounded = torch.from_numpy(pre).to(torch.bfloat16).to(torch.float32).numpy()
+                    assert np.array_equal(rounded, inter[key]), key
+                    assert np.any(pre.view(np.uint32) & 0xFFFF), key
+            for key in ("q_pre", "k_pre", "v_pre", "att_pre", "act_pre"):
+                assert rel_err(inter[key], rint[key]) <= 1e-5, (dtype, key, rel_err(inter[key], rint[key]))
+
+
+def test_kv_append_places_every_value(oracle):
+    """[TIR] How it works, KV cache paragraph: the keys and values of new
+    tokens go to rows start[b] + t of their sequence and KV head.  Each value
+    encodes its own (b, t, g, e), so the cache shows where every value landed;
+    every other row keeps its sentinel."""
+    B, Hkv, dh, t_max, n = 3, 2, 6, 11, 4
+    start = np.array([0, 5, 7], np.int32)
+    b, t, g, e = np.meshgrid(np.arange(B), np.arange(n), np.arange(Hkv), np.arange(dh), indexing="ij")
+    code = (1000 * b + 100 * t + 10 * g + e).astype(np.float32) + 1.0
+    kc = np.full((B, Hkv, t_max, dh), -7.0, np.float32)
+    vc = np.full_like(kc, -9.0)
+    oracle.kv_append(kc, vc, code, -code, start)
+    for bb in range(B):
+        for gg in range(Hkv):
+            for row in range(t_max):
+                tt = row - start[bb]
+                if 0 <= tt < n:
+                    want = 1.0 + 1000 * bb + 100 * tt + 10 * gg + np.arange(dh)
+                    assert np.array_equal(kc[bb, gg, row], want) and np.array_equal(vc[bb, gg, row], -want)
+                else:
+                    assert np.all(kc[bb, gg, row] == -7.0) and np.all(vc[bb, gg, row] == -9.0)
+    # a start that would run past t_max is refused and writes nothing
+    before = kc.copy()
+    with pytest.raises(ValueError):
+        oracle.kv_append(kc, vc, code, -code, np.array([0, 5, 8], np.int32))
+    assert np.array_equal(kc, before)
+
+
+def test_kv_append_equals_the_block_cache_write(oracle):
+    """Appending a block's own post-RoPE k and v (bf16 operands, as stored)
+    gives bit for bit the cache rows the block itself writes, at a nonzero start."""
+    cfg = small_cfg(d=64, H=4, Hkv=2, f=192, number=48, dtype="bf16")
+    w, _ = block_weights(cfg, gains="random")
+    x, _ = activations(cfg, 2, 9)
+    start = np.array([3, 6], np.int32)
+    B, T, dh, t_max = 2, 9, 16, 20
+    kc = np.zeros((B, 2, t_max, dh), np.float32)
+    vc = np.zeros_like(kc)
+    # earlier rows the block reads, and rows after the write, hold sentinels
+    kc[:], vc[:] = 0.25, -0.25
+    _, inter = oracle.block_forward(cfg, w, x, start=start, kc=kc, vc=vc, intermediates=True)
+    bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()  # noqa: E731
+    k_new = bf(inter["k_pre"]).reshape(B, T, 2, dh)
+    v_new = bf(inter["v_pre"]).reshape(B, T, 2, dh)
+    kc2 = np.full_like(kc, 0.25)
+    vc2 = np.full_like(vc, -0.25)
+    oracle.kv_append(kc2, vc2, k_new, v_new, start)
+    assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)
 
 
 def test_bf16_operands_are_bf16_values(oracle):
@@ -224,6 +252,38 @@ def test_decode_matches_fp64_library_composition(oracle):
         out = oracle.block_forward(cfg, w, x[:, p:p + 1], start=[p], kc=kc, vc=vc)
         assert rel_err(out[0, 0], ref[0, p]) <= 1e-5
     assert np.isnan(kc[:, :, 20:]).all() and np.isnan(vc[:, :, 20:]).all()
+
+
+def test_exact_decode_and_model_compositions(oracle):
+    """The fp64 decode and model compositions (tests/exact.py, used to measure
+    how far the method itself sits from the oracle at full size) agree with
+    the oracle at tiny shapes: a decode step over a cache of earlier rows, with
+    and without bf16 operands, and the bf16 model's last-row logits."""
+    from tests.exact import decode_f64, model_f64
+    import synth
+    for dtype in ("f32", "bf16"):
+        cfg = small_cfg(d=64, H=4, Hkv=2, f=192, number=62, dtype=dtype)
+        w, _ = block_weights(cfg, gains="random")
+        x, _ = activations(cfg, 3, 1)
+        lens = np.array([5, 11, 1], np.int32)
+        kc, _ = synth.normal(cfg.seed, 11, (3, 2, 16, 16), 1.0, dtype == "bf16")
+        vc, _ = synth.normal(cfg.seed, 12, (3, 2, 16, 16), 1.0, dtype == "bf16")
+        ref, inter = oracle.block_forward(cfg, w, x, start=lens, kc=kc.copy(), vc=vc.copy(), intermediates=True)
+        got, ex = decode_f64(cfg, w, x, lens, kc, vc, bf16=dtype == "bf16")
+        assert rel_err(got, ref) <= 1e-5, rel_err(got, ref)
+        for key in ("q_pre", "k_pre", "att_pre", "act_pre"):
+            assert rel_err(ex[key], inter[key]) <= 1e-5, key
+    cfg = small_cfg(number=73, dtype="bf16")
+    L, V, T = 2, 40, 7
+    layers = [block_weights(cfg, layer=l, gains="random")[0] for l in range(L)]
+    emb, _ = synth.normal(cfg.seed, 15, (V, cfg.d), 1.0, True)
+    wu, _ = synth.normal(cfg.seed, 17, (cfg.d, V), 0.1, True)
+    gf = synth.to_bf16(1.0 + synth.normal(cfg.seed, 16, (cfg.d,), 0.1, False)[0])[1]
+    ids = synth.integers(cfg.seed, 14, (2, T), 0, V - 1)
+    kcs = [np.zeros((2, cfg.n_kv_heads, T, cfg.head_dim), np.float32) for _ in range(L)]
+    vcs = [a.copy() for a in kcs]
+    logits, _ = oracle.model_forward(cfg, L, V, emb, layers, gf, wu, ids, kcs, vcs, rows=[T - 1])
+    assert rel_err(logits, model_f64(cfg, layers, emb, gf, wu, ids)) <= 1e-5
 
 
 def test_prefix_invariance_bitwise(oracle):

@@ -21,7 +21,8 @@ STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTY
 EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
            "tfb_model_forward", "tfb_block_prefill_varlen", "tfb_block_prefill_paged", "tfb_block_decode_paged",
            "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
-           "tfb_profile_stages", "tfb_profile_stage_name")
+           "tfb_profile_stages", "tfb_profile_stage_name", "tfb_workspace_view")
+VIEWS = {"q": 0, "att": 1, "r": 2, "act": 3}
 
 _VP = ctypes.c_void_p
 
@@ -72,6 +73,9 @@ def lib():
         L.tfb_workspace_bytes.argtypes = [ctypes.POINTER(BlockConfig), ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32]
         L.tfb_workspace_bytes.restype = ctypes.c_size_t
+        L.tfb_workspace_view.argtypes = [ctypes.POINTER(BlockConfig), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.tfb_workspace_view.restype = ctypes.c_int
         L.tfb_rope_table_init.argtypes = [ctypes.POINTER(BlockConfig), ctypes.c_int32, _VP, _VP]
         L.tfb_block_prefill.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
                                         ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -172,6 +176,25 @@ def workspace(cfg: Config, B: int, T: int, vocab: int = 0, device="cuda"):
     if n == 0:
         raise TfbError(-2, "tfb_workspace_bytes")
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def workspace_view(cfg: Config, ws, B: int, T: int, name: str, vocab: int = 0):
+    """A tensor view (no copy) of an intermediate the last block call left in
+    the workspace ``ws``: q [B, H, T, dh], att [B, T, H*dh], r [B, T, d]
+    (fp32) or act [B, T, f]."""
+    import torch
+    off = ctypes.c_size_t(0)
+    _check(lib().tfb_workspace_view(ctypes.byref(cfg.c()), B, T, vocab, VIEWS[name], ctypes.byref(off)),
+           "tfb_workspace_view")
+    dh = cfg.head_dim
+    shape = {"q": (B, cfg.n_heads, T, dh), "att": (B, T, cfg.n_heads * dh), "r": (B, T, cfg.d),
+             "act": (B, T, cfg.d_ff)}[name]
+    dt = torch.float32 if (name == "r" or cfg.dtype != "bf16") else torch.bfloat16
+    n = 1
+    for v in shape:
+        n *= v
+    nbytes = n * (4 if dt == torch.float32 else 2)
+    return ws[off.value:off.value + nbytes].view(dt).view(shape)
 
 
 def rope_table_init(cfg: Config, t_max: int, table=None):

@@ -3,6 +3,7 @@
 // "Transformer block", [PID] pidoku "The Transformer".
 #include <math.h>
 #include <stdint.h>
+#include <cstdint>
 #include <string.h>
 
 #include <algorithm>
@@ -25,11 +26,13 @@ inline size_t esize(int dtype) { return dtype == TFB_BF16 ? 2 : 4; }
 constexpr int kMaxSplits = 64;
 
 struct WsLayout {
-    size_t h, q, att, r, act, kv_k, kv_v, part, skinny, skinny_bytes, gsplit, gsplit_bytes, x0, x1, last, logits,
-        total;
+    size_t h, q, att, r, act, kv_k, kv_v, part, part_bytes, skinny, skinny_bytes, gsplit, gsplit_bytes, x0, x1, last,
+        logits, total;
 };
 
-WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
+// part_bytes: room for the decode-attention partials; the default holds
+// kMaxSplits chunks per (sequence, head), whatever the call's positions.
+WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab, size_t part_bytes = SIZE_MAX) {
     WsLayout L{};
     const size_t es = esize(c.dtype), M = (size_t)B * T;
     const size_t qd = (size_t)c.n_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
@@ -42,7 +45,9 @@ WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
     L.act = take(M * (size_t)c.d_ff * es);
     L.kv_k = take(M * kvd * es);  // keys and values when no cache is given
     L.kv_v = take(M * kvd * es);
-    L.part = take(attention_decode_scratch_bytes(B, c.n_heads, c.head_dim, kMaxSplits));
+    L.part_bytes =
+        part_bytes == SIZE_MAX ? attention_decode_scratch_bytes(B, c.n_heads, c.head_dim, kMaxSplits) : part_bytes;
+    L.part = take(L.part_bytes);
     if (c.dtype == TFB_BF16) {
         // split-K partials of the skinny GEMMs (rows <= kSkinnyMaxM): the
         // block's GEMMs in decode and the LM head over the last rows
@@ -51,7 +56,10 @@ WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab) {
             sk = std::max({skinny_part_bytes((int)M, c.d, (int)(qd + 2 * kvd)),
                            skinny_part_bytes((int)M, (int)qd, c.d), skinny_part_bytes((int)M, c.d, 2 * c.d_ff),
                            skinny_part_bytes((int)M, c.d_ff, c.d)});
+        // the LM head runs on the last row of each sequence, or on every row
+        // when all logits are wanted: both row counts may take this path
         if (vocab > 0 && B <= kSkinnyMaxM) sk = std::max(sk, skinny_part_bytes(B, c.d, vocab));
+        if (vocab > 0 && M <= (size_t)kSkinnyMaxM) sk = std::max(sk, skinny_part_bytes((int)M, c.d, vocab));
         if (sk) {
             L.skinny_bytes = sk;
             L.skinny = take(sk);
@@ -217,7 +225,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     a.kvm = kvm;
     a.scale = 1.0f / sqrtf((float)dh);
     a.partials = ws + L.part;
-    a.partial_bytes = attention_decode_scratch_bytes(B, H, dh, kMaxSplits);
+    a.partial_bytes = L.part_bytes;
     a.max_keys = pos ? max_pos + 1 : start + T;
     a.max_splits = kMaxSplits;
     a.window = c.window;
@@ -335,6 +343,20 @@ const char *tfb_status_string(tfb_status st) {
 size_t tfb_workspace_bytes(const tfb_block_config *cfg, int32_t B, int32_t T, int32_t vocab) {
     if (check_cfg(cfg) != TFB_OK || B <= 0 || T <= 0 || vocab < 0) return 0;
     return ws_layout(*cfg, B, T, vocab).total;
+}
+
+tfb_status tfb_workspace_view(const tfb_block_config *cfg, int32_t B, int32_t T, int32_t vocab, int32_t which,
+                              size_t *offset) {
+    if (check_cfg(cfg) != TFB_OK || B <= 0 || T <= 0 || vocab < 0) return TFB_ERR_SHAPE;
+    if (!offset) return TFB_ERR_NULL;
+    const WsLayout L = ws_layout(*cfg, B, T, vocab);
+    switch (which) {
+        case TFB_VIEW_Q: *offset = L.q; return TFB_OK;
+        case TFB_VIEW_ATT: *offset = L.att; return TFB_OK;
+        case TFB_VIEW_R: *offset = L.r; return TFB_OK;
+        case TFB_VIEW_ACT: *offset = L.act; return TFB_OK;
+    }
+    return TFB_ERR_SHAPE;
 }
 
 tfb_status tfb_rope_table_init(const tfb_block_config *cfg, int32_t t_max, float *table, void *stream) {

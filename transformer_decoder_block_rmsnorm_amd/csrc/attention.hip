@@ -100,7 +100,14 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
 //   S^T[keys, queries] = K . Q^T : lane l holds query l%32, so the softmax of
 //                                  a query lives in one lane (plus lane l^32).
 //   O^T[e, queries]   += V^T . P^T : P^T comes straight from the S^T
-//                                  accumulators (converted to bf16).
+//                                  accumulators, as a hi + lo pair of bf16
+//                                  fragments (two products per V^T
+//                                  fragment), so the fp32 softmax weights
+//                                  keep ~16 significant bits.  Rounded to
+//                                  one bf16 operand instead, they made the
+//                                  block output's error sigma against the
+//                                  fp32 reference 15% larger at the 7B
+//                                  shape (the attention delta's 84%).
 // K and V tiles of 64 keys go from global memory straight into a ring of LDS
 // stages (global_load_lds_dwordx4) in their cache layout, rows of dh values.
 // K rows are read as 16-byte fragments (chunks XOR-swizzled by key); the V^T
@@ -324,18 +331,23 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
                 }
             l_run += sum_halves(sum);
             // P^T fragment of 16-key slice s2: lane (query lr, half lh) holds
-            // keys 16 s2 + {4lh .. 4lh+3, 8+4lh .. 8+4lh+3}
-            bf16x8 pf[4];
+            // keys 16 s2 + {4lh .. 4lh+3, 8+4lh .. 8+4lh+3}.  The weights are
+            // fp32 softmax values; they enter the bf16 product as a hi + lo
+            // pair of bf16 fragments, both against the same V^T fragment.
+            bf16x8 pf[4], pl[4];
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 const f32x16 &src = sacc[s2 >> 1];
                 const int o = 8 * (s2 & 1);
-                u32x4 w;
-                w[0] = pack_bf16x2(src[o + 0], src[o + 1]);
-                w[1] = pack_bf16x2(src[o + 2], src[o + 3]);
-                w[2] = pack_bf16x2(src[o + 4], src[o + 5]);
-                w[3] = pack_bf16x2(src[o + 6], src[o + 7]);
+                u32x4 w, wl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x2 hl = split_bf16x2(src[o + 2 * i], src[o + 2 * i + 1]);
+                    w[i] = hl[0];
+                    wl[i] = hl[1];
+                }
                 pf[s2] = as_bf16x8(w);
+                pl[s2] = as_bf16x8(wl);
             }
 #pragma unroll
             for (int te = 0; te < NE; ++te) {
@@ -345,7 +357,9 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
                     const int r0 = 16 * s2 + v_row, r1 = r0 + 8;
                     const u32x2 lo = lds_read_tr16(Vs + r0 * DH + ((gran ^ v_granule_swz<DH>(r0)) * 16) + v_in);
                     const u32x2 hi = lds_read_tr16(Vs + r1 * DH + ((gran ^ v_granule_swz<DH>(r1)) * 16) + v_in);
-                    oacc[te] = mfma32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pf[s2], oacc[te]);
+                    const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    oacc[te] = mfma32(vf, pf[s2], oacc[te]);
+                    oacc[te] = mfma32(vf, pl[s2], oacc[te]);
                 }
             }
         }
@@ -596,16 +610,22 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
             for (int v = 0; v < 4; ++v) oacc[c][v] *= al[v];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            u32x4 pw;
-            pw[0] = pack_bf16x2(sacc[2 * u][0], sacc[2 * u][1]);
-            pw[1] = pack_bf16x2(sacc[2 * u][2], sacc[2 * u][3]);
-            pw[2] = pack_bf16x2(sacc[2 * u + 1][0], sacc[2 * u + 1][1]);
-            pw[3] = pack_bf16x2(sacc[2 * u + 1][2], sacc[2 * u + 1][3]);
-            const bf16x8 pf = as_bf16x8(pw);
+            // fp32 softmax weights as a hi + lo pair of bf16 operands
+            u32x4 pw, pwl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 hl = split_bf16x2(sacc[2 * u + (i >> 1)][2 * (i & 1)], sacc[2 * u + (i >> 1)][2 * (i & 1) + 1]);
+                pw[i] = hl[0];
+                pwl[i] = hl[1];
+            }
+            const bf16x8 pf = as_bf16x8(pw), pl = as_bf16x8(pwl);
             u32x4 vt[8];
             transpose8x8_bf16(vr[u], vt);
 #pragma unroll
-            for (int c = 0; c < 8; ++c) oacc[c] = mfma16(pf, as_bf16x8(vt[c]), oacc[c]);
+            for (int c = 0; c < 8; ++c) {
+                oacc[c] = mfma16(pf, as_bf16x8(vt[c]), oacc[c]);
+                oacc[c] = mfma16(pl, as_bf16x8(vt[c]), oacc[c]);
+            }
         }
     }
     // per-wave results to LDS: head 4*g4 + v, e = 8*ln + c
@@ -790,6 +810,12 @@ hipError_t attention_decode_merge_launch(const AttnCall &a, hipStream_t s) {
 }
 size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits) {
     return decode_part_bytes(B, H, dh, max_splits);
+}
+size_t attention_decode_call_bytes(const AttnCall &a) {
+    if (!split_decode_applies(a)) return 0;
+    DecArgs d;
+    split_decode_args(a, d);
+    return decode_part_bytes(a.B, a.H, a.dh, d.max_chunks);
 }
 
 }  // namespace tfb

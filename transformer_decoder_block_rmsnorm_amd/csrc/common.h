@@ -27,6 +27,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xFFFFu); }
 
+// Two fp32 values as a sum of two bf16 pairs: hi = nearest bf16, lo = nearest
+// bf16 of what that rounding left (a - hi is exact in fp32).  hi + lo carries
+// ~16 significant bits, so a bf16 product fed with both halves and fp32
+// accumulation matches an fp32 operand to ~2^-17 relative.  Used for the
+// softmax weights of P.V, which the method keeps in fp32.
+// Returns {hi, lo}.
+__device__ __forceinline__ u32x2 split_bf16x2(float a, float b) {
+    const uint32_t hi = pack_bf16x2(a, b);
+    return u32x2{hi, pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u))};
+}
+
 // Storage-type traits: load/store one element as fp32.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

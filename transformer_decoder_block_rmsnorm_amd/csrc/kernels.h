@@ -71,7 +71,10 @@ hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
 // Merge of the split-KV chunk partials into o (after attention_decode_launch).
 hipError_t attention_decode_merge_launch(const AttnCall &a, hipStream_t s);
-size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_keys);
+size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits);
+// Partial-buffer bytes the decode kernels use for this call (its chunk count),
+// never more than attention_decode_scratch_bytes(B, H, dh, a.max_splits).
+size_t attention_decode_call_bytes(const AttnCall &a);
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
                             int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s);

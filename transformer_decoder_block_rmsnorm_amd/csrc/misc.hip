@@ -4,6 +4,8 @@
 // Transformer".
 #include <atomic>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace tfb {
@@ -143,15 +145,18 @@ hipError_t rope_table_launch(int t_max, int dh, double base, float *table, hipSt
 }
 
 // KV append ([TIR] How it works, KV cache): [B, n, Hkv, dh] -> cache rows
-// start[b] + t.  One thread per 4 elements; rows outside [0, t_max) are skipped.
+// start[b] + t.  One thread per pair of elements (dh is even, so a pair never
+// straddles a row and every pair is 4- or 8-byte aligned); rows outside
+// [0, t_max) are skipped.
 template <typename T>
 __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const int32_t *start, int B, int n_new,
                                  int Hkv, int dh, KvMap kvm) {
+    typedef typename std::conditional<sizeof(T) == 2, uint32_t, u32x2>::type Pair;
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int per_row = dh / 4;
+    const int per_row = dh / 2;
     const int64_t total = (int64_t)B * n_new * Hkv * per_row;
     if (idx >= total) return;
-    const int e4 = (int)(idx % per_row);
+    const int e2 = (int)(idx % per_row);
     int64_t r = idx / per_row;
     const int g = (int)(r % Hkv);
     r /= Hkv;
@@ -159,20 +164,15 @@ __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const i
     const int b = (int)(r / n_new);
     const int p = start[b] + t;
     if (p < 0 || p >= kvm.t_max) return;
-    const int64_t src = (((int64_t)b * n_new + t) * Hkv + g) * dh + e4 * 4;
-    const int64_t dst = kv_row(kvm, b, Hkv, g, p) * dh + e4 * 4;
-    if constexpr (sizeof(T) == 2) {
-        *(u32x2 *)(kc + dst) = *(const u32x2 *)(kn + src);
-        *(u32x2 *)(vc + dst) = *(const u32x2 *)(vn + src);
-    } else {
-        *(u32x4 *)(kc + dst) = *(const u32x4 *)(kn + src);
-        *(u32x4 *)(vc + dst) = *(const u32x4 *)(vn + src);
-    }
+    const int64_t src = (((int64_t)b * n_new + t) * Hkv + g) * dh + e2 * 2;
+    const int64_t dst = kv_row(kvm, b, Hkv, g, p) * dh + e2 * 2;
+    *(Pair *)(kc + dst) = *(const Pair *)(kn + src);
+    *(Pair *)(vc + dst) = *(const Pair *)(vn + src);
 }
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
                             int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s) {
-    const int64_t total = (int64_t)B * n_new * Hkv * (dh / 4);
+    const int64_t total = (int64_t)B * n_new * Hkv * (dh / 2);
     dim3 grid((unsigned)((total + 255) / 256));
     if (dtype == TFB_BF16)
         hipLaunchKernelGGL(kv_append_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)kc, (bf16_t *)vc,
