@@ -1,18 +1,24 @@
 """Benchmark of the decoder-block hot path on one MI355X.
 
-Headline (`value`): block prefill TFLOP/s on the Llama-2-7B-shaped block
-(d=4096, H=Hkv=32, dh=128, f=11008, B=1, T=2048, bf16 storage, fp32
-accumulation, KV cache written), algorithmic causal FLOP count.  In the same
-run:
+Headline (`value`): block prefill TFLOP/s on the largest block-prefill
+workload, the GQA long-context block (d=4096, H=32, Hkv=8, dh=128, f=14336,
+RoPE base 5e5, B=2, T=8192, bf16 storage, fp32 accumulation, KV cache
+written), algorithmic causal FLOP count; `roofline` is its dominant kernel,
+the fused gate-up GEMM.  In the same run:
+  - the Llama-2-7B-shaped block prefill (d=4096, H=Hkv=32, f=11008, B=1,
+    T=2048) in TFLOP/s;
   - the GQA decode step (d=4096, H=32, Hkv=8, f=14336, B=64 sequences with
     cache lengths uniform in [1024, 4096]) in tokens/s, with the
-    decode-attention kernel's achieved HBM bandwidth;
-  - the GQA long-context block prefill (B=2, T=8192) in TFLOP/s;
+    decode-attention kernel's and each weight-streaming GEMM's achieved HBM
+    bandwidth;
   - the 32-layer model (B=4, prompt T=1024, V=32000): prefill TFLOP/s and
     128 greedy decode steps in tokens/s.
 Inputs are synthetic and seeded, resident in HBM before timing starts.
+Every timed leg first runs its warmup steps and then keeps stepping until at
+least a second of warm work has run, so a short --warmup cannot leave the
+timed steps on a cold clock.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-long] [--no-model]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-7b] [--no-model]
        python bench.py --copy-calibration   (a plain 1 GiB device copy, for
                                              scaling the HBM byte counters)
 """
@@ -35,7 +41,7 @@ PEAK_HBM_GBPS = 8000.0      # HBM3E
 
 # HBM traffic of the gate-up GEMM from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
 # with the sources of the kernel it was taken on (stale counters give null)
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "gateup_gemm_7b_prefill_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gateup_gemm_gqa_long_prefill_pmc.md")
 GEMM_SOURCES = [os.path.join(ROOT, "transformer_decoder_block_rmsnorm_amd", "csrc", n)
                 for n in ("gemm.hip", "epilogue.h", "common.h")]
 
@@ -90,6 +96,24 @@ def _dev_tensor(f32, bits):
     return torch.from_numpy(f32).cuda()
 
 
+MIN_WARM_SECONDS = 1.0  # set from --min-warm
+
+
+def warm_up(step, warmup, min_seconds=None):
+    """`warmup` untimed steps, then more until min_seconds of work have run."""
+    import torch
+    if min_seconds is None:
+        min_seconds = MIN_WARM_SECONDS
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    while time.time() - t0 < min_seconds:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
 def block_inputs(cfg, B, T):
     from synth.inputs import activations, block_weights
     w32, bits = block_weights(cfg)
@@ -113,9 +137,7 @@ def time_prefill(cfg, steps, warmup):
     def step():
         tfb.block_prefill(tc, w, rope, x, out, cache=(kc, vc), ws=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     # timed region: K steps; the dominant kernel (the fused gate-up GEMM) is
     # bracketed by HIP events on its launch stream
     tfb.profile_read()
@@ -175,9 +197,7 @@ def time_decode(cfg, steps, warmup):
     def step():
         tfb.block_decode(tc, w, rope, x, out, (kc, vc), pos, int(lens.max()), ws=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, warmup)
     tfb.profile_read()
     tfb.profile_stages(["attention", "attention_combine"])
     total = 0.0
@@ -207,48 +227,20 @@ def time_decode(cfg, steps, warmup):
     return dict(ms=ms, stages=stages, dominant=dominant, attn_bytes=attn_bytes, weight_bytes=wbytes, lens=lens)
 
 
-def time_long_prefill(cfg, steps, warmup):
-    """The GQA long-context block prefill: whole-step time, then one pass with
-    every stage bracketed by events for the breakdown."""
-    import torch
-    import transformer_decoder_block_rmsnorm_amd as tfb
-    tc = tfb.Config.of(cfg)
-    B, T = cfg.B, cfg.T
-    _, w, _, x = block_inputs(cfg, B, T)
-    rope = tfb.rope_table_init(tc, cfg.t_max)
-    kc = torch.zeros((B, cfg.n_kv_heads, cfg.t_max, tc.head_dim), dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros_like(kc)
-    out = torch.empty_like(x)
-    ws = tfb.workspace(tc, B, T)
-
-    def step():
-        tfb.block_prefill(tc, w, rope, x, out, cache=(kc, vc), ws=ws)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    tfb.profile_read()
-    tfb.profile_stages(None)
-    tfb.profile_enable(True)
-    step()
-    torch.cuda.synchronize()
-    tfb.profile_enable(False)
-    stages = {k: round(v[0] / v[1], 4) for k, v in tfb.profile_read().items()}
-    flops = prefill_flops(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
-    attn = 4 * (cfg.d // cfg.n_heads) * cfg.n_heads * B * T * (T + 1) // 2
-    return {"workload": "GQA long-context block prefill: d=4096 H=32 Hkv=8 dh=128 f=14336 B=2 T=8192, "
-                        "KV cache written",
-            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
-                                                                                PEAK_BF16_TFLOPS, 4),
-            "ms_per_step": round(ms, 4), "steps": steps, "flops_per_step": flops, "stage_ms": stages,
-            "attention_tflops": round(attn / (stages["attention"] * 1e-3) / 1e12, 2)}
+def decode_gemm_rates(cfg, stages):
+    """Weight bytes of each decode GEMM (the bytes it must stream; the 64
+    activation rows add <2%) over its bracketed time, reduce pass included."""
+    d, H, Hkv, f = cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff
+    dh = d // H
+    wbytes = {"qkv_gemm": 2 * d * (H + 2 * Hkv) * dh, "wo_gemm": 2 * H * dh * d, "gateup_gemm": 2 * d * 2 * f,
+              "w2_gemm": 2 * f * d}
+    out = {}
+    for k, b in wbytes.items():
+        if k in stages and stages[k][1]:
+            ms = stages[k][0] / stages[k][1]
+            out[k] = {"weight_bytes": b, "ms": round(ms, 4), "GB_s": round(b / (ms * 1e-3) / 1e9, 1),
+                      "frac": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    return out
 
 
 def time_model(cfg, decode_steps, reps):
@@ -295,9 +287,13 @@ def time_model(cfg, decode_steps, reps):
         for s in range(decode_steps):
             tfb.model_forward(h, rope, nxt, caches, lens, T + s, last_only=True, next_ids=nxt.view(B), ws=ws_dec)
 
-    prefill()
-    decode()
-    torch.cuda.synchronize()
+    t0 = time.time()
+    while True:
+        prefill()
+        decode()
+        torch.cuda.synchronize()
+        if time.time() - t0 >= MIN_WARM_SECONDS:
+            break
     pre_ms, dec_ms = [], []
     for _ in range(reps):
         flush.fill_(1)
@@ -390,14 +386,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-7b", action="store_true")
     ap.add_argument("--model-reps", type=int, default=3)
     ap.add_argument("--decode-only", action="store_true",
                     help="only the GQA decode step (for counter runs); prints the decode fields alone")
     ap.add_argument("--no-model", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--min-warm", type=float, default=1.0,
+                    help="seconds of warm steps before each timed leg (after --warmup steps)")
     args = ap.parse_args()
+    global MIN_WARM_SECONDS
+    MIN_WARM_SECONDS = args.min_warm
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
@@ -424,28 +424,48 @@ def main():
                           "ms_per_step": round(dec["ms"], 4), "attention_bytes": dec["attn_bytes"],
                           "weight_bytes": dec["weight_bytes"]}), flush=True)
         return
-    pre = time_prefill(C2, args.steps, args.warmup)
-    tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
-    gms, gcalls = pre["dominant"]["gateup_gemm"]
-    g_ms = gms / gcalls
-    g_flops = 2 * C2.B * C2.T * C2.d * 2 * C2.d_ff
-    roof = {"kernel": "gateup_gemm (fused W1|W3 GEMM + SiLU*up)", "bound": "mfma",
-            "achieved": round(g_flops / (g_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-            "launch_ms": round(g_ms, 4), "flops_per_launch": g_flops}
-    stages = {k: round(v[0] / v[1], 4) for k, v in pre["stages"].items()}
+    def prefill_summary(cfg, pre, workload):
+        """TFLOP/s of the block step and the roofline entry of its gate-up GEMM."""
+        tflops = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+        gms, gcalls = pre["dominant"]["gateup_gemm"]
+        g_ms = gms / gcalls
+        g_flops = 2 * cfg.B * cfg.T * cfg.d * 2 * cfg.d_ff
+        roof = {"kernel": "gateup_gemm (fused W1|W3 GEMM + SiLU*up)", "bound": "mfma",
+                "achieved": round(g_flops / (g_ms * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "launch_ms": round(g_ms, 4), "flops_per_launch": g_flops}
+        stages = {k: round(v[0] / v[1], 4) for k, v in pre["stages"].items()}
+        attn = 4 * (cfg.d // cfg.n_heads) * cfg.n_heads * cfg.B * cfg.T * (cfg.T + 1) // 2
+        return tflops, roof, {"workload": workload, "tflops": round(tflops, 2),
+                              "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4), "ms_per_step": round(pre["ms"], 4),
+                              "ms_per_step_all_events": round(pre["ms_all_events"], 4),
+                              "flops_per_step": pre["flops"], "stage_ms": stages,
+                              "attention_tflops": round(attn / (stages["attention"] * 1e-3) / 1e12, 2)}
+
+    long_workload = ("GQA long-context block prefill: d=4096 H=32 Hkv=8 dh=128 f=14336 RoPE base 5e5 B=2 T=8192, "
+                     "KV cache written")
+    pre = time_prefill(C3, args.steps, args.warmup)
+    tflops, roof, long_summary = prefill_summary(C3, pre, long_workload)
+    roof["traffic"] = measured_traffic()
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4), "ms_per_step_all_events": round(pre["ms_all_events"], 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4),
+        "ms_per_step_all_events": round(pre["ms_all_events"], 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Llama-2-7B-shaped block prefill: d=4096 H=Hkv=32 dh=128 f=11008 B=1 T=2048, "
-                               "KV cache written", "global_batch": C2.B, "seq_len": C2.T, "parallelism": "none"},
+        "config": {"workload": long_workload, "global_batch": C3.B, "seq_len": C3.T, "parallelism": "none"},
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "flops_per_step": pre["flops"],
         "roofline": roof,
-        "prefill_stage_ms": stages,
+        "prefill_stage_ms": long_summary["stage_ms"],
+        "attention_tflops": long_summary["attention_tflops"],
     }
+    if not args.no_7b:
+        pre7 = time_prefill(C2, args.steps, args.warmup)
+        _, roof7, sum7 = prefill_summary(C2, pre7, "Llama-2-7B-shaped block prefill: d=4096 H=Hkv=32 dh=128 "
+                                                   "f=11008 B=1 T=2048, KV cache written")
+        sum7["gateup_roofline"] = roof7
+        result["prefill_7b"] = sum7
     if not args.no_decode:
         dec = time_decode(C4, args.steps, args.warmup)
         ams, acalls = dec["dominant"]["attention"]
@@ -468,14 +488,13 @@ def main():
             "step_hbm_frac": round((dec["attn_bytes"] + dec["weight_bytes"]) / (dec["ms"] * 1e-3) / 1e9 /
                                    PEAK_HBM_GBPS, 4),
             "stage_ms": {k: round(v[0] / v[1], 4) for k, v in dec["stages"].items()},
+            "gemm_hbm": decode_gemm_rates(C4, dec["stages"]),
         }
-    if not args.no_long:
-        result["long_prefill"] = time_long_prefill(C3, max(2, args.steps // 6), max(1, args.warmup // 10))
     if not args.no_model:
         result["model"] = time_model(C5, C5.decode_steps, max(1, args.model_reps))
         result["tiny"] = time_tiny(C1, 21)
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(C2, pre["w32"], pre["x32"], args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(C3, pre["w32"], pre["x32"], args.cpu_rows)
     print(json.dumps(result), flush=True)
 
 
