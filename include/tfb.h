@@ -196,6 +196,26 @@ tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights
                             int32_t t_max_table, const void *x, void *out, int32_t B, tfb_kv_cache *cache,
                             const int32_t *pos, int32_t h_max_pos, void *ws, size_t ws_bytes, void *stream);
 
+/* tfb_block_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and the same kernels, with the workspace taken from a
+ * static device array of the library instead of a caller buffer.  The array
+ * holds tfb_noalloc_scratch_bytes() bytes (32 MiB) on every GPU the library
+ * runs on, until the process ends; its device address is looked up once per
+ * device, on the first call with that device current (the calling thread's
+ * current device must be the device of `stream`).  A call whose workspace
+ * would exceed it returns TFB_ERR_WORKSPACE before launching anything (the
+ * GQA decode step with B = 64, d = 4096, f = 14336 and 4096 cached rows needs
+ * ~23 MiB).  Nothing in the array needs to start at zero: every partial
+ * result is written before it is read.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (different streams, or
+ * threads) race; serialise them.  No device memory is allocated or freed. */
+tfb_status tfb_block_decode_noalloc(const tfb_block_config *cfg, const tfb_block_weights *w,
+                                    const float *rope_table, int32_t t_max_table, const void *x, void *out, int32_t B,
+                                    tfb_kv_cache *cache, const int32_t *pos, int32_t h_max_pos, void *stream);
+/* Size of the static array tfb_block_decode_noalloc works in, per GPU. */
+size_t tfb_noalloc_scratch_bytes(void);
+
 /* tfb_block_prefill and tfb_block_decode on a paged cache: the same
  * computation, with cache rows found through the block table (positions and
  * bounds as in the contiguous calls, with t_max = max_blocks * block_size).

@@ -21,7 +21,8 @@ STATUS = {0: "TFB_OK", -1: "TFB_ERR_NULL", -2: "TFB_ERR_SHAPE", -3: "TFB_ERR_DTY
 EXPORTS = ("tfb_workspace_bytes", "tfb_rope_table_init", "tfb_block_prefill", "tfb_block_decode", "tfb_kv_append",
            "tfb_model_forward", "tfb_block_prefill_varlen", "tfb_block_prefill_paged", "tfb_block_decode_paged",
            "tfb_status_string", "tfb_version", "tfb_profile_enable", "tfb_profile_read",
-           "tfb_profile_stages", "tfb_profile_stage_name", "tfb_workspace_view")
+           "tfb_profile_stages", "tfb_profile_stage_name", "tfb_workspace_view",
+           "tfb_block_decode_noalloc", "tfb_noalloc_scratch_bytes")
 VIEWS = {"q": 0, "att": 1, "r": 2, "act": 3}
 
 _VP = ctypes.c_void_p
@@ -92,6 +93,11 @@ def lib():
         L.tfb_block_decode.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
                                        ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.POINTER(KVCache), _VP,
                                        ctypes.c_int32, _VP, ctypes.c_size_t, _VP]
+        L.tfb_block_decode_noalloc.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeights), _VP,
+                                               ctypes.c_int32, _VP, _VP, ctypes.c_int32, ctypes.POINTER(KVCache), _VP,
+                                               ctypes.c_int32, _VP]
+        L.tfb_block_decode_noalloc.restype = ctypes.c_int
+        L.tfb_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.tfb_kv_append.argtypes = [ctypes.POINTER(BlockConfig), ctypes.POINTER(KVCache), _VP, _VP, _VP,
                                     ctypes.c_int32, ctypes.c_int32, _VP]
         L.tfb_model_forward.argtypes = [ctypes.POINTER(Model), _VP, ctypes.c_int32, _VP, ctypes.c_int32,
@@ -273,6 +279,20 @@ def block_decode(cfg: Config, w: dict, rope, x, out, cache, pos, h_max_pos: int,
                                   rope.shape[0], _ptr(x), _ptr(out), B, ctypes.byref(cache_struct(*cache)),
                                   _ptr(pos), h_max_pos, _ptr(ws), ws_n, _stream()), "tfb_block_decode")
     return out
+
+
+def block_decode_noalloc(cfg: Config, w: dict, rope, x, out, cache, pos, h_max_pos: int):
+    """tfb_block_decode with the library's static scratch as workspace (no
+    allocation anywhere in the call)."""
+    B = x.shape[0]
+    _check(lib().tfb_block_decode_noalloc(ctypes.byref(cfg.c()), ctypes.byref(weights_struct(w)), _ptr(rope),
+                                          rope.shape[0], _ptr(x), _ptr(out), B, ctypes.byref(cache_struct(*cache)),
+                                          _ptr(pos), h_max_pos, _stream()), "tfb_block_decode_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().tfb_noalloc_scratch_bytes())
 
 
 def kv_append(cfg: Config, cache, k_new, v_new, start, h_max_start: int):

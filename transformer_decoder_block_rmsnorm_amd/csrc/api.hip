@@ -284,6 +284,34 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
 
 }  // namespace
 
+// ---- allocation-free decode (tfb_block_decode_noalloc) ----------------------
+// The workspace of one decode step lives in this file-scope device array.  In
+// host code `scratch` names a host-side stand-in; the device address of each
+// GPU's own copy is looked up once per device and kept in g_scratch_dev.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_dev[kMaxDevices];  // nullptr: not looked up yet on that device
+
+// Device address of the current device's `scratch` (hipGetSymbolAddress with
+// that device current, once per device).
+tfb_status scratch_on_current_device(uint8_t **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TFB_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TFB_ERR_HIP;
+        g_scratch_dev[dev] = (uint8_t *)p;
+    }
+    *out = g_scratch_dev[dev];
+    return TFB_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t tfb_version(void) { return 100; }
@@ -431,6 +459,36 @@ tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights
     if (!aligned(ws)) return TFB_ERR_ALIGN;
     return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v, cache->t_max, (uint8_t *)ws,
                      L, (hipStream_t)stream);
+}
+
+// ---- allocation-free decode: see scratch_on_current_device above ----
+size_t tfb_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+tfb_status tfb_block_decode_noalloc(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
+                                    int32_t t_max_table, const void *x, void *out, int32_t B, tfb_kv_cache *cache,
+                                    const int32_t *pos, int32_t h_max_pos, void *stream) {
+    tfb_status st = check_cfg(cfg);
+    if (st != TFB_OK) return st;
+    if ((st = check_weights(w)) != TFB_OK) return st;
+    if (!rope_table || !x || !out || !cache || !pos) return TFB_ERR_NULL;
+    if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
+    if (B <= 0 || h_max_pos < 0) return TFB_ERR_SHAPE;
+    if ((st = check_cache(cache, B)) != TFB_OK) return st;
+    if (h_max_pos >= cache->t_max || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    // the decode-attention partials this call's chunk plan needs (the plan
+    // is the one tfb_block_decode makes, so the launches are the same)
+    AttnCall a{};
+    a.dtype = cfg->dtype;
+    a.B = B; a.T = 1; a.H = cfg->n_heads; a.Hkv = cfg->n_kv_heads; a.dh = cfg->head_dim;
+    a.max_keys = h_max_pos + 1;
+    a.max_splits = kMaxSplits;
+    a.window = cfg->window;
+    const WsLayout L = ws_layout(*cfg, B, 1, 0, attention_decode_call_bytes(a));
+    if (L.total > kScratchBytes) return TFB_ERR_WORKSPACE;
+    uint8_t *ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != TFB_OK) return st;
+    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v,
+                     cache->t_max, ws, L, (hipStream_t)stream);
 }
 
 // Paged cache: validated host fields, and the row map the kernels use.
