@@ -65,9 +65,9 @@ typedef enum { TFB_F32 = 0, TFB_BF16 = 1 } tfb_dtype;
  * epsilon inside the square root.  window > 0 limits attention to a sliding
  * window: the query at position p attends to keys p - window + 1 .. p, its own
  * included (pidoku "The Transformer", Sliding-window attention); 0 is full
- * causal attention.  The cache layout does not change with a window: rows
- * stay at their absolute positions, and rows below a query's window are not
- * read. */
+ * causal attention.  Rows below a query's window are never read.  With a
+ * window, a cache may also be a bounded ring (the `ring` field of the cache
+ * structs): that page notes that the window caps the KV cache. */
 typedef struct {
     int32_t d, n_heads, n_kv_heads, head_dim, d_ff;
     float rope_base, rms_eps;
@@ -87,11 +87,23 @@ typedef struct {
 
 /* KV cache of one layer: k and v are each [batch, Hkv, t_max, dh] in the
  * config's storage type.  Keys are kept after RoPE, values as projected (the
- * KV cache paragraph of How it works).  Row t of sequence b holds the token
- * at absolute position t. */
+ * KV cache paragraph of How it works).
+ * ring == 0: row t of sequence b holds the token at absolute position t, and
+ *   positions must stay below t_max.
+ * ring != 0: a bounded sliding-window cache (pidoku "The Transformer",
+ *   Sliding-window attention: the KV cache is capped at the window).  It
+ *   holds the last t_max positions of each sequence: position p lives in row
+ *   p mod t_max, positions are bounded only by the RoPE table, and rows older
+ *   than t_max positions are overwritten.  Needs config window > 0 with
+ *   window <= t_max (t_max == window is the smallest), and for fp32 storage
+ *   dh % 4 == 0.  Every call gives the same results, bit for bit, as on an
+ *   uncapped cache; a prefill chunk works in a contiguous copy of its window
+ *   in the workspace.  Variable-length prefill does not take a ring cache
+ *   (TFB_ERR_UNSUPPORTED). */
 typedef struct {
     void *k, *v;
     int32_t batch, t_max;
+    int32_t ring;
 } tfb_kv_cache;
 
 /* The thin model: embedding [V, d], L blocks, final RMSNorm gain [d] and an
@@ -123,6 +135,8 @@ typedef struct {
     void *k, *v;
     const int32_t *block_table;
     int32_t batch, block_size, max_blocks, n_blocks;
+    int32_t ring; /* != 0: bounded window cache over max_blocks * block_size
+                     slots, as in tfb_kv_cache: slot p mod that count */
 } tfb_paged_kv_cache;
 
 /* Bytes of workspace the calls below need for batch B, sequence T (T = 1 for
@@ -238,7 +252,8 @@ tfb_status tfb_block_decode_paged(const tfb_block_config *cfg, const tfb_block_w
  * sequence and head.  start: [B] int32 device, read-only; h_max_start is a
  * host upper bound of max(start) with h_max_start + n_new <= t_max (checked;
  * device code also skips any row outside [0, t_max)).  Rows outside the
- * written range are never touched.  Any even dh is accepted for fp32 storage. */
+ * written range are never touched.  Any even dh is accepted for fp32 storage.
+ * A ring cache takes rows at their slots p mod t_max, n_new <= t_max. */
 tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const void *k_new, const void *v_new,
                          const int32_t *start, int32_t n_new, int32_t h_max_start, void *stream);
 
@@ -250,7 +265,7 @@ tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const
  *          sequence starts at position 0) and becomes T;
  *   T == 1 decode: the new token sits at position lens[b]; lens[b] += 1.
  * h_max_len: host upper bound of max(lens) on entry (0 for prefill); must
- * satisfy h_max_len + T <= t_max.
+ * satisfy h_max_len + T <= t_max (ring caches: h_max_len + T <= t_max_table).
  * logits (nullable): fp32 [B, T, V], or [B, 1, V] when last_only != 0 (the
  * last row of each sequence only).
  * next_ids (nullable): [B] int32, argmax of each sequence's last row, lowest

@@ -185,6 +185,37 @@ def test_decode_and_append_reject_invalid_arguments():
     assert app(start=0) == -1
 
 
+def test_ring_cache_arguments():
+    """A bounded window cache needs a window no longer than the cache (and, in
+    fp32, head widths the staging copy moves in 16-byte pieces); positions
+    past its row count are fine; varlen prefill does not take one."""
+    lib = tfb.lib()
+    w = _weights()
+
+    def dec(cfg, t_max, h_max, ring=1, t_tab=100000):
+        c = tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 2, t_max, ring)
+        return lib.tfb_block_decode(ctypes.byref(cfg.c()), ctypes.byref(w), ctypes.c_void_p(FAKE), t_tab,
+                                    ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 2, ctypes.byref(c),
+                                    ctypes.c_void_p(FAKE), h_max, ctypes.c_void_p(FAKE), 16, None)
+
+    win = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024, window=64)
+    assert dec(win, 64, 5000) == -5              # passes every position check, stops at the workspace
+    assert dec(win, 64, 5000, t_tab=5000) == -6  # the RoPE table still bounds positions
+    assert dec(win, 64, 5000, ring=0) == -6      # an uncapped cache does not
+    assert dec(win, 63, 10) == -2                # window longer than the ring
+    assert dec(_cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024), 64, 10) == -2  # no window
+    f32 = _cfg(d=24, n_heads=4, n_kv_heads=2, d_ff=32, dtype="f32", window=8)  # dh = 6
+    assert dec(f32, 16, 10) == -2
+    c = tfb.KVCache(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 4096), 2, 64, 1)
+    assert lib.tfb_block_prefill_varlen(ctypes.byref(win.c()), ctypes.byref(w), ctypes.c_void_p(FAKE), 128,
+                                        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 2, 8, ctypes.c_void_p(FAKE),
+                                        ctypes.c_void_p(FAKE), 20, ctypes.byref(c), ctypes.c_void_p(FAKE), 1 << 40,
+                                        None) == -8
+    # appends: at most t_max rows per call (more would share slots)
+    assert lib.tfb_kv_append(ctypes.byref(win.c()), ctypes.byref(c), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), 65, 9000, None) == -6
+
+
 def test_model_rejects_invalid_arguments():
     lib = tfb.lib()
     cfg = _cfg(d=512, n_heads=4, n_kv_heads=2, d_ff=1024)

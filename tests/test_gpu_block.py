@@ -642,3 +642,154 @@ def test_paged_cache_matches_contiguous_bitwise(oracle, dtype, bs, W):
     # pool blocks no sequence owns are untouched
     free = np.setdiff1d(np.arange(n_blocks), perm.ravel())
     assert np.isnan(gkp[free]).all()
+
+
+# ---- bounded sliding-window cache (pidoku "The Transformer", Sliding-window
+# attention: with a window of W keys the KV cache is capped at W)
+def _ring_run(cfg, x, chunks, steps, caches, paged=None):
+    """Prefill in chunks then decode steps through one set of caches (either
+    (k, v[, ring]) tuples or a paged tuple); returns the outputs."""
+    torch = _torch()
+    tc = tfb.Config.of(cfg)
+    B = x.shape[0]
+    T = sum(chunks) + steps
+    rope = tfb.rope_table_init(tc, T)
+    outs, s0 = [], 0
+    for c in chunks:
+        xi = x[:, s0:s0 + c].contiguous()
+        o = torch.empty_like(xi)
+        if paged is None:
+            tfb.block_prefill(tc, caches["w"], rope, xi, o, start_pos=s0, cache=caches["kv"])
+        else:
+            tfb.block_prefill_paged(tc, caches["w"], rope, xi, o, paged, start_pos=s0)
+        outs.append(o)
+        s0 += c
+    for s in range(steps):
+        p = s0 + s
+        xi = x[:, p:p + 1].contiguous()
+        o = torch.empty_like(xi)
+        pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+        if paged is None:
+            tfb.block_decode(tc, caches["w"], rope, xi, o, caches["kv"], pos, p)
+        else:
+            tfb.block_decode_paged(tc, caches["w"], rope, xi, o, paged, pos, p)
+        outs.append(o)
+    torch.cuda.synchronize()
+    return np.concatenate([to_np(o) for o in outs], axis=1)
+
+
+@pytest.mark.parametrize("dtype,d,H,Hkv,W,ring_rows,chunks,steps", [
+    ("bf16", 256, 4, 2, 64, 64, [100], 160),          # ring of exactly W rows; decode to position 259 (> 4W)
+    ("bf16", 256, 4, 2, 64, 64, [40, 70, 1, 30], 40),  # chunked prefill into the ring, a one-row chunk
+    ("bf16", 512, 4, 1, 300, 300, [350], 400),         # dh 128, four heads per KV head, ring not a power of two
+    ("bf16", 512, 4, 2, 100, 160, [90, 90], 100),      # ring longer than the window
+    ("f32", 64, 4, 2, 7, 7, [20, 5], 30),              # fp32: row-wise attention over a 7-row ring
+])
+def test_ring_window_cache_matches_uncapped_bitwise(oracle, dtype, d, H, Hkv, W, ring_rows, chunks, steps):
+    """A bounded window cache of ring_rows rows (position p in row p mod
+    ring_rows) gives bit for bit the outputs of the same calls on an uncapped
+    cache, far past 2W positions, and matches the oracle's full-cache
+    computation."""
+    torch = _torch()
+    cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype=dtype, base=500000.0, number=150, window=W)
+    w32, w = dev_weights(cfg)
+    B = 2
+    T = sum(chunks) + steps
+    x32, x = dev_x(cfg, B, T)
+    print("case: ring cache", dtype, d, H, Hkv, W, ring_rows, chunks, steps, flush=True)
+    kr, vr = new_cache(cfg, B, ring_rows)
+    ku, vu = new_cache(cfg, B, T)
+    got_r = _ring_run(cfg, x, chunks, steps, {"w": w, "kv": (kr, vr, True)})
+    got_u = _ring_run(cfg, x, chunks, steps, {"w": w, "kv": (ku, vu)})
+    assert np.array_equal(got_r, got_u)
+    # the ring holds exactly the last ring_rows positions, each at its slot
+    gr, gu = widen_cache(kr), widen_cache(ku)
+    for p in range(T - ring_rows, T):
+        assert np.array_equal(gr[:, :, p % ring_rows], gu[:, :, p])
+    ref = oracle.block_forward(cfg, w32, x32)
+    check("out", got_r, ref, tol(cfg))
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_paged_ring_window_cache_matches_uncapped_bitwise(bs):
+    """A paged bounded window cache (ring over max_blocks * block_size slots)
+    equals the contiguous uncapped cache bit for bit; pool blocks no sequence
+    owns stay untouched."""
+    torch = _torch()
+    cfg = small_cfg(d=256, H=4, Hkv=2, f=512, dtype="bf16", base=500000.0, number=151, window=64)
+    _, w = dev_weights(cfg)
+    B, chunks, steps = 2, [70, 30], 120
+    T = sum(chunks) + steps
+    _, x = dev_x(cfg, B, T)
+    max_blocks = 64 // bs
+    n_blocks = B * max_blocks + 2
+    perm = np.random.default_rng(bs).permutation(n_blocks)[:B * max_blocks].reshape(B, max_blocks)
+    table = torch.from_numpy(perm.astype(np.int32)).cuda()
+    kp = torch.full((n_blocks, 2, bs, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vp = kp.clone()
+    print("case: paged ring", bs, flush=True)
+    got_p = _ring_run(cfg, x, chunks, steps, {"w": w}, paged=(kp, vp, table, bs, True))
+    ku, vu = new_cache(cfg, B, T)
+    got_u = _ring_run(cfg, x, chunks, steps, {"w": w, "kv": (ku, vu)})
+    assert np.array_equal(got_p, got_u)
+    free = np.setdiff1d(np.arange(n_blocks), perm.ravel())
+    assert np.isnan(widen_cache(kp)[free]).all()
+
+
+def test_model_with_ring_window_caches_matches_uncapped_bitwise():
+    """The model (prefill, then greedy decode far past the window) on bounded
+    window caches of W rows gives the logits and tokens of uncapped caches."""
+    import torch
+    import synth
+    from synth.configs import tensor_id
+    from tests.test_gpu_model import model_inputs
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=152, window=32)
+    L, V, B, T, steps = 2, 1024, 2, 50, 80
+    _, (ld, ed, gd, ud) = model_inputs(cfg, L, V)
+    tc = tfb.Config.of(cfg)
+    h = tfb.ModelHandle(tc, ld, ed, gd, ud)
+    rope = tfb.rope_table_init(tc, T + steps)
+    ids = torch.from_numpy(synth.integers(cfg.seed, tensor_id("ids"), (B, T), 0, V - 1)).cuda()
+    print("case: model ring caches", flush=True)
+    res = []
+    for ring, rows in ((True, 32), (False, T + steps)):
+        caches = [(torch.full((B, 2, rows, 128), float("nan"), dtype=torch.bfloat16, device="cuda"),
+                   torch.full((B, 2, rows, 128), float("nan"), dtype=torch.bfloat16, device="cuda"), ring)
+                  for _ in range(L)]
+        lens = torch.zeros(B, dtype=torch.int32, device="cuda")
+        nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+        lg = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
+        out = []
+        tfb.model_forward(h, rope, ids, caches, lens, 0, logits=lg, last_only=True, next_ids=nxt)
+        out.append(lg.clone())
+        for s in range(steps):
+            tfb.model_forward(h, rope, nxt.view(B, 1), caches, lens, T + s, logits=lg, next_ids=nxt)
+            out.append(lg.clone())
+        torch.cuda.synchronize()
+        res.append(torch.stack(out))
+    assert torch.equal(res[0], res[1])
+
+
+def test_kv_append_ring_slots():
+    """Rows appended to a bounded window cache land at slots p mod t_max."""
+    torch = _torch()
+    cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=153, window=8)
+    tc = tfb.Config.of(cfg)
+    B, n, t_max = 2, 5, 8
+    import synth
+    from tests.gpu_util import to_dev
+    kf, kb = synth.normal(cfg.seed, 11, (B, n, 2, 128), 1.0, True)
+    vf, vb = synth.normal(cfg.seed, 12, (B, n, 2, 128), 1.0, True)
+    start = np.array([3, 30], np.int32)
+    kc, vc = new_cache(cfg, B, t_max)
+    tfb.kv_append(tc, (kc, vc, True), to_dev(kf, kb), to_dev(vf, vb), torch.from_numpy(start).cuda(), int(start.max()))
+    torch.cuda.synchronize()
+    gk, gv = widen_cache(kc), widen_cache(vc)
+    for b in range(B):
+        written = set()
+        for t in range(n):
+            slot = (start[b] + t) % t_max
+            written.add(slot)
+            assert np.array_equal(gk[b, :, slot], kf[b, t]) and np.array_equal(gv[b, :, slot], vf[b, t])
+        for slot in set(range(t_max)) - written:
+            assert np.isnan(gk[b, :, slot]).all()

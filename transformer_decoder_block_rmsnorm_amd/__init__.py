@@ -39,12 +39,14 @@ class BlockWeights(ctypes.Structure):
 
 
 class KVCache(ctypes.Structure):
-    _fields_ = [("k", _VP), ("v", _VP), ("batch", ctypes.c_int32), ("t_max", ctypes.c_int32)]
+    _fields_ = [("k", _VP), ("v", _VP), ("batch", ctypes.c_int32), ("t_max", ctypes.c_int32),
+                ("ring", ctypes.c_int32)]
 
 
 class PagedKVCache(ctypes.Structure):
     _fields_ = [("k", _VP), ("v", _VP), ("block_table", _VP), ("batch", ctypes.c_int32),
-                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("n_blocks", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("n_blocks", ctypes.c_int32),
+                ("ring", ctypes.c_int32)]
 
 
 class Model(ctypes.Structure):
@@ -168,8 +170,10 @@ def weights_struct(w: dict) -> BlockWeights:
     return BlockWeights(*[_VP(w[n].data_ptr()) for n in WEIGHT_NAMES])
 
 
-def cache_struct(k, v) -> KVCache:
-    return KVCache(_VP(k.data_ptr()), _VP(v.data_ptr()), k.shape[0], k.shape[2])
+def cache_struct(k, v, ring: bool = False) -> KVCache:
+    """k, v: [B, Hkv, t_max, dh]; ring: a bounded window cache holding the last
+    t_max positions (position p in row p mod t_max)."""
+    return KVCache(_VP(k.data_ptr()), _VP(v.data_ptr()), k.shape[0], k.shape[2], 1 if ring else 0)
 
 
 def workspace_bytes(cfg: Config, B: int, T: int, vocab: int = 0) -> int:
@@ -238,10 +242,10 @@ def block_prefill_varlen(cfg: Config, w: dict, rope, x, out, start, lens, max_en
     return out
 
 
-def paged_cache_struct(k, v, table, block_size: int) -> PagedKVCache:
+def paged_cache_struct(k, v, table, block_size: int, ring: bool = False) -> PagedKVCache:
     """k, v: pools [n_blocks, Hkv, block_size, dh]; table: int32 [B, max_blocks] device tensor."""
     return PagedKVCache(_VP(k.data_ptr()), _VP(v.data_ptr()), _VP(table.data_ptr()), table.shape[0], block_size,
-                        table.shape[1], k.shape[0])
+                        table.shape[1], k.shape[0], 1 if ring else 0)
 
 
 def block_prefill_paged(cfg: Config, w: dict, rope, x, out, paged, start_pos: int = 0, ws=None):
@@ -318,7 +322,7 @@ def model_forward(h: ModelHandle, rope, ids, caches: list, lens, h_max_len: int,
     B, T = ids.shape
     if ws is None:
         ws = workspace(h.cfg, B, T, h.vocab)
-    kv = (KVCache * len(caches))(*[cache_struct(k, v) for k, v in caches])
+    kv = (KVCache * len(caches))(*[cache_struct(*c) for c in caches])
     ws_n = ws.numel() * ws.element_size()
     _check(lib().tfb_model_forward(ctypes.byref(h.m), _ptr(rope), rope.shape[0], _ptr(ids), B, T, kv, _ptr(lens),
                                    h_max_len, _ptr(logits), 1 if last_only else 0, _ptr(next_ids), _ptr(ws), ws_n,

@@ -43,8 +43,12 @@ WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab, size_t pa
     L.att = take(M * qd * es);
     L.r = take(M * c.d * sizeof(float));  // block-internal residual, fp32
     L.act = take(M * (size_t)c.d_ff * es);
-    L.kv_k = take(M * kvd * es);  // keys and values when no cache is given
-    L.kv_v = take(M * kvd * es);
+    // keys and values when no cache is given; with a sliding window, also the
+    // contiguous staging copy (chunk + the window's history) that a prefill
+    // into a bounded window cache works in
+    const size_t kv_rows = (c.window > 0 && T > 1) ? std::max(M, (size_t)B * ((size_t)T + c.window - 1)) : M;
+    L.kv_k = take(kv_rows * kvd * es);
+    L.kv_v = take(kv_rows * kvd * es);
     L.part_bytes =
         part_bytes == SIZE_MAX ? attention_decode_scratch_bytes(B, c.n_heads, c.head_dim, kMaxSplits) : part_bytes;
     L.part = take(L.part_bytes);
@@ -172,16 +176,16 @@ bool norms_fuse(const tfb_block_config &c, int M, const WsLayout &L) {
 }
 
 tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
-                     int max_pos, const void *x,
-                     void *out, int B, int T, int start, const int32_t *pos, void *kc, void *vc, int t_max,
-                     uint8_t *ws, const WsLayout &L, hipStream_t s, const int32_t *starts = nullptr,
-                     const int32_t *lens = nullptr, const KvMap *paged = nullptr, bool h_ready = false,
+                     int max_pos, const void *x, void *out, int B, int T, int start, const int32_t *pos, void *kc,
+                     void *vc, const KvMap &kvm, uint8_t *ws, const WsLayout &L, hipStream_t s,
+                     const int32_t *starts = nullptr, const int32_t *lens = nullptr, bool h_ready = false,
                      const void *next_g = nullptr) {
     // h_ready: h in the workspace already holds RMSNorm1(x) (written by the
     // previous layer's W2 step).  next_g: on the skinny path, the W2 step also
     // writes RMSNorm(out) with this gain into h for whoever reads h next.
-    // cache rows: contiguous [B, Hkv, t_max, dh], or a paged pool and block table
-    const KvMap kvm = paged ? *paged : KvMap{nullptr, t_max, 0, 0, 0};
+    // cache rows: contiguous [B, Hkv, t_max, dh], or a paged pool and block
+    // table; a bounded window cache is only ever passed here for decode
+    const int t_max = kvm.t_max;
     const int M = B * T, d = c.d, H = c.n_heads, Hkv = c.n_kv_heads, dh = c.head_dim, f = c.d_ff;
     const int qd = H * dh, kvd = Hkv * dh;
     void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
@@ -279,6 +283,46 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
         dn.norm_eps = c.rms_eps;
     }
     TRY_HIP(STAGE(ST_W2, gemm_launch(dn, s)));
+    return TFB_OK;
+}
+
+// Prefill of rows start .. start+T-1.  A bounded sliding-window cache (ring)
+// holds only the last `ring` positions.  When the chunk and the window's
+// history before it (hist positions) fit in the ring, every position the
+// call touches has its own slot and the block runs on the ring directly.
+// Otherwise the chunk's own rows would overwrite history that its earlier
+// rows still attend to, so the chunk works in a contiguous staging copy in
+// the workspace: the history is copied in, the block runs on the copy
+// exactly as on an uncapped cache, and the chunk's last rows go to their
+// ring slots at the end.
+tfb_status run_prefill(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
+                       const void *x, void *out, int B, int T, int start, void *kc, void *vc, const KvMap &kvm,
+                       uint8_t *ws, const WsLayout &L, hipStream_t s, bool h_ready = false,
+                       const void *next_g = nullptr) {
+    const int hist = kvm.ring ? std::min(start, c.window - 1) : 0;
+    if (!kvm.ring || (int64_t)T + hist <= kvm.ring)
+        return run_block(c, w, rope, rope_rows, 0, x, out, B, T, start, nullptr, kc, vc, kvm, ws, L, s, nullptr,
+                         nullptr, h_ready, next_g);
+    const KvMap stg{nullptr, T + hist, 0, 0, 0, start - hist, 0};
+    void *sk = ws + L.kv_k, *sv = ws + L.kv_v;
+    TRY_HIP(kv_copy_launch(c.dtype, kc, vc, kvm, sk, sv, stg, B, c.n_kv_heads, c.head_dim, start - hist, hist, s));
+    const tfb_status st = run_block(c, w, rope, rope_rows, 0, x, out, B, T, start, nullptr, sk, sv, stg, ws, L, s,
+                                    nullptr, nullptr, h_ready, next_g);
+    if (st != TFB_OK) return st;
+    const int n = std::min(T, kvm.ring);
+    TRY_HIP(kv_copy_launch(c.dtype, sk, sv, stg, kc, vc, kvm, B, c.n_kv_heads, c.head_dim, start + T - n, n, s));
+    return TFB_OK;
+}
+
+// Row map of a contiguous cache; a ring cache holds the last t_max positions.
+KvMap contig_map(const tfb_kv_cache &kv) { return KvMap{nullptr, kv.t_max, 0, 0, 0, 0, kv.ring ? kv.t_max : 0}; }
+
+// A bounded window cache needs a window no longer than the cache and rows the
+// staging copy moves in 16-byte pieces.
+tfb_status check_ring(const tfb_block_config &c, int ring, int capacity) {
+    if (!ring) return TFB_OK;
+    if (c.window <= 0 || capacity < c.window) return TFB_ERR_SHAPE;
+    if (c.dtype == TFB_F32 && c.head_dim % 4) return TFB_ERR_SHAPE;
     return TFB_OK;
 }
 
@@ -408,7 +452,8 @@ tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weight
     if (B <= 0 || T <= 0 || start_pos < 0) return TFB_ERR_SHAPE;
     if (cache) {
         if ((st = check_cache(cache, B)) != TFB_OK) return st;
-        if ((int64_t)start_pos + T > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
+        if ((st = check_ring(*cfg, cache->ring, cache->t_max)) != TFB_OK) return st;
+        if (!cache->ring && (int64_t)start_pos + T > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
     } else if (start_pos != 0) {
         return TFB_ERR_SHAPE;
     }
@@ -417,11 +462,11 @@ tfb_status tfb_block_prefill(const tfb_block_config *cfg, const tfb_block_weight
     if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
     if (!aligned(ws)) return TFB_ERR_ALIGN;
     uint8_t *wsb = (uint8_t *)ws;
-    void *kc = cache ? cache->k : (void *)(wsb + L.kv_k);
-    void *vc = cache ? cache->v : (void *)(wsb + L.kv_v);
-    const int t_max = cache ? cache->t_max : T;
-    return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, start_pos, nullptr, kc, vc, t_max, wsb, L,
-                     (hipStream_t)stream);
+    if (!cache)
+        return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, 0, nullptr, wsb + L.kv_k, wsb + L.kv_v,
+                         KvMap{nullptr, T, 0, 0, 0, 0, 0}, wsb, L, (hipStream_t)stream);
+    return run_prefill(*cfg, *w, rope_table, t_max_table, x, out, B, T, start_pos, cache->k, cache->v,
+                       contig_map(*cache), wsb, L, (hipStream_t)stream);
 }
 
 tfb_status tfb_block_prefill_varlen(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
@@ -435,12 +480,13 @@ tfb_status tfb_block_prefill_varlen(const tfb_block_config *cfg, const tfb_block
     if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
     if (B <= 0 || T <= 0 || h_max_end < 0) return TFB_ERR_SHAPE;
     if ((st = check_cache(cache, B)) != TFB_OK) return st;
+    if (cache->ring) return TFB_ERR_UNSUPPORTED;  // per-sequence starts would need per-sequence staging
     if (h_max_end > cache->t_max || h_max_end > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
     const WsLayout L = ws_layout(*cfg, B, T, 0);
     if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
     if (!aligned(ws)) return TFB_ERR_ALIGN;
     return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, 0, nullptr, cache->k, cache->v,
-                     cache->t_max, (uint8_t *)ws, L, (hipStream_t)stream, start, len);
+                     contig_map(*cache), (uint8_t *)ws, L, (hipStream_t)stream, start, len);
 }
 
 tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
@@ -453,12 +499,13 @@ tfb_status tfb_block_decode(const tfb_block_config *cfg, const tfb_block_weights
     if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
     if (B <= 0 || h_max_pos < 0) return TFB_ERR_SHAPE;
     if ((st = check_cache(cache, B)) != TFB_OK) return st;
-    if (h_max_pos >= cache->t_max || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    if ((st = check_ring(*cfg, cache->ring, cache->t_max)) != TFB_OK) return st;
+    if ((!cache->ring && h_max_pos >= cache->t_max) || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
     const WsLayout L = ws_layout(*cfg, B, 1, 0);
     if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
     if (!aligned(ws)) return TFB_ERR_ALIGN;
-    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v, cache->t_max, (uint8_t *)ws,
-                     L, (hipStream_t)stream);
+    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v,
+                     contig_map(*cache), (uint8_t *)ws, L, (hipStream_t)stream);
 }
 
 // ---- allocation-free decode: see scratch_on_current_device above ----
@@ -474,7 +521,8 @@ tfb_status tfb_block_decode_noalloc(const tfb_block_config *cfg, const tfb_block
     if (!aligned(rope_table) || !aligned(x) || !aligned(out)) return TFB_ERR_ALIGN;
     if (B <= 0 || h_max_pos < 0) return TFB_ERR_SHAPE;
     if ((st = check_cache(cache, B)) != TFB_OK) return st;
-    if (h_max_pos >= cache->t_max || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    if ((st = check_ring(*cfg, cache->ring, cache->t_max)) != TFB_OK) return st;
+    if ((!cache->ring && h_max_pos >= cache->t_max) || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
     // the decode-attention partials this call's chunk plan needs (the plan
     // is the one tfb_block_decode makes, so the launches are the same)
     AttnCall a{};
@@ -488,7 +536,7 @@ tfb_status tfb_block_decode_noalloc(const tfb_block_config *cfg, const tfb_block
     uint8_t *ws = nullptr;
     if ((st = scratch_on_current_device(&ws)) != TFB_OK) return st;
     return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v,
-                     cache->t_max, ws, L, (hipStream_t)stream);
+                     contig_map(*cache), ws, L, (hipStream_t)stream);
 }
 
 // Paged cache: validated host fields, and the row map the kernels use.
@@ -501,7 +549,8 @@ static tfb_status paged_map(const tfb_paged_kv_cache *pc, int B, KvMap &m) {
     int shift = 0;
     while ((1 << shift) < bs) ++shift;
     if ((int64_t)pc->max_blocks * bs > INT32_MAX) return TFB_ERR_SHAPE;
-    m = KvMap{pc->block_table, pc->max_blocks * bs, shift, pc->max_blocks, pc->n_blocks};
+    m = KvMap{pc->block_table, pc->max_blocks * bs, shift, pc->max_blocks, pc->n_blocks, 0,
+              pc->ring ? pc->max_blocks * bs : 0};
     return TFB_OK;
 }
 
@@ -517,12 +566,14 @@ tfb_status tfb_block_prefill_paged(const tfb_block_config *cfg, const tfb_block_
     if (B <= 0 || T <= 0 || start_pos < 0) return TFB_ERR_SHAPE;
     KvMap m;
     if ((st = paged_map(cache, B, m)) != TFB_OK) return st;
-    if ((int64_t)start_pos + T > m.t_max || (int64_t)start_pos + T > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    if ((st = check_ring(*cfg, m.ring, m.t_max)) != TFB_OK) return st;
+    if ((!m.ring && (int64_t)start_pos + T > m.t_max) || (int64_t)start_pos + T > t_max_table)
+        return TFB_ERR_CACHE_OVERFLOW;
     const WsLayout L = ws_layout(*cfg, B, T, 0);
     if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
     if (!aligned(ws)) return TFB_ERR_ALIGN;
-    return run_block(*cfg, *w, rope_table, t_max_table, 0, x, out, B, T, start_pos, nullptr, cache->k, cache->v,
-                     m.t_max, (uint8_t *)ws, L, (hipStream_t)stream, nullptr, nullptr, &m);
+    return run_prefill(*cfg, *w, rope_table, t_max_table, x, out, B, T, start_pos, cache->k, cache->v, m,
+                       (uint8_t *)ws, L, (hipStream_t)stream);
 }
 
 tfb_status tfb_block_decode_paged(const tfb_block_config *cfg, const tfb_block_weights *w, const float *rope_table,
@@ -537,12 +588,13 @@ tfb_status tfb_block_decode_paged(const tfb_block_config *cfg, const tfb_block_w
     if (B <= 0 || h_max_pos < 0) return TFB_ERR_SHAPE;
     KvMap m;
     if ((st = paged_map(cache, B, m)) != TFB_OK) return st;
-    if (h_max_pos >= m.t_max || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
+    if ((st = check_ring(*cfg, m.ring, m.t_max)) != TFB_OK) return st;
+    if ((!m.ring && h_max_pos >= m.t_max) || h_max_pos >= t_max_table) return TFB_ERR_CACHE_OVERFLOW;
     const WsLayout L = ws_layout(*cfg, B, 1, 0);
     if (!ws || ws_bytes < L.total) return TFB_ERR_WORKSPACE;
     if (!aligned(ws)) return TFB_ERR_ALIGN;
-    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v, m.t_max,
-                     (uint8_t *)ws, L, (hipStream_t)stream, nullptr, nullptr, &m);
+    return run_block(*cfg, *w, rope_table, t_max_table, h_max_pos, x, out, B, 1, 0, pos, cache->k, cache->v, m,
+                     (uint8_t *)ws, L, (hipStream_t)stream);
 }
 
 tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const void *k_new, const void *v_new,
@@ -554,9 +606,11 @@ tfb_status tfb_kv_append(const tfb_block_config *cfg, tfb_kv_cache *cache, const
     if (cache->batch <= 0) return TFB_ERR_SHAPE;
     if ((st = check_cache(cache, cache->batch)) != TFB_OK) return st;
     if (n_new <= 0 || h_max_start < 0) return TFB_ERR_SHAPE;
-    if ((int64_t)h_max_start + n_new > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
+    if ((st = check_ring(*cfg, cache->ring, cache->t_max)) != TFB_OK) return st;
+    // a ring takes at most t_max rows per call (more would share slots)
+    if (cache->ring ? n_new > cache->t_max : (int64_t)h_max_start + n_new > cache->t_max) return TFB_ERR_CACHE_OVERFLOW;
     hipStream_t s = (hipStream_t)stream;
-    const KvMap kvm{nullptr, cache->t_max, 0, 0, 0};
+    const KvMap kvm = contig_map(*cache);
     TRY_HIP(STAGE(ST_KV_APPEND, kv_append_launch(cfg->dtype, cache->k, cache->v, k_new, v_new, start, cache->batch,
                                                  n_new, cfg->n_kv_heads, cfg->head_dim, kvm, s)));
     return TFB_OK;
@@ -583,7 +637,8 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     for (int l = 0; l < model->n_layers; ++l) {
         if ((st = check_weights(&model->layers[l])) != TFB_OK) return st;
         if ((st = check_cache(&caches[l], B)) != TFB_OK) return st;
-        if ((int64_t)h_max_len + T > caches[l].t_max) return TFB_ERR_CACHE_OVERFLOW;
+        if ((st = check_ring(c, caches[l].ring, caches[l].t_max)) != TFB_OK) return st;
+        if (!caches[l].ring && (int64_t)h_max_len + T > caches[l].t_max) return TFB_ERR_CACHE_OVERFLOW;
     }
     if ((int64_t)h_max_len + T > t_max_table) return TFB_ERR_CACHE_OVERFLOW;
     const WsLayout L = ws_layout(c, B, T, model->vocab);
@@ -605,12 +660,13 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
         const bool last = l + 1 == model->n_layers;
         const void *next_g = !fuse ? nullptr : (last ? (final_fused ? model->g_final : nullptr) : model->layers[l + 1].g_attn);
         const bool h_ready = fuse && l > 0;
+        const KvMap kvm = contig_map(caches[l]);
         if (T > 1)
-            st = run_block(c, model->layers[l], rope_table, t_max_table, 0, cur, nxt, B, T, 0, nullptr, caches[l].k, caches[l].v,
-                           caches[l].t_max, wsb, L, s, nullptr, nullptr, nullptr, h_ready, next_g);
+            st = run_prefill(c, model->layers[l], rope_table, t_max_table, cur, nxt, B, T, 0, caches[l].k, caches[l].v,
+                             kvm, wsb, L, s, h_ready, next_g);
         else
-            st = run_block(c, model->layers[l], rope_table, t_max_table, h_max_len, cur, nxt, B, 1, 0, lens, caches[l].k, caches[l].v,
-                           caches[l].t_max, wsb, L, s, nullptr, nullptr, nullptr, h_ready, next_g);
+            st = run_block(c, model->layers[l], rope_table, t_max_table, h_max_len, cur, nxt, B, 1, 0, lens,
+                           caches[l].k, caches[l].v, kvm, wsb, L, s, nullptr, nullptr, h_ready, next_g);
         if (st != TFB_OK) return st;
         void *tmp = cur; cur = nxt; nxt = tmp;
     }

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
 
     if (a.lens && t >= a.lens[b]) return;  // padding row (after the only barrier)
     int p = a.pos ? a.pos[b] : (a.starts ? a.starts[b] : a.start) + t;
-    if (p >= a.t_max) p = a.t_max - 1;  // never read past the cache
+    // never read past the cache (a ring holds every position asked of it)
+    if (!a.kvm.ring && p - a.kvm.pos0 >= a.kvm.t_max) p = a.kvm.pos0 + a.kvm.t_max - 1;
     const int n_keys = p + 1;
     const int kvh = h / (a.H / a.Hkv);
     const T *K = (const T *)a.kc;
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     }
     const int qpos = start + t0 + lr;
     // cache row j of this sequence and KV head (a contiguous slab unless paged)
-    const int64_t slab = ((int64_t)b * a.Hkv + kvh) * a.t_max;
+    const int64_t slab = ((int64_t)b * a.Hkv + kvh) * a.t_max - a.kvm.pos0;
     auto row = [&](int j) -> int64_t { return PAGED ? kv_row(a.kvm, b, a.Hkv, kvh, j) : slab + j; };
 
     // Per-lane part of this wave's DMA blocks: block bi (K for bi < BLK/2,
@@ -228,7 +229,10 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + stg * (2 * TILE * 2) + wave * PER * 1024);
         // every row of the tile is a valid row, and (paged cache) the tile
         // lies in one pool block of at least BKV rows, whose rows for this KV
-        // head are consecutive: scalar base + fixed lane offsets
+        // head are consecutive: scalar base + fixed lane offsets.  (A paged
+        // ring has a multiple of the block size in slots, so an aligned tile
+        // never wraps; a contiguous ring has bs_shift 0 and takes the
+        // general path.)
         if ((!PAGED || (1 << a.kvm.bs_shift) >= BKV) && j0 >= key_floor && j0 + BKV <= kv_len) {
             const bf16_t *src = kv_src + row(j0) * DH;
 #pragma unroll
@@ -434,7 +438,9 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     // the whole grid resident at once (two single-group workgroups per CU):
     // split each workgroup's key range over two wave groups
     const bool two = blocks <= 2 * device_cus();
-    const bool paged = a.kvm.table != nullptr;
+    // a ring (bounded window cache) maps every row through kv_row, as a
+    // paged cache does; the caller guarantees the call's rows do not share slots
+    const bool paged = a.kvm.table != nullptr || a.kvm.ring != 0;
     const dim3 g(blocks), b1(256), b2(512);
     if (c.dh == 128) {
         if (paged) {
@@ -508,7 +514,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     // to the 8 XCDs in turn, are different (sequence, KV head) pairs of one
     // chunk index, so every XCD gets the same mix of long and empty chunks
     const int kvh = blockIdx.x, b = blockIdx.y, ch = blockIdx.z;
-    const int n_keys = min(a.pos[b] + 1, a.t_max);
+    const int n_keys = a.kvm.ring ? a.pos[b] + 1 : min(a.pos[b] + 1, a.kvm.pos0 + a.kvm.t_max);
     // keys [k_first, n_keys): all of them, or the last `window` ones
     const int k_first = a.window > 0 ? max(0, n_keys - a.window) : 0;
     const int k_begin = k_first + ch * a.chunk_keys;
@@ -532,21 +538,27 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     for (int c = 0; c < 8; ++c) oacc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int base = k_begin + wave * 64; base < k_end; base += 256) {
+        // cache row of key base + o, o < 64: the slot of `base` once, then a
+        // ring (bounded window cache) wraps by a compare
+        const int sbase = kv_slot(a.kvm, base);
+        auto row_at = [&](int o) -> int64_t {
+            int sl = sbase + o;
+            if (a.kvm.ring && sl >= a.kvm.ring) sl = sl - a.kvm.ring < a.kvm.ring ? sl - a.kvm.ring : sl % a.kvm.ring;
+            return kv_row_of_slot(a.kvm, b, a.Hkv, kvh, sl);
+        };
         u32x4 kw[NCH], vr[2][8];
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int r = RPI * i + lane / NCH, j = base + r;
-            kw[i] = (j < k_end) ? ld_stream(a.kc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + (lane % NCH) * 8)
-                                : u32x4{0, 0, 0, 0};
+            kw[i] = (j < k_end) ? ld_stream(a.kc + row_at(r) * DH + (lane % NCH) * 8) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 // slots 0-3: keys 32u + 4g + v; slots 4-7: keys 32u + 16 + 4g + v
-                const int j = base + 32 * u + 16 * (r >> 2) + 4 * g4 + (r & 3);
-                vr[u][r] = (v_lane && j < k_end) ? ld_stream(a.vc + kv_row(a.kvm, b, a.Hkv, kvh, j) * DH + ln * 8)
-                                                 : u32x4{0, 0, 0, 0};
+                const int o = 32 * u + 16 * (r >> 2) + 4 * g4 + (r & 3), j = base + o;
+                vr[u][r] = (v_lane && j < k_end) ? ld_stream(a.vc + row_at(o) * DH + ln * 8) : u32x4{0, 0, 0, 0};
             }
         bf16_t *ks = kst[wave];
 #pragma unroll
@@ -671,7 +683,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs a) {
     const int bh = blockIdx.x * 4 + wave;
     if (bh >= a.B * a.H) return;
     const int b = bh / a.H;
-    const int n_keys = min(a.pos[b] + 1, a.t_max);
+    const int n_keys = a.kvm.ring ? a.pos[b] + 1 : min(a.pos[b] + 1, a.kvm.pos0 + a.kvm.t_max);
     const int n_range = a.window > 0 ? min(n_keys, a.window) : n_keys;
     const int n_ch = min((n_range + a.chunk_keys - 1) / a.chunk_keys, a.max_chunks);
     const float *base = a.part + (int64_t)bh * a.max_chunks * (DH + 4);

@@ -132,25 +132,45 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
-// Where row j (absolute position) of sequence b, KV head g lives in a KV
-// cache, as a row index (the element offset is row * dh).
+// Where the key and value of absolute position j of sequence b, KV head g
+// live in a KV cache.  A position first maps to a slot of the sequence:
+//  - slot = j - pos0 (pos0 = 0 except for a prefill's staging copy, whose
+//    row 0 holds position pos0);
+//  - bounded sliding-window cache (ring > 0): slot = (j - pos0) mod ring, so
+//    the cache holds the last `ring` positions ([PID] "The Transformer",
+//    Sliding-window attention: with a window the KV cache is capped);
+// and a slot to a row (the element offset is row * dh):
 //  - contiguous cache [B, Hkv, t_max, dh] (table == NULL);
 //  - paged cache: a pool [n_blocks, Hkv, 2^bs_shift, dh] of fixed-size
 //    blocks, and a block table [B, max_blocks] giving the pool block of each
-//    logical block j >> bs_shift of a sequence (tirogla "Transformer block",
-//    Implementation notes: a KV cache allocated in fixed blocks per
+//    logical block slot >> bs_shift of a sequence (tirogla "Transformer
+//    block", Implementation notes: a KV cache allocated in fixed blocks per
 //    sequence).  A table entry outside [0, n_blocks) is clamped into it, so a
 //    bad table can give wrong values but never an access outside the pool.
 struct KvMap {
     const int32_t *table;
-    int t_max;        // rows per sequence (paged: max_blocks << bs_shift)
+    int t_max;        // slots per sequence (paged: max_blocks << bs_shift)
     int bs_shift, max_blocks, n_blocks;
+    int pos0;         // position held by slot 0 (no ring)
+    int ring;         // > 0: position j lives in slot (j - pos0) mod ring (ring == t_max)
 };
-__device__ __forceinline__ int64_t kv_row(const KvMap &m, int b, int Hkv, int g, int j) {
-    if (!m.table) return ((int64_t)b * Hkv + g) * m.t_max + j;
-    int blk = m.table[(int64_t)b * m.max_blocks + (j >> m.bs_shift)];
+__device__ __forceinline__ int kv_slot(const KvMap &m, int j) {
+    const int s = j - m.pos0;  // callers pass j >= pos0
+    return m.ring ? s % m.ring : s;
+}
+// Whether position j has a slot (writes outside the cache are skipped).
+__device__ __forceinline__ bool kv_has(const KvMap &m, int j) {
+    const int s = j - m.pos0;
+    return s >= 0 && (m.ring || s < m.t_max);
+}
+__device__ __forceinline__ int64_t kv_row_of_slot(const KvMap &m, int b, int Hkv, int g, int s) {
+    if (!m.table) return ((int64_t)b * Hkv + g) * m.t_max + s;
+    int blk = m.table[(int64_t)b * m.max_blocks + (s >> m.bs_shift)];
     blk = min(max(blk, 0), m.n_blocks - 1);
-    return (((int64_t)blk * Hkv + g) << m.bs_shift) + (j & ((1 << m.bs_shift) - 1));
+    return (((int64_t)blk * Hkv + g) << m.bs_shift) + (s & ((1 << m.bs_shift) - 1));
+}
+__device__ __forceinline__ int64_t kv_row(const KvMap &m, int b, int Hkv, int g, int j) {
+    return kv_row_of_slot(m, b, Hkv, g, kv_slot(m, j));
 }
 
 // ---- LDS staging helpers (gfx950) ----------------------------------------

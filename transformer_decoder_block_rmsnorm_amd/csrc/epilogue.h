@@ -86,7 +86,7 @@ __device__ __forceinline__ void epi_store_pair(const EpiParams &p, int m, int c,
             Elem<T>::store(q, iq, v0);
             Elem<T>::store(q, iq + 1, v1);
         } else {
-            if (ps < 0 || ps >= p.t_max) return;  // never write outside the cache
+            if (!kv_has(p.kvm, ps)) return;  // never write outside the cache
             if (p.lens && t >= p.lens[b]) return;  // padding rows leave the cache alone
             int cc = c - qd;
             T *dst = (T *)p.kc;
@@ -185,7 +185,7 @@ __device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, con
             const int h = c / p.dh, e = c - h * p.dh;
             store_bf16x8((bf16_t *)p.q + (((int64_t)b * p.H + h) * p.T + t) * p.dh + e, w);
         } else {
-            if (ps < 0 || ps >= p.t_max) return;  // never write outside the cache
+            if (!kv_has(p.kvm, ps)) return;  // never write outside the cache
             if (p.lens && t >= p.lens[b]) return;  // padding rows leave the cache alone
             int cc = c - qd;
             bf16_t *dst = (bf16_t *)p.kc;

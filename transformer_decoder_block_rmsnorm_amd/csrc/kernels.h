@@ -78,6 +78,10 @@ size_t attention_decode_call_bytes(const AttnCall &a);
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
                             int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s);
+// Keys and values of positions p_lo .. p_lo+n-1 from one cache map to another
+// (row width dh in the storage type must be a multiple of 16 bytes).
+hipError_t kv_copy_launch(int dtype, const void *sk, const void *sv, const KvMap &sm, void *dk, void *dv,
+                          const KvMap &dm, int B, int Hkv, int dh, int p_lo, int n, hipStream_t s);
 hipError_t embed_launch(int dtype, const int32_t *ids, const void *table, void *x, int64_t rows, int d, int vocab,
                         hipStream_t s);
 // Copy row (T-1) of each sequence of x [B, T, d] into y [B, d].

@@ -145,9 +145,9 @@ hipError_t rope_table_launch(int t_max, int dh, double base, float *table, hipSt
 }
 
 // KV append ([TIR] How it works, KV cache): [B, n, Hkv, dh] -> cache rows
-// start[b] + t.  One thread per pair of elements (dh is even, so a pair never
-// straddles a row and every pair is 4- or 8-byte aligned); rows outside
-// [0, t_max) are skipped.
+// start[b] + t (or their ring slots).  One thread per pair of elements (dh is even, so a pair never
+// straddles a row and every pair is 4- or 8-byte aligned); positions the
+// cache has no slot for are skipped.
 template <typename T>
 __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const int32_t *start, int B, int n_new,
                                  int Hkv, int dh, KvMap kvm) {
@@ -163,7 +163,7 @@ __global__ void kv_append_kernel(T *kc, T *vc, const T *kn, const T *vn, const i
     const int t = (int)(r % n_new);
     const int b = (int)(r / n_new);
     const int p = start[b] + t;
-    if (p < 0 || p >= kvm.t_max) return;
+    if (!kv_has(kvm, p)) return;
     const int64_t src = (((int64_t)b * n_new + t) * Hkv + g) * dh + e2 * 2;
     const int64_t dst = kv_row(kvm, b, Hkv, g, p) * dh + e2 * 2;
     *(Pair *)(kc + dst) = *(const Pair *)(kn + src);
@@ -180,6 +180,37 @@ hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, co
     else
         hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, (float *)kc, (float *)vc,
                            (const float *)k_new, (const float *)v_new, start, B, n_new, Hkv, dh, kvm);
+    return hipGetLastError();
+}
+
+// Copy the keys and values of positions p_lo .. p_lo+n-1 of every sequence
+// and KV head between two caches with different row maps (a bounded window
+// cache and the contiguous staging copy a prefill works in).  16-byte chunks;
+// a position either map has no slot for is skipped.
+__global__ void kv_copy_kernel(const uint8_t *sk, const uint8_t *sv, KvMap sm, uint8_t *dk, uint8_t *dv, KvMap dm,
+                               int B, int Hkv, int row_bytes, int p_lo, int n) {
+    const int chunks = row_bytes / 16;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)B * Hkv * n * chunks) return;
+    const int c = (int)(idx % chunks);
+    int64_t r = idx / chunks;
+    const int p = p_lo + (int)(r % n);
+    r /= n;
+    const int g = (int)(r % Hkv), b = (int)(r / Hkv);
+    if (!kv_has(sm, p) || !kv_has(dm, p)) return;
+    const int64_t so = kv_row(sm, b, Hkv, g, p) * row_bytes + c * 16, d = kv_row(dm, b, Hkv, g, p) * row_bytes + c * 16;
+    *(u32x4 *)(dk + d) = *(const u32x4 *)(sk + so);
+    *(u32x4 *)(dv + d) = *(const u32x4 *)(sv + so);
+}
+
+hipError_t kv_copy_launch(int dtype, const void *sk, const void *sv, const KvMap &sm, void *dk, void *dv,
+                          const KvMap &dm, int B, int Hkv, int dh, int p_lo, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int row_bytes = dh * (dtype == TFB_BF16 ? 2 : 4);
+    if (row_bytes % 16) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)B * Hkv * n * (row_bytes / 16);
+    hipLaunchKernelGGL(kv_copy_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, (const uint8_t *)sk,
+                       (const uint8_t *)sv, sm, (uint8_t *)dk, (uint8_t *)dv, dm, B, Hkv, row_bytes, p_lo, n);
     return hipGetLastError();
 }
 
