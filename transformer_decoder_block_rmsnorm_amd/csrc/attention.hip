@@ -140,8 +140,13 @@ __device__ __forceinline__ int v_granule_swz(int key) {
     else return key & 3;
 }
 
-template <int DH, bool PAGED, int NGRP>
+// Cache row map of the flash kernel: a contiguous slab per (sequence, KV
+// head), a paged pool, or a ring (bounded window cache, contiguous or paged).
+enum FlashMap { FM_CONTIG = 0, FM_PAGED = 1, FM_RING = 2 };
+
+template <int DH, int MAP, int NGRP>
 __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(FlashArgs a) {
+    constexpr bool PAGED = MAP != FM_CONTIG;  // rows through the map, one by one
     constexpr int BKV = 64;                    // keys per tile
     constexpr int NS = DH / 16;                // 16-wide dh slices of q.k
     constexpr int NE = DH / 32;                // 32-row e tiles of O^T
@@ -203,7 +208,11 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     const int qpos = start + t0 + lr;
     // cache row j of this sequence and KV head (a contiguous slab unless paged)
     const int64_t slab = ((int64_t)b * a.Hkv + kvh) * a.t_max - a.kvm.pos0;
-    auto row = [&](int j) -> int64_t { return PAGED ? kv_row(a.kvm, b, a.Hkv, kvh, j) : slab + j; };
+    auto row = [&](int j) -> int64_t {
+        if constexpr (MAP == FM_CONTIG) return slab + j;
+        else if constexpr (MAP == FM_PAGED) return kv_row_of_slot(a.kvm, b, a.Hkv, kvh, j - a.kvm.pos0);
+        else return kv_row(a.kvm, b, a.Hkv, kvh, j);
+    };
 
     // Per-lane part of this wave's DMA blocks: block bi (K for bi < BLK/2,
     // then V) holds keys RPB*(bi % (BLK/2)) .. +RPB-1; lane slot -> key and
@@ -440,25 +449,23 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
     const bool two = blocks <= 2 * device_cus();
     // a ring (bounded window cache) maps every row through kv_row, as a
     // paged cache does; the caller guarantees the call's rows do not share slots
-    const bool paged = a.kvm.table != nullptr || a.kvm.ring != 0;
     const dim3 g(blocks), b1(256), b2(512);
+    const int map = a.kvm.ring ? FM_RING : (a.kvm.table ? FM_PAGED : FM_CONTIG);
+#define TFB_FLASH(DH, MAP)                                                                          \
+    do {                                                                                           \
+        if (two) hipLaunchKernelGGL((flash_prefill_kernel<DH, MAP, 2>), g, b2, 0, s, a);           \
+        else hipLaunchKernelGGL((flash_prefill_kernel<DH, MAP, 1>), g, b1, 0, s, a);               \
+    } while (0)
     if (c.dh == 128) {
-        if (paged) {
-            if (two) hipLaunchKernelGGL((flash_prefill_kernel<128, true, 2>), g, b2, 0, s, a);
-            else hipLaunchKernelGGL((flash_prefill_kernel<128, true, 1>), g, b1, 0, s, a);
-        } else {
-            if (two) hipLaunchKernelGGL((flash_prefill_kernel<128, false, 2>), g, b2, 0, s, a);
-            else hipLaunchKernelGGL((flash_prefill_kernel<128, false, 1>), g, b1, 0, s, a);
-        }
+        if (map == FM_RING) TFB_FLASH(128, FM_RING);
+        else if (map == FM_PAGED) TFB_FLASH(128, FM_PAGED);
+        else TFB_FLASH(128, FM_CONTIG);
     } else {
-        if (paged) {
-            if (two) hipLaunchKernelGGL((flash_prefill_kernel<64, true, 2>), g, b2, 0, s, a);
-            else hipLaunchKernelGGL((flash_prefill_kernel<64, true, 1>), g, b1, 0, s, a);
-        } else {
-            if (two) hipLaunchKernelGGL((flash_prefill_kernel<64, false, 2>), g, b2, 0, s, a);
-            else hipLaunchKernelGGL((flash_prefill_kernel<64, false, 1>), g, b1, 0, s, a);
-        }
+        if (map == FM_RING) TFB_FLASH(64, FM_RING);
+        else if (map == FM_PAGED) TFB_FLASH(64, FM_PAGED);
+        else TFB_FLASH(64, FM_CONTIG);
     }
+#undef TFB_FLASH
     return hipGetLastError();
 }
 
@@ -485,7 +492,7 @@ struct DecArgs {
     float scale_log2e;
 };
 
-template <int DH, int G>
+template <int DH, int G, bool RING>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     // Per wave, 64 keys at a time on MFMA 16x16x32 (lane l: column l%16,
     // k group g = l/16):
@@ -538,13 +545,18 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     for (int c = 0; c < 8; ++c) oacc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     for (int base = k_begin + wave * 64; base < k_end; base += 256) {
-        // cache row of key base + o, o < 64: the slot of `base` once, then a
-        // ring (bounded window cache) wraps by a compare
-        const int sbase = kv_slot(a.kvm, base);
+        // cache row of key base + o, o < 64.  A ring (bounded window cache):
+        // the slot of `base` once, then a wrap by a compare
+        int sbase = base;
+        if constexpr (RING) sbase = kv_slot(a.kvm, base);
         auto row_at = [&](int o) -> int64_t {
-            int sl = sbase + o;
-            if (a.kvm.ring && sl >= a.kvm.ring) sl = sl - a.kvm.ring < a.kvm.ring ? sl - a.kvm.ring : sl % a.kvm.ring;
-            return kv_row_of_slot(a.kvm, b, a.Hkv, kvh, sl);
+            if constexpr (RING) {
+                int sl = sbase + o;
+                if (sl >= a.kvm.ring) sl = sl - a.kvm.ring < a.kvm.ring ? sl - a.kvm.ring : sl % a.kvm.ring;
+                return kv_row_of_slot(a.kvm, b, a.Hkv, kvh, sl);
+            } else {
+                return kv_row_of_slot(a.kvm, b, a.Hkv, kvh, base + o - a.kvm.pos0);
+            }
         };
         u32x4 kw[NCH], vr[2][8];
 #pragma unroll
@@ -736,19 +748,23 @@ size_t decode_part_bytes(int B, int H, int dh, int max_chunks) {
     return (size_t)B * H * max_chunks * (dh + 4) * sizeof(float);
 }
 
-template <int DH>
-static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s) {
+template <int DH, bool RING>
+static hipError_t decode_launch_g(const AttnCall &c, DecArgs &a, hipStream_t s) {
     const int G = c.H / c.Hkv;
     dim3 grid(c.Hkv, c.B, a.max_chunks);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_attn_kernel<DH, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_attn_kernel<DH, 4>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_attn_kernel<DH, 8>), grid, dim3(256), 0, s, a); break;
-        case 16: hipLaunchKernelGGL((decode_attn_kernel<DH, 16>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_attn_kernel<DH, 1, RING>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2, RING>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_attn_kernel<DH, 4, RING>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_attn_kernel<DH, 8, RING>), grid, dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((decode_attn_kernel<DH, 16, RING>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+template <int DH>
+static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s) {
+    return c.kvm.ring ? decode_launch_g<DH, true>(c, a, s) : decode_launch_g<DH, false>(c, a, s);
 }
 
 // Arguments of the split decode kernels for one call.

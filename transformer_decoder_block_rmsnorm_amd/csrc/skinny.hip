@@ -6,8 +6,10 @@
 //
 // Work unit = one 4-wave workgroup: a BN-column block of W (BN = 64 or 128)
 // times a range of k, split only as far as needed to give every compute unit
-// a workgroup.  Stages of 64 k rows of the weight block, plus the same 64
-// columns of x (64 rows, rows past M clamped), go from global memory straight
+// a workgroup.  Stages of SK k rows of the weight block, plus the same SK
+// columns of the rows of x the MFMA row tiles cover (16 per tile, rows past M
+// clamped; SK = 128 when a 64-row stage of those rows would not split into
+// whole 1 KB blocks per wave), go from global memory straight
 // into a ring of LDS stages (global_load_lds_dwordx4 with the nontemporal
 // policy), so the loads in flight cost no registers and the ring keeps
 // several stages of HBM reads outstanding.  Each wave owns BN/4 output columns: its weight fragments come
@@ -70,7 +72,7 @@ template <int BN, int SK, int MT>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     // SK: k rows per stage
     constexpr int WST = SK * BN;               // weight elements per stage
-    constexpr int XST = 64 * SK;               // x elements per stage (64 rows)
+    constexpr int XST = 16 * MT * SK;          // x elements per stage (the rows of the MT row tiles)
     constexpr int STAGE = WST + XST;
     constexpr int NST = (144 * 1024) / (STAGE * 2) < 16 ? (144 * 1024) / (STAGE * 2) : 16;  // ring stages
     constexpr int WBLK = WST * 2 / 1024, XBLK = XST * 2 / 1024;  // 1 KB blocks
@@ -79,9 +81,9 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     constexpr int CPR = BN / 8;                // 16-byte chunks per weight row
     constexpr int NC = BN / 64;                // 16-column tiles per wave
     constexpr int XCH = SK / 8;                // 16-byte chunks per x row
-    constexpr int XRPL = 8 / XCH;              // x rows per 128 bytes
+    constexpr int XRPL = XCH >= 8 ? 1 : 8 / XCH;  // x rows per 128 bytes (at least one)
     static_assert(PW * 4 == WBLK && PX * 4 == XBLK && WRPB >= 1, "stage splits into 1 KB blocks per wave");
-    static_assert(NST >= 3 && (SK == 32 || SK == 64), "ring depth and x row layout");
+    static_assert(NST >= 3 && (SK == 32 || SK == 64 || SK == 128), "ring depth and x row layout");
     __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;
 
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int i = 0; i < PX; ++i) {
         // x rows of 2 SK bytes; chunk XOR (row / XRPL) keeps the 16-lane fragment reads conflict free
-        const int row = (wave * PX + i) * (64 / XCH) + lane / XCH, p = lane % XCH;
+        const int row = (wave * PX + i) * (64 / XCH) + lane / XCH, p = lane % XCH;  // row < 16 MT
         xsrc[i] = a.x + (int64_t)min(row, a.M - 1) * a.ldx + st_lo * SK + 8 * (p ^ ((row / XRPL) & (XCH - 1)));
     }
     auto issue = [&](int st, int slot) {
@@ -331,27 +333,37 @@ __global__ __launch_bounds__(NT) void skinny_reduce_norm_kernel(const float *par
 // allows (each workgroup also streams its x slice, 64/BN of its weight bytes),
 // then k is split so that the workgroups come close to one per compute unit
 // without exceeding it.
-static void skinny_plan(int K, int N, int &bn, int &splits) {
+// Stage depth by row tiles: the x part of a stage (16 MT rows of SK k) must
+// split into whole 1 KB blocks over the four waves.
+constexpr int skinny_sk(int mt) { return (mt == 1 || mt == 3) ? 128 : 64; }
+// Row tiles a launch uses: one more than M needs when K does not take
+// 128-deep stages (the extra tile holds clamped copies of the last row).
+static int skinny_mt(int M, int K) {
+    int mt = (M + 15) / 16;
+    if ((mt == 1 || mt == 3) && K % 128) ++mt;
+    return mt;
+}
+
+static void skinny_plan(int M, int K, int N, int &bn, int &splits) {
     bn = N % 128 == 0 ? 128 : 64;
     const int n_cb = N / bn;
-    splits = std::max(1, std::min(device_cus() / n_cb, K / 64));
+    splits = std::max(1, std::min(device_cus() / n_cb, K / skinny_sk(skinny_mt(M, K))));
     splits = std::min(splits, kSkinnyMaxSplits);
 }
 
 size_t skinny_part_bytes(int M, int K, int N) {
     int bn, splits;
-    skinny_plan(K, N, bn, splits);
+    skinny_plan(M, K, N, bn, splits);
     return (size_t)splits * M * N * sizeof(float);
 }
 
-template <int BN, int SK>
+template <int BN>
 static void skinny_launch_bn(const SkinnyArgs &a, int blocks, hipStream_t s) {
-    const int mt = (a.M + 15) / 16;
-    switch (mt) {
-        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 1>), dim3(blocks), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 2>), dim3(blocks), dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 3>), dim3(blocks), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, SK, 4>), dim3(blocks), dim3(256), 0, s, a); break;
+    switch (skinny_mt(a.M, a.K)) {
+        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(1), 1>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(2), 2>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(3), 3>), dim3(blocks), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(4), 4>), dim3(blocks), dim3(256), 0, s, a); break;
     }
 }
 
@@ -372,7 +384,7 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     for (int i = 0; i < 3; ++i)
         if (a.w[i] && a.w_cols[i] % 64) return hipErrorInvalidValue;
     int bn;
-    skinny_plan(a.K, a.N, bn, a.splits);
+    skinny_plan(a.M, a.K, a.N, bn, a.splits);
     if (a.splits > kSkinnyMaxSplits) return hipErrorInvalidValue;  // the reduce passes hold at most this many
     if ((size_t)a.splits * a.M * a.N * sizeof(float) > part_bytes) return hipErrorInvalidValue;
     a.part = (float *)part;
@@ -383,8 +395,8 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
         a.ld_act = c.ep.ldo;
     }
     const int blocks = (a.N / bn) * a.splits;
-    if (bn == 128) skinny_launch_bn<128, 64>(a, blocks, s);
-    else skinny_launch_bn<64, 64>(a, blocks, s);
+    if (bn == 128) skinny_launch_bn<128>(a, blocks, s);
+    else skinny_launch_bn<64>(a, blocks, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     if (c.norm_g) {
