@@ -196,6 +196,132 @@ __device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, con
     }
 }
 
+// What the epilogue of one 8-column group reads from memory besides the
+// accumulators: the residual (EPI_RESID) or the RoPE (cos, sin) pairs and the
+// row's position (EPI_QKV).  Loading it apart from the store lets a caller
+// issue the loads of its next rows before it stores the current ones.
+struct EpiPre {
+    f32x4 a, b;  // RESID: fp32 residual columns 0..3 and 4..7, or the 16 bytes of the bf16 residual in a;
+                 // QKV: table entries of pairs 0..1 (a) and 2..3 (b), each (cos, sin)
+    int ps;      // QKV: position of the row
+};
+
+// Whole-tile fast path.  In a tile that lies wholly inside the output with
+// 16-byte groups (p.vec8), a lane keeps the same 8-column group over all of
+// its rows, so what depends on the column is computed once (EpiLane), and
+// its rows only move forward, so the row's sequence and token are carried
+// along instead of divided out for every group.
+struct EpiLane {
+    int c;          // first column of the group
+    int part, head, e;  // QKV: 0 q, 1 k, 2 v; head within that part; offset in the head
+    int b, t;       // QKV: sequence and token of the lane's current row
+    int m;          // that row
+};
+
+template <int KIND>
+__device__ __forceinline__ void epi_lane_init(const EpiParams &p, int c, int m, EpiLane &L) {
+    L.c = c;
+    L.m = m;
+    if constexpr (KIND == EPI_QKV) {
+        const int qd = p.H * p.dh, kvd = p.Hkv * p.dh;
+        int cc = c;
+        L.part = cc < qd ? 0 : (cc < qd + kvd ? 1 : 2);
+        cc -= L.part == 0 ? 0 : (L.part == 1 ? qd : qd + kvd);
+        L.head = cc / p.dh;
+        L.e = cc - L.head * p.dh;
+        L.b = m / p.T;
+        L.t = m - L.b * p.T;
+    }
+}
+
+// Move the lane to row m (m >= the current row).
+template <int KIND>
+__device__ __forceinline__ void epi_lane_seek(const EpiParams &p, int m, EpiLane &L) {
+    if constexpr (KIND == EPI_QKV) {
+        L.t += m - L.m;
+        while (L.t >= p.T) { L.t -= p.T; ++L.b; }
+    }
+    L.m = m;
+}
+
+template <int KIND>
+__device__ __forceinline__ void epi_load8_lane(const EpiParams &p, const EpiLane &L, EpiPre &pre) {
+    if constexpr (KIND == EPI_RESID) {
+        const int64_t ir = (int64_t)L.m * p.ldr + L.c;
+        if (p.res_f32) {
+            pre.a = *(const f32x4 *)((const float *)p.res + ir);
+            pre.b = *(const f32x4 *)((const float *)p.res + ir + 4);
+        } else {
+            pre.a = __builtin_bit_cast(f32x4, *(const u32x4 *)((const bf16_t *)p.res + ir));
+        }
+    } else if constexpr (KIND == EPI_QKV) {
+        pre.ps = p.pos ? p.pos[L.b] : (p.starts ? p.starts[L.b] : p.start) + L.t;
+        if (L.part < 2) {
+            const int pr = min(max(pre.ps, 0), p.rope_rows - 1);
+            const f32x4 *cs = (const f32x4 *)(p.rope + ((int64_t)pr * (p.dh >> 1) + (L.e >> 1)) * 2);
+            pre.a = cs[0];
+            pre.b = cs[1];
+        }
+    }
+}
+
+template <int KIND>
+__device__ __forceinline__ void epi_store8_lane(const EpiParams &p, const EpiLane &L, const float (&v)[8],
+                                                const EpiPre &pre) {
+    if constexpr (KIND == EPI_SWIGLU) {
+        store_bf16x8((bf16_t *)p.out + (int64_t)L.m * p.ldo + L.c, v);
+    } else if constexpr (KIND == EPI_RESID) {
+        const int64_t io = (int64_t)L.m * p.ldo + L.c;
+        float r[8];
+        if (p.res_f32) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { r[k] = pre.a[k]; r[k + 4] = pre.b[k]; }
+        } else {
+            const u32x4 w = __builtin_bit_cast(u32x4, pre.a);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[2 * k] = bf16_lo(w[k]);
+                r[2 * k + 1] = bf16_hi(w[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r[k] += v[k];
+        if (p.out_f32) {
+            float *o = (float *)p.out + io;
+            *(f32x4 *)o = f32x4{r[0], r[1], r[2], r[3]};
+            *(f32x4 *)(o + 4) = f32x4{r[4], r[5], r[6], r[7]};
+        } else {
+            store_bf16x8((bf16_t *)p.out + io, r);
+        }
+    } else if constexpr (KIND == EPI_F32) {
+        float *o = (float *)p.out + (int64_t)L.m * p.ldo + L.c;
+        *(f32x4 *)o = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4 *)(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    } else if constexpr (KIND == EPI_QKV) {
+        float w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = v[k];
+        if (L.part < 2) {
+            // RoPE on the four pairs of the group ([TIR] Code, rope; never on v)
+            const float co[4] = {pre.a[0], pre.a[2], pre.b[0], pre.b[2]}, si[4] = {pre.a[1], pre.a[3], pre.b[1], pre.b[3]};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float a = v[2 * k], bb = v[2 * k + 1];
+                w[2 * k] = a * co[k] - bb * si[k];
+                w[2 * k + 1] = a * si[k] + bb * co[k];
+            }
+        }
+        if (L.part == 0) {
+            store_bf16x8((bf16_t *)p.q + (((int64_t)L.b * p.H + L.head) * p.T + L.t) * p.dh + L.e, w);
+        } else {
+            if (!kv_has(p.kvm, pre.ps)) return;  // never write outside the cache
+            if (p.lens && L.t >= p.lens[L.b]) return;  // padding rows leave the cache alone
+            bf16_t *dst = (bf16_t *)(L.part == 1 ? p.kc : p.vc);
+            store_bf16x8(dst + kv_row(p.kvm, L.b, p.Hkv, L.head, pre.ps) * p.dh + L.e, w);
+        }
+    }
+}
+
 // SwiGLU epilogue: one logical column c of act.
 template <typename T>
 __device__ __forceinline__ void epi_store_swiglu(const EpiParams &p, int m, int c, float gate, float up) {
