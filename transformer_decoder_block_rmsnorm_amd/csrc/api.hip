@@ -193,6 +193,20 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     if (!h_ready) TRY_HIP(STAGE(ST_RMSNORM_ATTN, rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s)));
     const bool fuse = norms_fuse(c, M, L);
 
+    AttnCall a{};
+    a.dtype = c.dtype;
+    a.q = q; a.kc = kc; a.vc = vc; a.o = att; a.pos = pos;
+    a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.dh = dh; a.t_max = t_max; a.start = start;
+    a.starts = starts;
+    a.lens = lens;
+    a.kvm = kvm;
+    a.scale = 1.0f / sqrtf((float)dh);
+    a.partials = ws + L.part;
+    a.partial_bytes = L.part_bytes;
+    a.max_keys = pos ? max_pos + 1 : start + T;
+    a.max_splits = kMaxSplits;
+    a.window = c.window;
+
     GemmCall g{};
     g.dtype = c.dtype;
     g.epi = EPI_QKV;
@@ -218,21 +232,20 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.scratch_bytes = L.skinny_bytes;
     g.split_scratch = L.gsplit_bytes ? ws + L.gsplit : nullptr;
     g.split_bytes = L.gsplit_bytes;
+    // decode on the split attention kernel: the QKV GEMM leaves its split-K
+    // partials, and the attention kernel reduces them (q, RoPE, the new cache
+    // rows) instead of a separate reduce pass
+    int qkv_splits = 0;
+    if (pos && attention_decode_takes_qkv_partials(a)) g.qkv_deferred_splits = &qkv_splits;
     TRY_HIP(STAGE(ST_QKV, gemm_launch(g, s)));
+    if (qkv_splits > 0) {
+        a.qkv_part = (const float *)g.scratch;
+        a.qkv_splits = qkv_splits;
+        a.qkv_n = g.ep.N;
+        a.rope = rope;
+        a.rope_rows = rope_rows;
+    }
 
-    AttnCall a{};
-    a.dtype = c.dtype;
-    a.q = q; a.kc = kc; a.vc = vc; a.o = att; a.pos = pos;
-    a.B = B; a.T = T; a.H = H; a.Hkv = Hkv; a.dh = dh; a.t_max = t_max; a.start = start;
-    a.starts = starts;
-    a.lens = lens;
-    a.kvm = kvm;
-    a.scale = 1.0f / sqrtf((float)dh);
-    a.partials = ws + L.part;
-    a.partial_bytes = L.part_bytes;
-    a.max_keys = pos ? max_pos + 1 : start + T;
-    a.max_splits = kMaxSplits;
-    a.window = c.window;
     TRY_HIP(STAGE(ST_ATTN, pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s)));
     if (pos) TRY_HIP(STAGE(ST_ATTN_COMBINE, attention_decode_merge_launch(a, s)));
 

@@ -490,9 +490,43 @@ struct DecArgs {
     int window;       // keys per query (0: full causal)
     KvMap kvm;        // cache row addressing
     float scale_log2e;
+    // QKV split-K partials [splits][B][qkv_n] (NULL: q and the new rows are
+    // in place); see AttnCall
+    const float *qkv_part;
+    int qkv_splits, qkv_n;
+    const float *rope;
+    int rope_rows;
 };
 
-template <int DH, int G, bool RING>
+// Sum of the QKV partials of columns c, c+1 of sequence b, in split order
+// (as the reduce pass adds them).  Every split is loaded before any is
+// added: with the count known only at run time, a plain loop would wait for
+// each load in turn.
+constexpr int kQkvMaxSplits = 16;
+__device__ __forceinline__ float2 qkv_pair_sum(const DecArgs &a, int b, int c) {
+    const float *p = a.qkv_part + (int64_t)b * a.qkv_n + c;
+    const int64_t stride = (int64_t)a.B * a.qkv_n;
+    float2 t[kQkvMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kQkvMaxSplits; ++s)
+        if (s < a.qkv_splits) t[s] = *(const float2 *)(p + s * stride);
+    float v0 = 0.0f, v1 = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kQkvMaxSplits; ++s)
+        if (s < a.qkv_splits) {
+            v0 += t[s].x;
+            v1 += t[s].y;
+        }
+    return make_float2(v0, v1);
+}
+// RoPE of the pair (e, e+1) of a head at position ps ([TIR] Code, rope).
+__device__ __forceinline__ float2 rope_pair(const DecArgs &a, int dh, int ps, int e, float2 v) {
+    const int pr = min(max(ps, 0), a.rope_rows - 1);
+    const float2 cs = ((const float2 *)a.rope)[(int64_t)pr * (dh >> 1) + (e >> 1)];
+    return make_float2(v.x * cs.x - v.y * cs.y, v.x * cs.y + v.y * cs.x);
+}
+
+template <int DH, int G, bool RING, bool QKV>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     // Per wave, 64 keys at a time on MFMA 16x16x32 (lane l: column l%16,
     // k group g = l/16):
@@ -507,12 +541,17 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     //                                 transposed 8x8 in registers; output
     //                                 column n of tile c is e = 8n + c.
     // Heads are MFMA columns: G <= 16 (unused columns are zero).
+    // QKV: a.qkv_part holds the QKV projection's split-K partials; this
+    // kernel builds q and the new key and value rows from them.
     static_assert(G <= 16, "at most 16 query heads per KV head");
     constexpr int NS = DH / 32;        // 32-wide dh slices
     constexpr int NCH = DH / 8;        // 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) float red_o[4][G][DH];
     __shared__ float red_ml[4][G][2];
     __shared__ __attribute__((aligned(16))) bf16_t kst[4][64 * DH];  // per wave: 64 K rows
+    // QKV: the new key and value row, and q, built from the partials
+    __shared__ __attribute__((aligned(16))) bf16_t newkv[QKV ? 2 : 1][QKV ? DH : 8];
+    __shared__ __attribute__((aligned(16))) bf16_t qsh[QKV ? G : 1][QKV ? DH : 8];
     constexpr int RPI = 64 / NCH;  // K rows per whole-row load instruction
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -528,13 +567,54 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
     if (k_begin >= n_keys) return;  // whole block leaves before any barrier
     const int k_end = min(n_keys, k_begin + a.chunk_keys);
     const int h0 = kvh * G;
+    const int pos_b = a.pos[b];
+    // with the QKV partials: this workgroup holds the new key (position
+    // pos[b]) when its chunk ends there and the cache has a row for it
+    const bool has_new = QKV && k_end == pos_b + 1 && kv_has(a.kvm, pos_b);
 
+    if constexpr (QKV) {
+        // q of the G heads and (the workgroup holding position pos[b]) the
+        // new key and value row, one pair of columns per item: summed over
+        // the splits, rotated, rounded to bf16 as the reduce pass does.  All
+        // items' partials are loaded before anything is stored.
+        constexpr int NQ = G * (DH / 2), NIT = (NQ + DH + 255) / 256;
+        float2 sum[NIT];
+#pragma unroll
+        for (int k = 0; k < NIT; ++k) {
+            const int i = tid + 256 * k, j = i - NQ;
+            const bool item = i < NQ || (has_new && j < DH);
+            const int col = i < NQ ? (h0 + i / (DH / 2)) * DH + 2 * (i % (DH / 2))
+                                   : a.H * DH + (j / (DH / 2)) * a.Hkv * DH + kvh * DH + 2 * (j % (DH / 2));
+            sum[k] = item ? qkv_pair_sum(a, b, col) : make_float2(0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int k = 0; k < NIT; ++k) {
+            const int i = tid + 256 * k, j = i - NQ;
+            if (i < NQ) {
+                const int hh = i / (DH / 2), e = 2 * (i % (DH / 2));
+                const float2 r = rope_pair(a, DH, pos_b, e, sum[k]);
+                const uint32_t w = pack_bf16x2(r.x, r.y);
+                *(uint32_t *)&qsh[hh][e] = w;
+                if (ch == 0) *(uint32_t *)((bf16_t *)a.q + ((int64_t)b * a.H + h0 + hh) * DH + e) = w;  // q in the workspace
+            } else if (has_new && j < DH) {
+                const int kv = j / (DH / 2), e = 2 * (j % (DH / 2));
+                const float2 r = kv == 0 ? rope_pair(a, DH, pos_b, e, sum[k]) : sum[k];
+                const uint32_t w = pack_bf16x2(r.x, r.y);
+                *(uint32_t *)&newkv[kv][e] = w;
+                bf16_t *dst = (bf16_t *)(kv == 0 ? a.kc : a.vc);
+                *(uint32_t *)(dst + kv_row(a.kvm, b, a.Hkv, kvh, pos_b) * DH + e) = w;
+            }
+        }
+        __syncthreads();  // q and the new row are in LDS for every wave
+    }
     // Q^T operand: column = head ln, k slots = dh chunk 4s + g4
     bf16x8 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         u32x4 v = {0, 0, 0, 0};
-        if (ln < G) v = *(const u32x4 *)(a.q + ((int64_t)b * a.H + h0 + ln) * DH + (4 * s + g4) * 8);
+        if (ln < G)
+            v = QKV ? *(const u32x4 *)&qsh[ln][(4 * s + g4) * 8]
+                    : *(const u32x4 *)(a.q + ((int64_t)b * a.H + h0 + ln) * DH + (4 * s + g4) * 8);
         qf[s] = as_bf16x8(v);
     }
     const bool v_lane = ln < NCH;  // dh = 64 uses half the output columns
@@ -577,6 +657,20 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecArgs a) {
         for (int i = 0; i < NCH; ++i) {
             const int r = RPI * i + lane / NCH, c = lane % NCH;
             *(u32x4 *)(ks + r * DH + ((c ^ (r & (NCH - 1))) * 8)) = kw[i];
+        }
+        // the new key and value (their cache rows are being written by this
+        // workgroup): key row pos[b] - base of this tile, if it is here
+        const int rn = pos_b - base;
+        if (QKV && has_new && rn >= 0 && rn < 64) {
+            asm volatile("");
+            if (lane < NCH) *(u32x4 *)(ks + rn * DH + ((lane ^ (rn & (NCH - 1))) * 8)) = *(const u32x4 *)&newkv[0][lane * 8];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int o = 32 * u + 16 * (r >> 2) + 4 * g4 + (r & 3);
+                    if (v_lane && o == rn) vr[u][r] = *(const u32x4 *)&newkv[1][ln * 8];
+                }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -748,23 +842,25 @@ size_t decode_part_bytes(int B, int H, int dh, int max_chunks) {
     return (size_t)B * H * max_chunks * (dh + 4) * sizeof(float);
 }
 
-template <int DH, bool RING>
+template <int DH, bool RING, bool QKV>
 static hipError_t decode_launch_g(const AttnCall &c, DecArgs &a, hipStream_t s) {
     const int G = c.H / c.Hkv;
     dim3 grid(c.Hkv, c.B, a.max_chunks);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_attn_kernel<DH, 1, RING>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2, RING>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_attn_kernel<DH, 4, RING>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_attn_kernel<DH, 8, RING>), grid, dim3(256), 0, s, a); break;
-        case 16: hipLaunchKernelGGL((decode_attn_kernel<DH, 16, RING>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_attn_kernel<DH, 1, RING, QKV>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_attn_kernel<DH, 2, RING, QKV>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_attn_kernel<DH, 4, RING, QKV>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_attn_kernel<DH, 8, RING, QKV>), grid, dim3(256), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((decode_attn_kernel<DH, 16, RING, QKV>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 template <int DH>
 static hipError_t decode_launch_dh(const AttnCall &c, DecArgs &a, hipStream_t s) {
-    return c.kvm.ring ? decode_launch_g<DH, true>(c, a, s) : decode_launch_g<DH, false>(c, a, s);
+    if (c.qkv_part)
+        return c.kvm.ring ? decode_launch_g<DH, true, true>(c, a, s) : decode_launch_g<DH, false, true>(c, a, s);
+    return c.kvm.ring ? decode_launch_g<DH, true, false>(c, a, s) : decode_launch_g<DH, false, false>(c, a, s);
 }
 
 // Arguments of the split decode kernels for one call.
@@ -796,6 +892,11 @@ static bool split_decode_args(const AttnCall &c, DecArgs &a) {
     a.max_chunks = chunks;
     a.kvm = c.kvm;
     a.scale_log2e = c.scale * 1.4426950408889634f;
+    a.qkv_part = c.qkv_part;
+    a.qkv_splits = c.qkv_splits;
+    a.qkv_n = c.qkv_n;
+    a.rope = c.rope;
+    a.rope_rows = c.rope_rows;
     return decode_part_bytes(c.B, c.H, c.dh, chunks) <= c.partial_bytes;
 }
 
@@ -838,6 +939,12 @@ hipError_t attention_decode_merge_launch(const AttnCall &a, hipStream_t s) {
 }
 size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits) {
     return decode_part_bytes(B, H, dh, max_splits);
+}
+// Only for few (sequence, KV head) pairs: there the reduce pass is a launch
+// of its own for little work, while with many pairs every workgroup of the
+// attention grid would rebuild q from the partials at its start.
+bool attention_decode_takes_qkv_partials(const AttnCall &a) {
+    return split_decode_applies(a) && 2 * (int64_t)a.B * a.Hkv <= device_cus();
 }
 size_t attention_decode_call_bytes(const AttnCall &a) {
     if (!split_decode_applies(a)) return 0;

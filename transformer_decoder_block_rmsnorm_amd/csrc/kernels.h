@@ -27,6 +27,11 @@ struct GemmCall {
     const void *norm_g;
     void *norm_out;
     float norm_eps;
+    // EPI_QKV on the skinny path: when set, the split-K partials are left for
+    // the decode attention kernel to reduce (no reduce pass is launched) and
+    // the split count goes here; other paths leave it untouched (the caller
+    // starts it at 0).
+    int *qkv_deferred_splits;
 };
 constexpr int kSkinnyNormMaxN = 8192;
 // Compute units of the current device (queried once per device; 256 if the
@@ -66,6 +71,15 @@ struct AttnCall {
     int max_splits;       // chunks per (b, h) the partial buffer holds
     int window;           // sliding window: keys per query (0: full causal)
     KvMap kvm;            // cache row addressing (contiguous or paged)
+    // decode only: the QKV projection's split-K partials [splits][B][qkv_n]
+    // (NULL: q and the new cache rows are already in place).  The attention
+    // kernel then sums them in split order, applies RoPE from `rope`
+    // ([rope_rows][dh/2] (cos, sin)), writes q to `q` and the new key and
+    // value rows to the cache, as the QKV reduce pass would.
+    const float *qkv_part;
+    int qkv_splits, qkv_n;
+    const float *rope;
+    int rope_rows;
 };
 hipError_t attention_prefill_launch(const AttnCall &a, hipStream_t s);
 hipError_t attention_decode_launch(const AttnCall &a, hipStream_t s);
@@ -75,6 +89,9 @@ size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits);
 // Partial-buffer bytes the decode kernels use for this call (its chunk count),
 // never more than attention_decode_scratch_bytes(B, H, dh, a.max_splits).
 size_t attention_decode_call_bytes(const AttnCall &a);
+// Whether attention_decode_launch runs the split MFMA kernel for this call
+// (the one that can take the QKV partials in place of the reduce pass).
+bool attention_decode_takes_qkv_partials(const AttnCall &a);
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
                             int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s);

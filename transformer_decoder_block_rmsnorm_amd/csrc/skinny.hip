@@ -399,6 +399,10 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     else skinny_launch_bn<64>(a, blocks, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
+    if (c.epi == EPI_QKV && c.qkv_deferred_splits) {  // the decode attention kernel reduces them
+        *c.qkv_deferred_splits = a.splits;
+        return hipSuccess;
+    }
     if (c.norm_g) {
         // the caller skips its own norm launch, so a norm that cannot be fused is an error
         if (c.epi != EPI_RESID || n_out > kSkinnyNormMaxN || n_out % 8 || !c.norm_out) return hipErrorInvalidValue;
