@@ -215,7 +215,10 @@ def test_gqa_equals_mha_with_repeated_kv():
 
 def test_decode_over_nan_tail_and_ragged_positions(oracle):
     """Sequences at different positions decode together; cache rows beyond
-    pos[b] hold NaN and must never influence the result."""
+    pos[b] hold NaN and must never influence the result.  With few
+    (sequence, KV head) pairs the attention kernel builds q and the new cache
+    rows from the QKV partials itself, so q (left in the workspace) and both
+    appended rows are checked too."""
     torch = _torch()
     for cfg in (C1, small_cfg(d=512, H=4, Hkv=1, f=1024, dtype="bf16", number=89)):
         tc = tfb.Config.of(cfg)
@@ -240,7 +243,8 @@ def test_decode_over_nan_tail_and_ragged_positions(oracle):
         pos = torch.tensor(lens, dtype=torch.int32, device="cuda")
         xd = torch.stack([x[b, lens[b]] for b in range(B)])[:, None].contiguous()
         o = torch.empty_like(xd)
-        tfb.block_decode(tc, w, rope, xd, o, (kc, vc), pos, max(lens))
+        ws = tfb.workspace(tc, B, 1)
+        tfb.block_decode(tc, w, rope, xd, o, (kc, vc), pos, max(lens), ws=ws)
         torch.cuda.synchronize()
         xd32 = np.stack([x32[b, lens[b]] for b in range(B)])[:, None]
         ref, inter = oracle.block_forward(cfg, w32, xd32, start=np.array(lens, np.int32), kc=okc, vc=ovc,
@@ -253,6 +257,11 @@ def test_decode_over_nan_tail_and_ragged_positions(oracle):
             assert np.isnan(gk[b, :, lens[b] + 1:]).all()
         check_cache("appended k rows", cfg, np.stack([gk[b, :, lens[b]] for b in range(B)]),
                     cache_rows(inter["k_pre"], cfg.n_kv_heads)[:, :, 0])
+        gv = widen_cache(vc)
+        check_cache("appended v rows", cfg, np.stack([gv[b, :, lens[b]] for b in range(B)]),
+                    cache_rows(inter["v_pre"], cfg.n_kv_heads)[:, :, 0])
+        q = to_np(tfb.workspace_view(tc, ws, B, 1, "q")).reshape(B, 1, cfg.d)
+        check("q (after RoPE)", q, inter["q_pre"], tol(cfg))
 
 
 def test_kv_append_bit_exact(oracle):
