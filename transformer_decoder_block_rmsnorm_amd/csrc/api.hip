@@ -247,7 +247,23 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     }
 
     TRY_HIP(STAGE(ST_ATTN, pos ? attention_decode_launch(a, s) : attention_prefill_launch(a, s)));
-    if (pos) TRY_HIP(STAGE(ST_ATTN_COMBINE, attention_decode_merge_launch(a, s)));
+    // with few (sequence, KV head) pairs the Wo GEMM merges the attention's
+    // chunk partials itself, under its first weight loads, instead of a
+    // separate merge pass
+    AttnChunks chunks{};
+    bool wo_merges = false;
+    if (pos && attention_decode_takes_qkv_partials(a) && c.dtype == TFB_BF16 && M <= kSkinnyMaxM && L.skinny_bytes &&
+        skinny_takes_attn_chunks(M, qd, d) && attention_decode_chunks(a, &chunks.chunk_keys, &chunks.max_chunks)) {
+        chunks.part = (const float *)a.partials;
+        chunks.pos = pos;
+        chunks.H = H;
+        chunks.dh = dh;
+        chunks.window = c.window;
+        chunks.kvm = kvm;
+        chunks.att_out = att;
+        wo_merges = true;
+    }
+    if (pos && !wo_merges) TRY_HIP(STAGE(ST_ATTN_COMBINE, attention_decode_merge_launch(a, s)));
 
     GemmCall o{};
     o.dtype = c.dtype;
@@ -255,6 +271,7 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     o.A = att; o.lda = qd; o.M = M; o.K = qd;
     o.w[0] = w.wo; o.w_cols[0] = d;
     o.ep.M = M; o.ep.N = d; o.ep.out = r; o.ep.ldo = d; o.ep.res = x; o.ep.ldr = d; o.ep.out_f32 = 1;
+    if (wo_merges) o.attn_chunks = &chunks;
     o.scratch = g.scratch;
     o.scratch_bytes = g.scratch_bytes;
     o.split_scratch = g.split_scratch;

@@ -946,6 +946,14 @@ size_t attention_decode_scratch_bytes(int B, int H, int dh, int max_splits) {
 bool attention_decode_takes_qkv_partials(const AttnCall &a) {
     return split_decode_applies(a) && 2 * (int64_t)a.B * a.Hkv <= device_cus();
 }
+bool attention_decode_chunks(const AttnCall &a, int *chunk_keys, int *max_chunks) {
+    if (!split_decode_applies(a)) return false;
+    DecArgs d;
+    if (!split_decode_args(a, d)) return false;
+    *chunk_keys = d.chunk_keys;
+    *max_chunks = d.max_chunks;
+    return true;
+}
 size_t attention_decode_call_bytes(const AttnCall &a) {
     if (!split_decode_applies(a)) return 0;
     DecArgs d;

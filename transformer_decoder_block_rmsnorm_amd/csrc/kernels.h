@@ -8,6 +8,17 @@
 
 namespace tfb {
 
+// Decode attention's chunk partials as the activations of the Wo GEMM: the
+// skinny kernel merges them itself (what the chunk merge pass computes) and
+// writes the merged rows to att_out for later readers of the workspace.
+struct AttnChunks {
+    const float *part;     // [B][H][max_chunks][dh + 4]: (m, l, -, -, o[dh])
+    const int32_t *pos;    // [B] decode positions
+    int H, dh, chunk_keys, max_chunks, window;
+    KvMap kvm;             // for the key count of each sequence
+    void *att_out;         // [B, H*dh] bf16
+};
+
 struct GemmCall {
     int dtype;             // TFB_F32 / TFB_BF16
     int epi;               // EpiKind
@@ -32,6 +43,9 @@ struct GemmCall {
     // the split count goes here; other paths leave it untouched (the caller
     // starts it at 0).
     int *qkv_deferred_splits;
+    // EPI_RESID on the skinny path only: the activations A are the decode
+    // attention's chunk partials (see skinny_takes_attn_chunks); A is unused
+    const AttnChunks *attn_chunks;
 };
 constexpr int kSkinnyNormMaxN = 8192;
 // Compute units of the current device (queried once per device; 256 if the
@@ -45,6 +59,10 @@ size_t gemm_split_bytes(int M, int N_virtual, int K);
 constexpr int kSkinnyMaxM = 64;
 hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, hipStream_t s);
 size_t skinny_part_bytes(int M, int K, int N);
+// Whether the skinny GEMM of this shape can take its activations as decode
+// attention chunk partials (one 16-row tile, a k range of at most 512 per
+// workgroup).
+bool skinny_takes_attn_chunks(int M, int K, int N);
 
 // y[m] = x[m] * rsqrt(mean(x[m]^2) + eps) * g, rows of width d.
 // x_f32: the input rows are fp32 (the block-internal residual) whatever the storage type.
@@ -92,6 +110,9 @@ size_t attention_decode_call_bytes(const AttnCall &a);
 // Whether attention_decode_launch runs the split MFMA kernel for this call
 // (the one that can take the QKV partials in place of the reduce pass).
 bool attention_decode_takes_qkv_partials(const AttnCall &a);
+// The split decode kernel's chunking of this call (what the chunk merge and
+// AttnChunks readers index by); false when the split kernel does not run.
+bool attention_decode_chunks(const AttnCall &a, int *chunk_keys, int *max_chunks);
 
 hipError_t kv_append_launch(int dtype, void *kc, void *vc, const void *k_new, const void *v_new, const int32_t *start,
                             int B, int n_new, int Hkv, int dh, const KvMap &kvm, hipStream_t s);

@@ -40,7 +40,12 @@ struct SkinnyArgs {
     float *part;      // [splits][M][N]
     bf16_t *act;      // src 2 with one k range: SiLU(gate) * up written here directly, row stride ld_act
     int64_t ld_act;
+    AttnChunks ac;    // XC kernels: x is the merge of these decode attention partials
 };
+
+// XC kernels: the k range of a workgroup is at most this many columns, so its
+// whole activation slice sits in LDS beside a weight-only ring.
+constexpr int kSkinnyXcMaxK = 512;
 
 // Column c of the virtual B -> (matrix, column).  Concat: matrices side by
 // side.  Dual: w1 and w3 interleaved in 16-column groups (virtual columns
@@ -68,14 +73,17 @@ __device__ __forceinline__ int skinny_gswz(int row) {
     else return row & 3;
 }
 
-template <int BN, int SK, int MT>
+template <int BN, int SK, int MT, bool XC>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
-    // SK: k rows per stage
+    // SK: k rows per stage.  XC: x is not loaded but built in LDS, once, from
+    // the decode attention's chunk partials (a.ac), for the whole k range.
     constexpr int WST = SK * BN;               // weight elements per stage
     constexpr int XST = 16 * MT * SK;          // x elements per stage (the rows of the MT row tiles)
-    constexpr int STAGE = WST + XST;
-    constexpr int NST = (144 * 1024) / (STAGE * 2) < 16 ? (144 * 1024) / (STAGE * 2) : 16;  // ring stages
-    constexpr int WBLK = WST * 2 / 1024, XBLK = XST * 2 / 1024;  // 1 KB blocks
+    constexpr int STAGE = XC ? WST : WST + XST;
+    constexpr int XFULL = XC ? 16 * MT * kSkinnyXcMaxK : 0;  // XC: the activation slice
+    constexpr int RING = 144 * 1024 - XFULL * 2;
+    constexpr int NST = RING / (STAGE * 2) < 16 ? RING / (STAGE * 2) : 16;  // ring stages
+    constexpr int WBLK = WST * 2 / 1024, XBLK = XC ? 0 : XST * 2 / 1024;  // 1 KB blocks
     constexpr int PW = WBLK / 4, PX = XBLK / 4, PER = PW + PX;   // DMAs per wave per stage
     constexpr int WRPB = 1024 / (BN * 2);      // weight rows per 1 KB block
     constexpr int CPR = BN / 8;                // 16-byte chunks per weight row
@@ -84,7 +92,8 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
     constexpr int XRPL = XCH >= 8 ? 1 : 8 / XCH;  // x rows per 128 bytes (at least one)
     static_assert(PW * 4 == WBLK && PX * 4 == XBLK && WRPB >= 1, "stage splits into 1 KB blocks per wave");
     static_assert(NST >= 3 && (SK == 32 || SK == 64 || SK == 128), "ring depth and x row layout");
-    __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
+    static_assert(!XC || MT == 1, "the activation slice is one 16-row tile");
+    __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE + XFULL];
     const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void_t *)lds;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
         wld[i] = ld;
         wsrc[i] = base + (int64_t)(st_lo * SK + row) * ld;
     }
-    const bf16_t *xsrc[PX];
+    const bf16_t *xsrc[PX > 0 ? PX : 1];
 #pragma unroll
     for (int i = 0; i < PX; ++i) {
         // x rows of 2 SK bytes; chunk XOR (row / XRPL) keeps the 16-lane fragment reads conflict free
@@ -148,11 +157,79 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (s < n_st) issue(s, s);
+    bf16_t *const xfull = lds + NST * STAGE;
+    if constexpr (XC) {
+        // The activation slice, while the first weight stages load: row b,
+        // columns st_lo*SK .. of att, merged from the chunk partials as the
+        // merge pass does it (max, then the weighted sums in chunk order, one
+        // division), rounded to bf16 and laid out per stage as the DMA would
+        // have put it.  Rows past M repeat row M-1.
+        const AttnChunks &ac = a.ac;
+        const int kr = n_st * SK, groups = kr / 8;
+        for (int it = tid; it < a.M * groups; it += 256) {
+            const int b = it / groups, gq = it % groups;
+            const int c0 = st_lo * SK + 8 * gq, h = c0 / ac.dh, e0 = c0 % ac.dh;
+            const int pos = ac.pos[b];
+            const int n_keys = ac.kvm.ring ? pos + 1 : min(pos + 1, ac.kvm.pos0 + ac.kvm.t_max);
+            const int n_range = ac.window > 0 ? min(n_keys, ac.window) : n_keys;
+            const int n_ch = min((n_range + ac.chunk_keys - 1) / ac.chunk_keys, ac.max_chunks);
+            const float *base = ac.part + ((int64_t)b * ac.H + h) * ac.max_chunks * (ac.dh + 4);
+            float M = -INFINITY, L = 0.0f, O[8] = {};
+            if (n_ch <= 16) {
+                float pm[16], pl[16];
+                f32x4 pa[16], pb[16];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const float *p = base + c * (ac.dh + 4);
+                    const bool in = c < n_ch;
+                    pm[c] = in ? p[0] : -INFINITY;
+                    pl[c] = in ? p[1] : 0.0f;
+                    pa[c] = in ? *(const f32x4 *)(p + 4 + e0) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    pb[c] = in ? *(const f32x4 *)(p + 8 + e0) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+#pragma unroll
+                for (int c = 0; c < 16; ++c) M = fmaxf(M, pm[c]);
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    if (c < n_ch) {
+                        const float sc = __builtin_amdgcn_exp2f(pm[c] - M);
+                        L += sc * pl[c];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            O[i] += sc * pa[c][i];
+                            O[i + 4] += sc * pb[c][i];
+                        }
+                    }
+                }
+            } else {
+                for (int c = 0; c < n_ch; ++c) M = fmaxf(M, base[c * (ac.dh + 4)]);
+                for (int c = 0; c < n_ch; ++c) {
+                    const float *p = base + c * (ac.dh + 4);
+                    const float sc = __builtin_amdgcn_exp2f(p[0] - M);
+                    L += sc * p[1];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) O[i] += sc * p[4 + e0 + i];
+                }
+            }
+            const float inv = 1.0f / L;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = O[i] * inv;
+            const u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7])};
+            const int sl = (8 * gq) / SK, ch = ((8 * gq) % SK) / 8;
+            for (int r = b; r < 16 * MT; r += (b == a.M - 1 ? 1 : 16 * MT)) {
+                *(u32x4 *)(xfull + sl * XST + r * SK + 8 * (ch ^ ((r / XRPL) & (XCH - 1)))) = w;
+            }
+            if (cb == 0) *(u32x4 *)((bf16_t *)ac.att_out + (int64_t)b * ac.H * ac.dh + c0) = w;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's slice writes are done (the loop's first barrier publishes them)
+    }
     for (int st = 0; st < n_st; ++st) {
         wait_stages(min(NST - 2, n_st - 1 - st));  // stage st landed
         asm volatile("s_barrier" ::: "memory");    // every wave's did; stage st-1's slot is free
         if (st + NST - 1 < n_st) issue(st + NST - 1, (st + NST - 1) % NST);
-        const bf16_t *Ws = lds + (st % NST) * STAGE, *Xs = Ws + WST;
+        const bf16_t *Ws = lds + (st % NST) * STAGE, *Xs = XC ? xfull + st * XST : Ws + WST;
 #pragma unroll
         for (int ks = 0; ks < SK / 32; ++ks) {
             bf16x8 bf[NC], af[MT];
@@ -357,13 +434,25 @@ size_t skinny_part_bytes(int M, int K, int N) {
     return (size_t)splits * M * N * sizeof(float);
 }
 
+bool skinny_takes_attn_chunks(int M, int K, int N) {
+    if (M < 1 || M > kSkinnyMaxM || K % 64 || N % 64 || skinny_mt(M, K) != 1) return false;
+    int bn, splits;
+    skinny_plan(M, K, N, bn, splits);
+    const int n_st = K / skinny_sk(1);
+    return (n_st + splits - 1) / splits * skinny_sk(1) <= kSkinnyXcMaxK;  // the longest k range of a workgroup
+}
+
 template <int BN>
-static void skinny_launch_bn(const SkinnyArgs &a, int blocks, hipStream_t s) {
+static void skinny_launch_bn(const SkinnyArgs &a, int blocks, hipStream_t s, bool xc) {
+    if (xc) {  // one 16-row tile (checked by skinny_takes_attn_chunks)
+        hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(1), 1, true>), dim3(blocks), dim3(256), 0, s, a);
+        return;
+    }
     switch (skinny_mt(a.M, a.K)) {
-        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(1), 1>), dim3(blocks), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(2), 2>), dim3(blocks), dim3(256), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(3), 3>), dim3(blocks), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(4), 4>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(1), 1, false>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(2), 2, false>), dim3(blocks), dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(3), 3, false>), dim3(blocks), dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((skinny_gemm_kernel<BN, skinny_sk(4), 4, false>), dim3(blocks), dim3(256), 0, s, a); break;
     }
 }
 
@@ -381,6 +470,16 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
     // the stage and block layout needs whole 64-row stages and 64-column
     // blocks, 16-byte aligned rows of x, and every matrix a multiple of 64 wide
     if (a.M < 1 || a.M > 64 || a.K % 64 || a.N % 64 || a.ldx % 8) return hipErrorInvalidValue;
+    // x from the decode attention's chunk partials: one 16-row tile, short
+    // k ranges, a plain residual GEMM over the head outputs (K = H * dh)
+    const bool xc = c.attn_chunks != nullptr;
+    if (xc) {
+        const AttnChunks &ac = *c.attn_chunks;
+        if (c.epi != EPI_RESID || !skinny_takes_attn_chunks(a.M, a.K, a.N) || a.K != ac.H * ac.dh || ac.dh % 8 ||
+            !ac.part || !ac.pos || !ac.att_out || ac.chunk_keys < 1 || ac.max_chunks < 1)
+            return hipErrorInvalidValue;
+        a.ac = ac;
+    }
     for (int i = 0; i < 3; ++i)
         if (a.w[i] && a.w_cols[i] % 64) return hipErrorInvalidValue;
     int bn;
@@ -395,8 +494,8 @@ hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, 
         a.ld_act = c.ep.ldo;
     }
     const int blocks = (a.N / bn) * a.splits;
-    if (bn == 128) skinny_launch_bn<128>(a, blocks, s);
-    else skinny_launch_bn<64>(a, blocks, s);
+    if (bn == 128) skinny_launch_bn<128>(a, blocks, s, xc);
+    else skinny_launch_bn<64>(a, blocks, s, xc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     if (c.epi == EPI_QKV && c.qkv_deferred_splits) {  // the decode attention kernel reduces them
