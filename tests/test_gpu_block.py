@@ -217,8 +217,9 @@ def test_decode_over_nan_tail_and_ragged_positions(oracle):
     """Sequences at different positions decode together; cache rows beyond
     pos[b] hold NaN and must never influence the result.  With few
     (sequence, KV head) pairs the attention kernel builds q and the new cache
-    rows from the QKV partials itself, so q (left in the workspace) and both
-    appended rows are checked too."""
+    rows from the QKV partials, and the Wo GEMM merges the attention's chunk
+    partials, so q and att (left in the workspace) and both appended rows are
+    checked too."""
     torch = _torch()
     for cfg in (C1, small_cfg(d=512, H=4, Hkv=1, f=1024, dtype="bf16", number=89)):
         tc = tfb.Config.of(cfg)
@@ -262,6 +263,8 @@ def test_decode_over_nan_tail_and_ragged_positions(oracle):
                     cache_rows(inter["v_pre"], cfg.n_kv_heads)[:, :, 0])
         q = to_np(tfb.workspace_view(tc, ws, B, 1, "q")).reshape(B, 1, cfg.d)
         check("q (after RoPE)", q, inter["q_pre"], tol(cfg))
+        att = to_np(tfb.workspace_view(tc, ws, B, 1, "att"))
+        check("att (head outputs)", att, inter["att_pre"], tol(cfg))
 
 
 def test_kv_append_bit_exact(oracle):
