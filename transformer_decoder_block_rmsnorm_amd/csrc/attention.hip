@@ -479,7 +479,8 @@ static hipError_t flash_launch(const AttnCall &c, hipStream_t s) {
 // merges the chunks of a (b, h) with log-sum-exp weights.  Keys at or beyond
 // pos[b] + 1 are never loaded.
 // ---------------------------------------------------------------------------
-constexpr int kDecChunk = 512;  // keys per workgroup (multiple of 256)
+constexpr int kDecChunk = 768;       // keys per workgroup (multiple of 256)
+constexpr int kDecChunkFew = 256;    // ... when (sequence, KV head) pairs are few
 
 struct DecArgs {
     const bf16_t *q, *kc, *vc;
@@ -872,16 +873,17 @@ static bool split_decode_args(const AttnCall &c, DecArgs &a) {
     a.pos = c.pos;
     a.part = (float *)c.partials;
     a.B = c.B; a.H = c.H; a.Hkv = c.Hkv; a.t_max = c.t_max;
-    // chunk size: kDecChunk keys; half of that when (sequence, KV head)
-    // pairs are few, so that a small batch still spreads over the CUs; grown
-    // in steps of kDecChunk when the longest sequence would need more chunks
-    // than the partial buffer holds
+    // chunk size: kDecChunk keys (768 streamed 5% faster than 512 and 1024
+    // at B=64); kDecChunkFew when (sequence, KV head) pairs are few, so that
+    // a small batch still spreads over the CUs; grown in steps of kDecChunk
+    // when the longest sequence would need more chunks than the partial
+    // buffer holds
     const int max_keys = c.window > 0 ? std::min(c.max_keys, c.window) : c.max_keys;
     a.window = c.window;
     int chunks = (max_keys + kDecChunk - 1) / kDecChunk;
     int chunk_keys = kDecChunk;
     if ((int64_t)c.B * c.Hkv * chunks < 2 * (int64_t)device_cus()) {
-        chunk_keys = kDecChunk / 2;
+        chunk_keys = kDecChunkFew;
         chunks = (max_keys + chunk_keys - 1) / chunk_keys;
     }
     if (chunks > c.max_splits) {
