@@ -217,22 +217,25 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     // Per-lane part of this wave's DMA blocks: block bi (K for bi < BLK/2,
     // then V) holds keys RPB*(bi % (BLK/2)) .. +RPB-1; lane slot -> key and
     // the element offset inside the row that belongs in that LDS slot.
-    int dkey[PER], doff[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int bi = wave * PER + i, isv = bi >= BLK / 2;
-        const int key = (bi % (BLK / 2)) * RPB + lane / KCH, pch = lane % KCH;
-        dkey[i] = key;
-        doff[i] = isv ? 16 * ((pch >> 1) ^ v_granule_swz<DH>(key)) + 8 * (pch & 1)  // V: granules
-                      : 8 * (pch ^ (key & (KCH - 1)));                              // K: chunks
-    }
+    // Computed where needed rather than kept for the whole loop.
+    auto blk_key = [&](int i) { return ((wave * PER + i) % (BLK / 2)) * RPB + lane / KCH; };
+    auto blk_off = [&](int i) {
+        const int key = blk_key(i), pch = lane % KCH;
+        return wave * PER + i >= BLK / 2 ? 16 * ((pch >> 1) ^ v_granule_swz<DH>(key)) + 8 * (pch & 1)  // V: granules
+                                         : 8 * (pch ^ (key & (KCH - 1)));                              // K: chunks
+    };
     // a wave's blocks are all K or all V; byte offset of each lane's chunk
-    // from the tile's first cache row (contiguous cache)
+    // from the tile's first cache row (contiguous cache).  Four blocks on,
+    // the keys are 4 RPB further and the swizzles (key mod KCH, key mod 4)
+    // repeat, so the offsets of blocks 4.. are those of blocks 0..3 plus
+    // 4 RPB rows, moved into the scalar base.
     static_assert((BLK / 2) % PER == 0, "a wave fills K blocks or V blocks only");
+    constexpr int NVO = PER > 4 ? 4 : PER;
+    static_assert(PER == NVO || ((4 * RPB) % KCH == 0 && (4 * RPB) % 4 == 0), "lane offsets repeat every 4 blocks");
     const bf16_t *const kv_src = wave * PER < BLK / 2 ? a.kc : a.vc;
-    uint32_t voff[PER];
+    uint32_t voff[NVO];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) voff[i] = (uint32_t)(dkey[i] * DH + doff[i]) * 2u;
+    for (int i = 0; i < NVO; ++i) voff[i] = (uint32_t)(blk_key(i) * DH + blk_off(i)) * 2u;
     auto issue = [&](int it, int stg) {
         const int j0 = it * BKV;
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base + stg * (2 * TILE * 2) + wave * PER * 1024);
@@ -245,14 +248,14 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
         if ((!PAGED || (1 << a.kvm.bs_shift) >= BKV) && j0 >= key_floor && j0 + BKV <= kv_len) {
             const bf16_t *src = kv_src + row(j0) * DH;
 #pragma unroll
-            for (int i = 0; i < PER; ++i) dma16_sbase(src, voff[i], base + i * 1024);
+            for (int i = 0; i < PER; ++i) dma16_sbase(src + (i / NVO) * (NVO * RPB * DH), voff[i % NVO], base + i * 1024);
             return;
         }
         int64_t rows[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) rows[i] = row(min(max(j0 + dkey[i], key_floor), kv_len - 1));
+        for (int i = 0; i < PER; ++i) rows[i] = row(min(max(j0 + blk_key(i), key_floor), kv_len - 1));
 #pragma unroll
-        for (int i = 0; i < PER; ++i) dma16(kv_src + rows[i] * DH + doff[i], base + i * 1024);
+        for (int i = 0; i < PER; ++i) dma16(kv_src + rows[i] * DH + blk_off(i), base + i * 1024);
     };
 
     f32x16 oacc[NE];
@@ -267,115 +270,148 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     const int q4 = lane >> 4, sl = lane & 15;
     const int v_row = 4 * (q4 >> 1) + (sl >> 2), v_in = (sl & 3) * 4;
 
-    // key tiles of this wave group; both groups run n_lo steps (the upper
-    // half has at most as many tiles) so that their barriers pair up
+    // key tiles of this wave group; both groups run n_lo steps so that their
+    // barriers pair up
     const int n_lo = NGRP == 2 ? (n_tiles - first_tile + 1) / 2 : n_tiles - first_tile;
     const int g_first = grp ? first_tile + n_lo : first_tile, g_end = grp ? n_tiles : first_tile + n_lo;
-    if (g_first < g_end) issue(g_first, 0);
-    for (int step = 0; step < n_lo; ++step) {
-        const int it = g_first + step, stg = step % NSTG;
-        wait_vmcnt<0>();                         // this wave's loads of tile it landed
-        asm volatile("s_barrier" ::: "memory");  // every wave's did; every wave is done with the previous tile
-        if (it + 1 < g_end) issue(it + 1, (stg + 1) % NSTG);
-        if (it < g_end && it < wave_tiles && it >= wave_first_tile) {
-            const bf16_t *Ks = ring + stg * 2 * TILE, *Vs = Ks + TILE;
-            const int j0 = it * BKV;
-            f32x16 sacc[2];
+    // tiles this wave computes: its group's, inside its own causal and window range
+    const int w_lo = max(g_first, wave_first_tile), w_hi = min(g_end, wave_tiles);
+
+    // S^T of a tile from K slot ks
+    auto scores = [&](int ks, f32x16 (&S)[2]) {
+        const bf16_t *Ks = ring + ks * 2 * TILE;
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) sacc[kt][v] = 0.0f;
-                const int key = kt * 32 + lr;
+            for (int v = 0; v < 16; ++v) S[kt][v] = 0.0f;
+            const int key = kt * 32 + lr;
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    const bf16x8 kf =
-                        as_bf16x8(*(const u32x4 *)(Ks + key * DH + (((2 * s + lh) ^ (key & (KCH - 1))) * 8)));
-                    sacc[kt] = mfma32(kf, qf[s], sacc[kt]);
-                }
+            for (int s = 0; s < NS; ++s) {
+                const bf16x8 kf = as_bf16x8(*(const u32x4 *)(Ks + key * DH + (((2 * s + lh) ^ (key & (KCH - 1))) * 8)));
+                S[kt] = mfma32(kf, qf[s], S[kt]);
             }
-            // Online softmax in the log2 domain.  The reference max of a
-            // query moves only when a tile raises it by more than 2^8 (in
-            // exponent units): until then the weights 2^(x - m) stay below
-            // 256 and the running sums stay exact up to rounding, so the
-            // output accumulators are rescaled only on those rare tiles.
-            // The diagonal crosses this tile, or (window) its lower edge
-            // does; rows past start + T sit above every real query's diagonal.
-            const bool need_mask = (j0 + BKV - 1 > start + t0) || (W > 0 && j0 < start + t0 + 31 - W + 1);
-            const int key_lo = W > 0 ? qpos - W + 1 : 0;
-            // one wave-uniform branch around the masking selects (a test
-            // per element would put a branch in front of every score; the
-            // empty asm keeps the compiler from executing the selects on
-            // every tile instead of branching)
-            if (need_mask) {
-                asm volatile("");
-#pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                        sacc[kt][v] = (key > qpos || key < key_lo) ? -INFINITY : sacc[kt][v];
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kt][v]);
-            mx = max_halves(mx) * a.scale_log2e;  // lane l holds keys 4lh.. of its query, l ^ 32 the rest
-            const bool grow = mx > m_run + 8.0f;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
-                if (grow) m_run = mx;
-                l_run *= alpha;
-#pragma unroll
-                for (int te = 0; te < NE; ++te)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) oacc[te][v] *= alpha;
-            }
-            const float msub = m_run == -INFINITY ? 0.0f : m_run;
-            float sum = -0.0f;  // the additive identity: the first add folds away
+        }
+    };
+    // Softmax and P.V of tile it (scores S, V slot vs), online in the log2
+    // domain.  The reference max of a query moves only when a tile raises it
+    // by more than 2^8 (in exponent units): until then the weights 2^(x - m)
+    // stay below 256 and the running sums stay exact up to rounding, so the
+    // output accumulators are rescaled only on those rare tiles.
+    // The first part: mask, max and the rare rescale; returns the max the
+    // weights of this tile are taken against.
+    auto softmax_head = [&](int it, f32x16 (&S)[2]) -> float {
+        const int j0 = it * BKV;
+        // The diagonal crosses this tile, or (window) its lower edge does;
+        // rows past start + T sit above every real query's diagonal.  One
+        // wave-uniform branch around the masking selects (a test per element
+        // would put a branch in front of every score; the empty asm keeps the
+        // compiler from executing the selects on every tile instead of
+        // branching).
+        const bool need_mask = (j0 + BKV - 1 > start + t0) || (W > 0 && j0 < start + t0 + 31 - W + 1);
+        const int key_lo = W > 0 ? qpos - W + 1 : 0;
+        if (need_mask) {
+            asm volatile("");
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][v], a.scale_log2e, -msub));
-                    sacc[kt][v] = p;
-                    sum += p;
+                    const int key = j0 + kt * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                    S[kt][v] = (key > qpos || key < key_lo) ? -INFINITY : S[kt][v];
                 }
-            l_run += sum_halves(sum);
-            // P^T fragment of 16-key slice s2: lane (query lr, half lh) holds
-            // keys 16 s2 + {4lh .. 4lh+3, 8+4lh .. 8+4lh+3}.  The weights are
-            // fp32 softmax values; they enter the bf16 product as a hi + lo
-            // pair of bf16 fragments, both against the same V^T fragment.
-            bf16x8 pf[4], pl[4];
+        }
+        float mx = -INFINITY;
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const f32x16 &src = sacc[s2 >> 1];
-                const int o = 8 * (s2 & 1);
-                u32x4 w, wl;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x2 hl = split_bf16x2(src[o + 2 * i], src[o + 2 * i + 1]);
-                    w[i] = hl[0];
-                    wl[i] = hl[1];
-                }
-                pf[s2] = as_bf16x8(w);
-                pl[s2] = as_bf16x8(wl);
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kt][v]);
+        mx = max_halves(mx) * a.scale_log2e;  // lane l holds keys 4lh.. of its query, l ^ 32 the rest
+        const bool grow = mx > m_run + 8.0f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+            if (grow) m_run = mx;
+            l_run *= alpha;
+#pragma unroll
+            for (int te = 0; te < NE; ++te)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) oacc[te][v] *= alpha;
+        }
+        return m_run == -INFINITY ? 0.0f : m_run;
+    };
+    // The rest: the weights and their products with V (slot vs).
+    auto softmax_tail = [&](int vs, f32x16 (&S)[2], float msub) {
+        const bf16_t *Vs = ring + vs * 2 * TILE + TILE;
+        float sum = -0.0f;  // the additive identity: the first add folds away
+        // One 16-key slice at a time, so that the products of a slice run
+        // while the next slice's weights are formed.  P^T fragment of slice
+        // s2: lane (query lr, half lh) holds keys 16 s2 + {4lh .. 4lh+3,
+        // 8+4lh .. 8+4lh+3}.  The weights are fp32 softmax values; they enter
+        // the bf16 product as a hi + lo pair of bf16 fragments, both against
+        // the same V^T fragment.
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            f32x16 &src = S[s2 >> 1];
+            const int o = 8 * (s2 & 1);
+#pragma unroll
+            for (int v = o; v < o + 8; ++v) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(src[v], a.scale_log2e, -msub));
+                src[v] = p;
+                sum += p;
             }
+            u32x4 w, wl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x2 hl = split_bf16x2(src[o + 2 * i], src[o + 2 * i + 1]);
+                w[i] = hl[0];
+                wl[i] = hl[1];
+            }
+            const bf16x8 pf = as_bf16x8(w), pl = as_bf16x8(wl);
 #pragma unroll
             for (int te = 0; te < NE; ++te) {
                 const int gran = 2 * te + (q4 & 1);
-#pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    const int r0 = 16 * s2 + v_row, r1 = r0 + 8;
-                    const u32x2 lo = lds_read_tr16(Vs + r0 * DH + ((gran ^ v_granule_swz<DH>(r0)) * 16) + v_in);
-                    const u32x2 hi = lds_read_tr16(Vs + r1 * DH + ((gran ^ v_granule_swz<DH>(r1)) * 16) + v_in);
-                    const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    oacc[te] = mfma32(vf, pf[s2], oacc[te]);
-                    oacc[te] = mfma32(vf, pl[s2], oacc[te]);
-                }
+                const int r0 = 16 * s2 + v_row, r1 = r0 + 8;
+                const u32x2 lo = lds_read_tr16(Vs + r0 * DH + ((gran ^ v_granule_swz<DH>(r0)) * 16) + v_in);
+                const u32x2 hi = lds_read_tr16(Vs + r1 * DH + ((gran ^ v_granule_swz<DH>(r1)) * 16) + v_in);
+                const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                oacc[te] = mfma32(vf, pf, oacc[te]);
+                oacc[te] = mfma32(vf, pl, oacc[te]);
             }
         }
+        l_run += sum_halves(sum);
+    };
+
+    // Software pipeline over the key tiles: step s issues the score products
+    // of tile s+1, then the softmax and P.V of tile s, so the matrix cores
+    // still work on the next scores while this tile's vector work starts.
+    // K tile j sits in K slot (j - g_first) % 2 and is loaded two steps
+    // before its softmax, V tile j in V slot (j - g_first) % 2, one step
+    // before.  Each wave loads K blocks or V blocks only.
+    const bool kwave = wave * PER < BLK / 2;
+    if (kwave) {
+        if (g_first < g_end) issue(g_first, 0);
+        if (g_first + 1 < g_end) issue(g_first + 1, 1);
+    } else if (g_first < g_end) {
+        issue(g_first, 0);
+    }
+    f32x16 S0[2], S1[2];
+    wait_vmcnt<0>();
+    asm volatile("s_barrier" ::: "memory");
+    if (g_first >= w_lo && g_first < w_hi) scores(0, S0);
+    auto step = [&](int s, f32x16 (&Sc)[2], f32x16 (&Sn)[2]) {
+        const int it = g_first + s;
+        wait_vmcnt<0>();                         // this wave's loads of the previous step landed
+        asm volatile("s_barrier" ::: "memory");  // every wave's did; every wave is done with the previous step
+        if (kwave) {
+            if (it + 2 < g_end) issue(it + 2, s & 1);
+        } else if (it + 1 < g_end) {
+            issue(it + 1, (s + 1) & 1);
+        }
+        const bool cur = it >= w_lo && it < w_hi, nxt = it + 1 >= w_lo && it + 1 < w_hi;
+        if (nxt) scores((s + 1) & 1, Sn);
+        if (cur) softmax_tail(s & 1, Sc, softmax_head(it, Sc));
+    };
+    for (int s = 0; s < n_lo; s += 2) {
+        step(s, S0, S1);
+        if (s + 1 < n_lo) step(s + 1, S1, S0);
     }
     wait_vmcnt<0>();
     if constexpr (NGRP == 2) {
