@@ -192,9 +192,13 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
 // Issued as inline assembly so that the compiler neither tracks the LDS write
 // nor inserts its own vmcnt waits; callers order it with wait_vmcnt and a
-// barrier.
+// barrier.  An LDS DMA that reads m0 right after a scalar write of m0 needs
+// one wait state on this chip family (the compiler adds it for its own
+// instructions, not inside inline assembly): without the s_nop, the first
+// 16 lanes of the load could still take the previous m0 and land in the
+// previous block.
 __device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte_addr), "v"(gptr)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_byte_addr), "v"(gptr)
                  : "memory", "m0");
 }
 
@@ -206,7 +210,7 @@ __device__ __forceinline__ void dma16_sbase(const void *sbase, uint32_t voff, ui
     const uint64_t b = (uint64_t)(uintptr_t)sbase;
     const uint64_t ub = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_byte_addr), "v"(voff),
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_byte_addr), "v"(voff),
                  "s"((const void *)(uintptr_t)ub)
                  : "memory", "m0");
 }
@@ -215,7 +219,7 @@ __device__ __forceinline__ void dma16_sbase(const void *sbase, uint32_t voff, ui
 // policy keeps it from displacing reused lines in the caches; measured on
 // MI355X it roughly doubles the rate of a weight stream over the plain form.
 __device__ __forceinline__ void dma16_stream(const void *gptr, uint32_t lds_byte_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_byte_addr), "v"(gptr)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(lds_byte_addr), "v"(gptr)
                  : "memory", "m0");
 }
 
