@@ -10,9 +10,12 @@
 // columns of the rows of x the MFMA row tiles cover (16 per tile, rows past M
 // clamped; SK = 128 when a 64-row stage of those rows would not split into
 // whole 1 KB blocks per wave), go from global memory straight
-// into a ring of LDS stages (global_load_lds_dwordx4 with the nontemporal
-// policy), so the loads in flight cost no registers and the ring keeps
-// several stages of HBM reads outstanding.  Each wave owns BN/4 output columns: its weight fragments come
+// into a ring of LDS stages (global_load_lds_dwordx4), so the loads in flight
+// cost no registers and the ring keeps several stages of HBM reads
+// outstanding.  The weights, read once, take the nontemporal policy; the
+// rows of x, which every column block reads again, take the plain one and
+// stay in L2 (streamed like the weights, they were fetched again from
+// beyond L2, and each GEMM of a 64-row decode step took 3.5-4.5 us longer).  Each wave owns BN/4 output columns: its weight fragments come
 // from the transpose read ds_read_b64_tr_b16 on the N-contiguous weight rows
 // (32-byte granules swizzled by row), the x fragments are 16-byte reads
 // (chunks swizzled by row), and the products run on MFMA 16x16x32.  Each
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(SkinnyArgs a) {
 #pragma unroll
         for (int i = 0; i < PW; ++i) dma16_stream(wsrc[i] + (int64_t)st * SK * wld[i], wb + i * 1024);
 #pragma unroll
-        for (int i = 0; i < PX; ++i) dma16_stream(xsrc[i] + st * SK, xb + i * 1024);
+        for (int i = 0; i < PX; ++i) dma16(xsrc[i] + st * SK, xb + i * 1024);
     };
     auto wait_stages = [&](int n) {  // at most n later stages of this wave still in flight
         static_assert((NST - 2) * PER < 64, "vmcnt range");
