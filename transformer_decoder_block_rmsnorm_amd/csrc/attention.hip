@@ -109,8 +109,10 @@ __global__ __launch_bounds__(256) void attn_rowwise_kernel(AttnCall a) {
 //                                  block output's error sigma against the
 //                                  fp32 reference 15% larger at the 7B
 //                                  shape (the attention delta's 84%).
-// K and V tiles of 64 keys go from global memory straight into a ring of LDS
-// stages (global_load_lds_dwordx4) in their cache layout, rows of dh values.
+// K and V tiles of 64 keys go from global memory straight into LDS
+// (global_load_lds_dwordx4) in their cache layout, rows of dh values: two K
+// slots and two V slots, K loaded two steps ahead of its softmax and V one
+// (the loop is a two-step pipeline, described below).
 // K rows are read as 16-byte fragments (chunks XOR-swizzled by key); the V^T
 // fragments come from the transpose read ds_read_b64_tr_b16 on rows of V
 // (32-byte granules swizzled by key), taking keys in the order in which the
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
     constexpr int NE = DH / 32;                // 32-row e tiles of O^T
     constexpr int KCH = DH / 8;                // 16-byte chunks per row
     constexpr int TILE = BKV * DH;             // elements of one K (or V) tile
-    constexpr int NSTG = 2;                    // ring stages
+    constexpr int NSTG = 2;                    // two stages, each a K slot and a V slot
     constexpr int BLK = 2 * TILE * 2 / 1024;   // 1 KB blocks per stage (K then V)
     constexpr int PER = BLK / 4;               // DMA instructions per wave per tile
     constexpr int RPB = 1024 / (DH * 2);       // keys per 1 KB block
