@@ -101,6 +101,17 @@ def test_bf16_block_prefill_then_decode(oracle, shape):
     check_against_oracle(oracle, cfg, shape["B"], shape["T0"], shape["steps"], shape["T0"] + shape["steps"] + 5)
 
 
+@pytest.mark.parametrize("T0", [1, 2, 63, 64, 65, 127, 128, 129, 192])
+def test_bf16_prefill_lengths_around_key_tiles(oracle, T0):
+    """Prefill lengths at and around the 64-key tiles of the flash kernel:
+    one tile, a partial second tile, whole tiles, and (with few workgroups)
+    the two wave groups splitting one to four tiles, where the upper group
+    may have none; every output and cache row against the oracle."""
+    cfg = small_cfg(d=256, H=4, Hkv=1, f=512, dtype="bf16", number=131)
+    print("case: bf16 prefill length", T0, flush=True)
+    check_against_oracle(oracle, cfg, 2, T0, 1, T0 + 4)
+
+
 @pytest.mark.parametrize("d,H,Hkv,B,T0,W", [
     (256, 4, 2, 80, 200, 0),    # dh 64, two heads per KV head: 4 x 80 x 2 = 640 blocks of 64 rows
     (256, 4, 2, 80, 200, 70),   # the same with a window
