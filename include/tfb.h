@@ -73,6 +73,20 @@ typedef struct {
     float rope_base, rms_eps;
     int32_t dtype;  /* tfb_dtype */
     int32_t window; /* keys per query; 0 = full causal */
+    /* fold_norms != 0 (bf16 calls over more than 64 rows, B * T > 64): an
+     * RMSNorm whose input a GEMM of the block produces (RMSNorm2 after the Wo
+     * GEMM; in tfb_model_forward also each later layer's RMSNorm1 after the
+     * previous W2 GEMM) is folded into that GEMM and the next one instead of
+     * running as a pass of its own.  The producing GEMM's epilogue stores
+     * bf16(y * g) and per-row partial sums of y^2; the consuming GEMM scales
+     * each row of its fp32 products by 1 / sqrt(mean(y^2) + eps).  This is
+     * the same product (row m of (s_m y_m * g) W is s_m ((y_m * g) W)); only
+     * the place where the GEMM operand is rounded to bf16 moves, from the
+     * normalised row to y * g.  0: every RMSNorm's output is the GEMM operand
+     * (the tirogla page, Implementation notes: norms in fp32, GEMM operands
+     * in bf16).  Ignored for fp32 storage and for calls of at most 64 rows,
+     * whose norms already run inside the GEMMs' reduce passes. */
+    int32_t fold_norms;
 } tfb_block_config;
 
 /* One block's weights, all in the config's storage type, [in, out] layout:

@@ -26,17 +26,37 @@ def _bf16(a):
     return a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
 
 
-def torch_block_f64(cfg, w, x, start=0, bf16=False, window=0):
+def _norm_operand(v, g, eps, rb, fold_rows):
+    """The GEMM operand of an RMSNorm over the last axis of v [B, T, d] and the
+    scale of each row of the GEMM's products.  Rows t < fold_rows take the
+    folded form, where the row scale 1/rms(v) is applied to the products
+    instead of the operand: operand rb(v * g), scale 1/rms(v).  The other rows
+    take rb(rms_norm(v) * g) and scale 1.  Both are the same product before
+    rounding (row m of (s v * g) W is s ((v * g) W)); only where the operand is
+    rounded to bf16 differs."""
+    d = v.shape[-1]
+    plain = rb(F.rms_norm(v, (d,), weight=g, eps=eps))
+    if not fold_rows:
+        return plain, None
+    rows = (torch.arange(v.shape[1]) < fold_rows)[None, :, None]
+    s = torch.rsqrt(v.pow(2).mean(-1, keepdim=True) + eps)
+    return torch.where(rows, rb(v * g), plain), torch.where(rows, s, torch.ones_like(s))
+
+
+def torch_block_f64(cfg, w, x, start=0, bf16=False, window=0, fold1=0, fold2=0):
+    """fold1, fold2: rows (token index t < fold) whose RMSNorm 1 / 2 takes the
+    folded form of _norm_operand."""
     d, H, Hkv = cfg.d, cfg.n_heads, cfg.n_kv_heads
     dh = d // H
     rb = _bf16 if bf16 else (lambda a: a)
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
     X = t(x)
     B, T, _ = X.shape
-    h = rb(F.rms_norm(X, (d,), weight=t(w["g_attn"]), eps=cfg.rms_eps))
-    q = (h @ t(w["wq"])).reshape(B, T, H, dh)
-    k = (h @ t(w["wk"])).reshape(B, T, Hkv, dh)
-    v = (h @ t(w["wv"])).reshape(B, T, Hkv, dh)
+    h, s1 = _norm_operand(X, t(w["g_attn"]), cfg.rms_eps, rb, fold1)
+    sc1 = (lambda a: a) if s1 is None else (lambda a: a * s1)  # noqa: E731
+    q = sc1(h @ t(w["wq"])).reshape(B, T, H, dh)
+    k = sc1(h @ t(w["wk"])).reshape(B, T, Hkv, dh)
+    v = sc1(h @ t(w["wv"])).reshape(B, T, Hkv, dh)
     pos = torch.arange(start, start + T, dtype=torch.float64)
     theta = torch.tensor([cfg.rope_base ** (-2.0 * i / dh) for i in range(dh // 2)], dtype=torch.float64)
     rot = torch.polar(torch.ones(T, dh // 2, dtype=torch.float64), pos[:, None] * theta[None, :])
@@ -63,8 +83,9 @@ def torch_block_f64(cfg, w, x, start=0, bf16=False, window=0):
     pre["att_pre"] = o.numpy()
     o = rb(o)
     r = X + o @ t(w["wo"])
-    h2 = rb(F.rms_norm(r, (d,), weight=t(w["g_mlp"]), eps=cfg.rms_eps))
-    act = F.silu(h2 @ t(w["w1"])) * (h2 @ t(w["w3"]))
+    h2, s2 = _norm_operand(r, t(w["g_mlp"]), cfg.rms_eps, rb, fold2)
+    sc2 = (lambda a: a) if s2 is None else (lambda a: a * s2)  # noqa: E731
+    act = F.silu(sc2(h2 @ t(w["w1"]))) * sc2(h2 @ t(w["w3"]))
     pre["act_pre"] = act.numpy()
     act = rb(act)
     return (r + act @ t(w["w2"])).numpy(), {"q": q.reshape(B, T, H * dh).numpy(), "att": o.numpy(),
@@ -117,15 +138,17 @@ def decode_f64(cfg, w, x, lens, kc, vc, bf16=True):
                                   "r": r[:, None].numpy(), "act": act[:, None].numpy(), **pre}
 
 
-def model_f64(cfg, layers, embed, g_final, w_unembed, ids, bf16=True, kv=False):
+def model_f64(cfg, layers, embed, g_final, w_unembed, ids, bf16=True, kv=False, fold_rows=0):
     """Logits of the last row of each sequence: embed, L blocks (outputs handed
     on as bf16 activations), final RMSNorm, untied head.  With kv, also each
-    layer's k (after RoPE) and v before bf16 storage, [B, T, Hkv*dh]."""
+    layer's k (after RoPE) and v before bf16 storage, [B, T, Hkv*dh].
+    fold_rows: rows t < fold_rows take the folded form of every RMSNorm that
+    follows a GEMM (RMSNorm 2, and RMSNorm 1 after the first layer)."""
     rb = _bf16 if bf16 else (lambda a: a)
     x = torch.from_numpy(embed[ids].astype(np.float64))
     ks, vs = [], []
-    for w in layers:
-        y, inter = torch_block_f64(cfg, w, x.numpy(), bf16=bf16)
+    for l, w in enumerate(layers):
+        y, inter = torch_block_f64(cfg, w, x.numpy(), bf16=bf16, fold1=fold_rows if l else 0, fold2=fold_rows)
         ks.append(inter["k_pre"])
         vs.append(inter["v_pre"])
         x = rb(torch.from_numpy(y))

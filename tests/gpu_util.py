@@ -38,6 +38,13 @@ def to_np(t) -> np.ndarray:
     return t.float().cpu().numpy()
 
 
+def folded_rows(cfg, M: int, T: int, fold: int) -> int:
+    """Rows per sequence whose RMSNorms that follow a GEMM the library folds
+    into the GEMMs around them (config fold_norms): every row of a bf16 call
+    over more rows than its weight-streaming GEMMs take (64), else none."""
+    return T if fold and cfg.dtype == "bf16" and M > 64 else 0
+
+
 def tol(cfg) -> float:
     return BF16_TOL if cfg.dtype == "bf16" else F32_TOL
 

@@ -22,11 +22,12 @@ def _torch():
     return torch
 
 
-def run_prefill_decode(cfg, B, T0, steps, t_max, gains="ones"):
+def run_prefill_decode(cfg, B, T0, steps, t_max, gains="ones", fold=0):
     """Prefill T0 tokens then `steps` decode steps on the GPU; returns outputs
-    [B, T0+steps, d], the caches, and the inputs."""
+    [B, T0+steps, d], the caches, and the inputs.  fold: the config's
+    fold_norms."""
     torch = _torch()
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     w32, w = dev_weights(cfg, gains=gains)
     x32, x = dev_x(cfg, B, T0 + steps)
     rope = tfb.rope_table_init(tc, t_max)
@@ -43,8 +44,8 @@ def run_prefill_decode(cfg, B, T0, steps, t_max, gains="ones"):
     return np.concatenate(outs, axis=1), kc, vc, w32, x32
 
 
-def check_against_oracle(oracle, cfg, B, T0, steps, t_max, gains="ones"):
-    got, kc, vc, w32, x32 = run_prefill_decode(cfg, B, T0, steps, t_max, gains)
+def check_against_oracle(oracle, cfg, B, T0, steps, t_max, gains="ones", fold=0):
+    got, kc, vc, w32, x32 = run_prefill_decode(cfg, B, T0, steps, t_max, gains, fold)
     dh = cfg.d // cfg.n_heads
     okc = np.full((B, cfg.n_kv_heads, t_max, dh), np.nan, np.float32)
     ovc = okc.copy()
@@ -99,6 +100,20 @@ def test_bf16_block_prefill_then_decode(oracle, shape):
     cfg = small_cfg(d=shape["d"], H=shape["H"], Hkv=shape["Hkv"], f=shape["f"], dtype="bf16", number=82)
     print("case: bf16", shape, flush=True)
     check_against_oracle(oracle, cfg, shape["B"], shape["T0"], shape["steps"], shape["T0"] + shape["steps"] + 5)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(d=512, H=4, Hkv=2, f=1024, B=2, T0=300, steps=2),    # 128x128 tiles, ragged last row tile
+    dict(d=768, H=6, Hkv=2, f=2048, B=1, T0=2048, steps=1),   # gate-up on 256x128 tiles (W1|W3 pairs)
+    dict(d=1024, H=8, Hkv=2, f=4096, B=1, T0=4096, steps=1),  # gate-up on 256x256 tiles
+])
+def test_bf16_folded_norms_prefill_then_decode(oracle, shape):
+    """fold_norms: RMSNorm2 folded into the Wo epilogue and the gate-up GEMM
+    in prefill (the decode steps, 64 rows or fewer, run as before)."""
+    cfg = small_cfg(d=shape["d"], H=shape["H"], Hkv=shape["Hkv"], f=shape["f"], dtype="bf16", number=83)
+    print("case: bf16 folded norms", shape, flush=True)
+    check_against_oracle(oracle, cfg, shape["B"], shape["T0"], shape["steps"], shape["T0"] + shape["steps"] + 5,
+                         gains="random", fold=1)
 
 
 @pytest.mark.parametrize("T0", [1, 2, 63, 64, 65, 127, 128, 129, 192])
@@ -551,14 +566,16 @@ def test_sliding_window_decode_long_cache(oracle, lens, W):
 
 # ---- variable-length batched prefill (tirogla "Transformer block", Pitfalls:
 # pad tokens must not be attended to in batched prefill)
-@pytest.mark.parametrize("dtype,d,H,Hkv,W", [("f32", 64, 4, 2, 0), ("bf16", 512, 4, 2, 0), ("bf16", 256, 4, 1, 30)])
-def test_varlen_prefill_matches_per_sequence(oracle, dtype, d, H, Hkv, W):
+@pytest.mark.parametrize("dtype,d,H,Hkv,W,fold", [("f32", 64, 4, 2, 0, 0), ("bf16", 512, 4, 2, 0, 0),
+                                                   ("bf16", 256, 4, 1, 30, 0), ("bf16", 512, 4, 2, 0, 1)])
+def test_varlen_prefill_matches_per_sequence(oracle, dtype, d, H, Hkv, W, fold):
     """Three right-padded sequences with their own starts and lengths (one
-    empty) in one call; each real row must match that sequence alone."""
+    empty) in one call; each real row must match that sequence alone (fold:
+    the config's fold_norms)."""
     torch = _torch()
     from tests.gpu_util import to_dev
     cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype=dtype, number=120, window=W)
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     w32, w = dev_weights(cfg)
     B, T = 3, 100
     starts, lens = np.array([0, 20, 64], np.int32), np.array([100, 37, 0], np.int32)

@@ -10,7 +10,10 @@ are compared with the oracle's fp32 values before its own bf16 rounding.
 At these sizes the method itself does not meet that bound against the fp32
 oracle: both round every GEMM operand to bf16, so any fp32 rounding
 difference moves some operand roundings to the neighbouring bf16 value, and
-each GEMM sums thousands of such steps.  An exact (fp64) evaluation of the
+each GEMM sums thousands of such steps.  Where the config folds an RMSNorm
+into the GEMMs around it (fold_norms: the row scale 1/rms is applied to the
+products of the GEMM that reads bf16(x * g)), the exact evaluation rounds that
+operand at the same place.  An exact (fp64) evaluation of the
 same method with the same bf16 operand roundings (tests/exact.py) sits at
 max 0.0201 rms from the oracle on the 7B block output once stored in bf16, and
 0.032 rms on the model's logits.  Every check therefore runs the exact
@@ -26,7 +29,7 @@ import synth
 from synth.configs import C2, C3, C4, C5, tensor_id
 from tests.conftest import gpu_available
 from tests.exact import decode_f64, model_f64, stored_bf16, torch_block_f64
-from tests.gpu_util import Checks, cache_rows, dev_weights, dev_x, to_dev, to_np, widen_cache
+from tests.gpu_util import Checks, cache_rows, dev_weights, dev_x, folded_rows, to_dev, to_np, widen_cache
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -56,9 +59,9 @@ def _intermediates(chk, tc, ws, B, T, inter, ex, x32, got, ref, ex_out):
     chk.flips("act operand", act, inter["act"])
 
 
-def _prefill_full(oracle, cfg, rows, intermediates):
+def _prefill_full(oracle, cfg, rows, intermediates, fold=0):
     import torch
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     w32, w = dev_weights(cfg)
     x32, x = dev_x(cfg, cfg.B, cfg.T)
     rope = tfb.rope_table_init(tc, cfg.t_max)
@@ -74,10 +77,13 @@ def _prefill_full(oracle, cfg, rows, intermediates):
     print("  GPU done; oracle ...", flush=True)
     ref, inter = oracle.block_forward(cfg, w32, x32, kc=okc, vc=ovc, intermediates=True)
     print("  oracle done; exact fp64 evaluation ...", flush=True)
-    ex_out, ex = torch_block_f64(cfg, w32, x32, bf16=True)
+    ex_out, ex = torch_block_f64(cfg, w32, x32, bf16=True, fold2=folded_rows(cfg, cfg.B * cfg.T, cfg.T, fold))
     got = to_np(out)
     chk = Checks()
-    chk("out, sampled rows", got[:, rows], ref[:, rows], TOL)
+    if fold:
+        chk.against_floor("out, sampled rows", got[:, rows], ref[:, rows], stored_bf16(ex_out)[:, rows], TOL)
+    else:
+        chk("out, sampled rows", got[:, rows], ref[:, rows], TOL)
     chk.against_floor("out, every value", got, ref, stored_bf16(ex_out), TOL)
     Hkv = cfg.n_kv_heads
     chk.against_floor("k cache", widen_cache(kc)[:, :, :cfg.T], cache_rows(inter["k_pre"], Hkv),
@@ -89,16 +95,19 @@ def _prefill_full(oracle, cfg, rows, intermediates):
     chk.done()
 
 
-def test_llama2_7b_block_prefill_full_size(oracle):
-    """d=4096, H=Hkv=32, f=11008, B=1, T=2048."""
-    print("case: full-size 7B block prefill", flush=True)
-    _prefill_full(oracle, C2, [0, 1, 2, 31, 32, 63, 64, 127, 128, 255, 256, 1000, 1023, 1024, 2046, 2047], True)
+@pytest.mark.parametrize("fold", [0, 1])
+def test_llama2_7b_block_prefill_full_size(oracle, fold):
+    """d=4096, H=Hkv=32, f=11008, B=1, T=2048; fold: the config's fold_norms."""
+    print("case: full-size 7B block prefill, fold_norms=%d" % fold, flush=True)
+    _prefill_full(oracle, C2, [0, 1, 2, 31, 32, 63, 64, 127, 128, 255, 256, 1000, 1023, 1024, 2046, 2047], True,
+                  fold)
 
 
-def test_gqa_long_context_block_prefill_full_size(oracle):
+@pytest.mark.parametrize("fold", [0, 1])
+def test_gqa_long_context_block_prefill_full_size(oracle, fold):
     """d=4096, H=32, Hkv=8, f=14336, base 5e5, B=2, T=8192 (the benchmark's headline shape)."""
-    print("case: full-size GQA long-context block prefill", flush=True)
-    _prefill_full(oracle, C3, [0, 1, 31, 32, 63, 64, 127, 128, 4095, 4096, 8190, 8191], False)
+    print("case: full-size GQA long-context block prefill, fold_norms=%d" % fold, flush=True)
+    _prefill_full(oracle, C3, [0, 1, 31, 32, 63, 64, 127, 128, 4095, 4096, 8190, 8191], False, fold)
 
 
 def test_gqa_decode_step_full_size(oracle):
@@ -146,16 +155,29 @@ def test_gqa_decode_step_full_size(oracle):
     chk.done()
 
 
-def test_model_two_layers_full_widths(oracle):
+@pytest.mark.parametrize("fold", [0, 1])
+def test_model_two_layers_full_widths(oracle, fold):
     """The 32-layer model's widths (d=4096, Hkv=8, f=14336, V=32000), B=4,
     T=1024 prompt, with 2 layers so the oracle finishes: prefill logits of the
     last rows, then 3 greedy decode steps teacher-forced with the GPU's ids.
     Logits are fp32 on both sides: the stated bound applies to them as written."""
+    print("case: 2-layer model at full widths, fold_norms=%d" % fold, flush=True)
+    _model_two_layers(oracle, C5, fold, 3)
+
+
+def test_model_two_layers_7b_widths_folded(oracle):
+    """Two layers at the 7B block's widths (d=4096, H=Hkv=32, f=11008), B=1,
+    T=2048, V=1024, with fold_norms: the first layer's W2 GEMM (2048 rows,
+    K=11008) runs a split-K tail whose fix-up pass folds the second layer's
+    RMSNorm1, so the second layer's cache rows and the logits check it."""
+    print("case: 2-layer model at 7B widths, fold_norms=1", flush=True)
+    _model_two_layers(oracle, C2.with_(vocab=1024, mode="model", n_layers=2), 1, 1)
+
+
+def _model_two_layers(oracle, cfg, fold, steps):
     import torch
-    cfg = C5
-    L, V, B, T, steps = 2, cfg.vocab, cfg.B, cfg.T, 3
-    print("case: 2-layer model at full widths", flush=True)
-    tc = tfb.Config.of(cfg)
+    L, V, B, T = 2, cfg.vocab, cfg.B, cfg.T
+    tc = tfb.Config.of(cfg, fold)
     layers32, layers = [], []
     for l in range(L):
         a, b = dev_weights(cfg, layer=l)
@@ -184,7 +206,8 @@ def test_model_two_layers_full_widths(oracle):
                                               kv_pre=True)
     chk = Checks()
     got = lg.cpu().numpy()
-    ex_logits, ex_k, ex_v = model_f64(cfg, layers32, e32, g32, u32, ids, kv=True)
+    fr = folded_rows(cfg, B * T, T, fold)
+    ex_logits, ex_k, ex_v = model_f64(cfg, layers32, e32, g32, u32, ids, kv=True, fold_rows=fr)
     chk.against_floor("prefill logits (last rows)", got, ref, ex_logits, TOL)
     Hkv = cfg.n_kv_heads
     for l in range(L):
@@ -204,6 +227,6 @@ def test_model_two_layers_full_widths(oracle):
                                      start=np.full(B, T + s, np.int32))
         # the exact evaluation of the same step: the whole sequence so far, last row
         chk.against_floor("decode step %d logits" % s, lg.cpu().numpy(), r1,
-                          model_f64(cfg, layers32, e32, g32, u32, seq), TOL)
+                          model_f64(cfg, layers32, e32, g32, u32, seq, fold_rows=fr), TOL)
         cur = nxt.cpu().numpy()
     chk.done()

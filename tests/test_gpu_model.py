@@ -35,17 +35,20 @@ def model_inputs(cfg, L, V):
     return (layers32, emb32, gf32, wu32), (layers, to_dev(emb32, embb), to_dev(gf32, gfb), to_dev(wu32, wub))
 
 
-@pytest.mark.parametrize("dtype,d,H,Hkv,f,L,V,B,T,steps", [
-    ("f32", 64, 4, 2, 192, 2, 100, 2, 12, 3),
-    ("bf16", 512, 4, 2, 1024, 2, 1024, 2, 40, 3),
-    ("bf16", 256, 2, 1, 512, 3, 512, 3, 70, 2),
+@pytest.mark.parametrize("dtype,d,H,Hkv,f,L,V,B,T,steps,fold", [
+    ("f32", 64, 4, 2, 192, 2, 100, 2, 12, 3, 0),
+    ("bf16", 512, 4, 2, 1024, 2, 1024, 2, 40, 3, 0),
+    ("bf16", 256, 2, 1, 512, 3, 512, 3, 70, 2, 0),
+    # RMSNorms folded into the GEMMs around them (prefill: 80 and 210 rows)
+    ("bf16", 512, 4, 2, 1024, 2, 1024, 2, 40, 3, 1),
+    ("bf16", 256, 2, 1, 512, 3, 512, 3, 70, 2, 1),
 ])
-def test_model_prefill_then_greedy_decode(oracle, dtype, d, H, Hkv, f, L, V, B, T, steps):
+def test_model_prefill_then_greedy_decode(oracle, dtype, d, H, Hkv, f, L, V, B, T, steps, fold):
     import torch
     cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=f, dtype=dtype, base=500000.0, number=95)
-    print("case: model", dtype, d, L, V, B, T, steps, flush=True)
+    print("case: model", dtype, d, L, V, B, T, steps, "fold_norms=%d" % fold, flush=True)
     (l32, e32, g32, u32), (ld, ed, gd, ud) = model_inputs(cfg, L, V)
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     h = tfb.ModelHandle(tc, ld, ed, gd, ud)
     t_max = T + steps + 2
     dh = d // H

@@ -286,6 +286,25 @@ def test_exact_decode_and_model_compositions(oracle):
     assert rel_err(logits, model_f64(cfg, layers, emb, gf, wu, ids)) <= 1e-5
 
 
+def test_folded_norm_form_is_the_same_product(oracle):
+    """The folded RMSNorm form of the exact evaluation (operand x * g, the row
+    scale 1/rms(x) applied to the GEMM's products) is the oracle's block
+    before any bf16 rounding, for every row folded or only a prefix; with bf16
+    operands it moves only where the operand is rounded (the result stays
+    within that rounding's reach of the oracle)."""
+    cfg = small_cfg(d=64, H=4, Hkv=2, f=192, number=64)
+    w, _ = block_weights(cfg, gains="random")
+    x, _ = activations(cfg, 2, 9)
+    ref = oracle.block_forward(cfg, w, x)
+    for f1, f2 in ((9, 9), (0, 9), (4, 6)):
+        got, _ = torch_block_f64(cfg, w, x, fold1=f1, fold2=f2)
+        assert rel_err(got, ref) <= 1e-5, (f1, f2, rel_err(got, ref))
+    plain, _ = torch_block_f64(cfg, w, x, bf16=True)
+    folded, _ = torch_block_f64(cfg, w, x, bf16=True, fold1=9, fold2=9)
+    assert not np.array_equal(plain, folded)
+    assert rel_err(folded, plain) <= 2e-2
+
+
 def test_prefix_invariance_bitwise(oracle):
     """[TIR] Code test: a prefix gives the same outputs as the full sequence.
     Exact here (the page asserts 1e-5)."""

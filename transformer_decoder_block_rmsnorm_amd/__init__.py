@@ -31,7 +31,8 @@ _VP = ctypes.c_void_p
 class BlockConfig(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rope_base", ctypes.c_float),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("fold_norms", ctypes.c_int32)]
 
 
 class BlockWeights(ctypes.Structure):
@@ -151,6 +152,7 @@ class Config:
     rms_eps: float = 1e-6
     dtype: str = "bf16"
     window: int = 0  # sliding-window attention: keys per query (0 = full causal)
+    fold_norms: int = 0  # fold RMSNorms that follow a GEMM into the GEMMs around them (bf16, > 64 rows)
 
     @property
     def head_dim(self) -> int:
@@ -158,12 +160,13 @@ class Config:
 
     def c(self) -> BlockConfig:
         return BlockConfig(self.d, self.n_heads, self.n_kv_heads, self.head_dim, self.d_ff, self.rope_base,
-                           self.rms_eps, TFB_BF16 if self.dtype == "bf16" else TFB_F32, self.window)
+                           self.rms_eps, TFB_BF16 if self.dtype == "bf16" else TFB_F32, self.window,
+                           self.fold_norms)
 
     @staticmethod
-    def of(obj) -> "Config":
+    def of(obj, fold_norms: int = 0) -> "Config":
         return Config(obj.d, obj.n_heads, obj.n_kv_heads, obj.d_ff, obj.rope_base, obj.rms_eps, obj.dtype,
-                      int(getattr(obj, "window", 0)))
+                      int(getattr(obj, "window", 0)), fold_norms)
 
 
 def weights_struct(w: dict) -> BlockWeights:

@@ -26,8 +26,15 @@ inline size_t esize(int dtype) { return dtype == TFB_BF16 ? 2 : 4; }
 constexpr int kMaxSplits = 64;
 
 struct WsLayout {
-    size_t h, q, att, r, act, kv_k, kv_v, part, part_bytes, skinny, skinny_bytes, gsplit, gsplit_bytes, x0, x1, last,
-        logits, total;
+    size_t h, q, att, r, act, kv_k, kv_v, part, part_bytes, skinny, skinny_bytes, gsplit, gsplit_bytes, rss,
+        rss_bytes, x0, x1, last, logits, total;
+};
+
+// A folded RMSNorm in flight between two large-M GEMMs: h holds bf16(x * g)
+// and ss [M][parts] the partial sums of x^2 that the next GEMM adds up.
+struct FoldedNorm {
+    const float *ss;
+    int parts;  // 0: nothing folded
 };
 
 // part_bytes: room for the decode-attention partials; the default holds
@@ -79,6 +86,11 @@ WsLayout ws_layout(const tfb_block_config &c, int B, int T, int vocab, size_t pa
             L.gsplit_bytes = gs;
             L.gsplit = take(gs);
         }
+    }
+    if (c.fold_norms && c.dtype == TFB_BF16 && M > (size_t)kSkinnyMaxM) {
+        // partial sums of squares of a folded RMSNorm (large-M GEMMs)
+        L.rss_bytes = M * kRowSsMaxParts * sizeof(float);
+        L.rss = take(L.rss_bytes);
     }
     if (vocab > 0) {
         L.x0 = take(M * c.d * es);
@@ -179,10 +191,21 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
                      int max_pos, const void *x, void *out, int B, int T, int start, const int32_t *pos, void *kc,
                      void *vc, const KvMap &kvm, uint8_t *ws, const WsLayout &L, hipStream_t s,
                      const int32_t *starts = nullptr, const int32_t *lens = nullptr, bool h_ready = false,
-                     const void *next_g = nullptr) {
+                     const void *next_g = nullptr, const FoldedNorm *h_fold = nullptr,
+                     FoldedNorm *next_fold = nullptr) {
     // h_ready: h in the workspace already holds RMSNorm1(x) (written by the
     // previous layer's W2 step).  next_g: on the skinny path, the W2 step also
     // writes RMSNorm(out) with this gain into h for whoever reads h next.
+    // h_fold (large-M path): h holds RMSNorm1's folded operand bf16(x * g_attn)
+    // instead, with its row sums.  next_fold (large-M path, with next_g): the
+    // W2 step folds the next norm into its epilogue and says so here.
+    //
+    // With fold_norms, on the large-M bf16 path RMSNorm2 is folded: the Wo
+    // epilogue writes bf16(r * g_mlp) and per-tile sums of r^2, and the
+    // gate-up GEMM scales each row's products by 1/rms(r) before SiLU.  The
+    // norm's row scale distributes over the GEMM (row m of h W is
+    // s_m (x_m * g) W), so only the place where the operand is rounded to
+    // bf16 moves.  (The workspace holds the sums only with fold_norms.)
     // cache rows: contiguous [B, Hkv, t_max, dh], or a paged pool and block
     // table; a bounded window cache is only ever passed here for decode
     const int t_max = kvm.t_max;
@@ -190,8 +213,12 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     const int qd = H * dh, kvd = Hkv * dh;
     void *h = ws + L.h, *q = ws + L.q, *att = ws + L.att, *r = ws + L.r, *act = ws + L.act;
 
-    if (!h_ready) TRY_HIP(STAGE(ST_RMSNORM_ATTN, rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s)));
+    const bool folded_in = h_fold && h_fold->parts > 0;
+    if (!h_ready && !folded_in)
+        TRY_HIP(STAGE(ST_RMSNORM_ATTN, rmsnorm_launch(c.dtype, x, d, w.g_attn, h, d, M, d, c.rms_eps, s)));
     const bool fuse = norms_fuse(c, M, L);
+    float *rss = L.rss_bytes ? (float *)(ws + L.rss) : nullptr;
+    const int mlp_parts = rss ? gemm_fold_parts(M, d, qd) : 0;
 
     AttnCall a{};
     a.dtype = c.dtype;
@@ -232,6 +259,11 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     g.scratch_bytes = L.skinny_bytes;
     g.split_scratch = L.gsplit_bytes ? ws + L.gsplit : nullptr;
     g.split_bytes = L.gsplit_bytes;
+    if (folded_in) {
+        g.row_ss = h_fold->ss;
+        g.row_ss_n = h_fold->parts;
+        g.row_ss_eps = c.rms_eps;
+    }
     // decode on the split attention kernel: the QKV GEMM leaves its split-K
     // partials, and the attention kernel reduces them (q, RoPE, the new cache
     // rows) instead of a separate reduce pass
@@ -280,10 +312,15 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
         o.norm_g = w.g_mlp;
         o.norm_out = h;
         o.norm_eps = c.rms_eps;
+    } else if (mlp_parts) {  // RMSNorm2 folded into the Wo epilogue and the gate-up
+        o.norm_g = w.g_mlp;
+        o.norm_out = h;
+        o.norm_ss = rss;
     }
     TRY_HIP(STAGE(ST_WO, gemm_launch(o, s)));
 
-    if (!fuse) TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
+    if (!fuse && !mlp_parts)
+        TRY_HIP(STAGE(ST_RMSNORM_MLP, rmsnorm_launch(c.dtype, r, d, w.g_mlp, h, d, M, d, c.rms_eps, s, true)));
 
     GemmCall gu{};
     gu.dtype = c.dtype;
@@ -295,6 +332,11 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
     gu.scratch_bytes = g.scratch_bytes;
     gu.split_scratch = g.split_scratch;
     gu.split_bytes = g.split_bytes;
+    if (mlp_parts) {
+        gu.row_ss = rss;
+        gu.row_ss_n = mlp_parts;
+        gu.row_ss_eps = c.rms_eps;
+    }
     TRY_HIP(STAGE(ST_GATEUP, gemm_launch(gu, s)));
 
     GemmCall dn{};
@@ -312,6 +354,13 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
         dn.norm_out = h;
         dn.norm_eps = c.rms_eps;
     }
+    const int next_parts = (rss && next_g && next_fold) ? gemm_fold_parts(M, d, f) : 0;
+    if (next_parts) {  // the next RMSNorm folded into the W2 epilogue
+        dn.norm_g = next_g;
+        dn.norm_out = h;
+        dn.norm_ss = rss;
+    }
+    if (next_fold) *next_fold = FoldedNorm{rss, next_parts};
     TRY_HIP(STAGE(ST_W2, gemm_launch(dn, s)));
     return TFB_OK;
 }
@@ -328,16 +377,17 @@ tfb_status run_block(const tfb_block_config &c, const tfb_block_weights &w, cons
 tfb_status run_prefill(const tfb_block_config &c, const tfb_block_weights &w, const float *rope, int rope_rows,
                        const void *x, void *out, int B, int T, int start, void *kc, void *vc, const KvMap &kvm,
                        uint8_t *ws, const WsLayout &L, hipStream_t s, bool h_ready = false,
-                       const void *next_g = nullptr) {
+                       const void *next_g = nullptr, const FoldedNorm *h_fold = nullptr,
+                       FoldedNorm *next_fold = nullptr) {
     const int hist = kvm.ring ? std::min(start, c.window - 1) : 0;
     if (!kvm.ring || (int64_t)T + hist <= kvm.ring)
         return run_block(c, w, rope, rope_rows, 0, x, out, B, T, start, nullptr, kc, vc, kvm, ws, L, s, nullptr,
-                         nullptr, h_ready, next_g);
+                         nullptr, h_ready, next_g, h_fold, next_fold);
     const KvMap stg{nullptr, T + hist, 0, 0, 0, start - hist, 0};
     void *sk = ws + L.kv_k, *sv = ws + L.kv_v;
     TRY_HIP(kv_copy_launch(c.dtype, kc, vc, kvm, sk, sv, stg, B, c.n_kv_heads, c.head_dim, start - hist, hist, s));
     const tfb_status st = run_block(c, w, rope, rope_rows, 0, x, out, B, T, start, nullptr, sk, sv, stg, ws, L, s,
-                                    nullptr, nullptr, h_ready, next_g);
+                                    nullptr, nullptr, h_ready, next_g, h_fold, next_fold);
     if (st != TFB_OK) return st;
     const int n = std::min(T, kvm.ring);
     TRY_HIP(kv_copy_launch(c.dtype, sk, sv, stg, kc, vc, kvm, B, c.n_kv_heads, c.head_dim, start + T - n, n, s));
@@ -686,18 +736,26 @@ tfb_status tfb_model_forward(const tfb_model *model, const float *rope_table, in
     // every row.
     const bool fuse = norms_fuse(c, M, L);
     const bool final_fused = fuse && (logits || next_ids) && !(last_only && T > 1);
+    // On the large-M path each layer's W2 epilogue folds the next layer's
+    // RMSNorm1 (the final norm stays a pass of its own).
+    const bool fold = L.rss_bytes > 0;
+    FoldedNorm fold_in{nullptr, 0}, fold_out{nullptr, 0};
     for (int l = 0; l < model->n_layers; ++l) {
         const bool last = l + 1 == model->n_layers;
-        const void *next_g = !fuse ? nullptr : (last ? (final_fused ? model->g_final : nullptr) : model->layers[l + 1].g_attn);
+        const void *next_g = last ? (final_fused ? model->g_final : nullptr)
+                                  : ((fuse || fold) ? model->layers[l + 1].g_attn : nullptr);
         const bool h_ready = fuse && l > 0;
         const KvMap kvm = contig_map(caches[l]);
+        fold_out = FoldedNorm{nullptr, 0};
         if (T > 1)
             st = run_prefill(c, model->layers[l], rope_table, t_max_table, cur, nxt, B, T, 0, caches[l].k, caches[l].v,
-                             kvm, wsb, L, s, h_ready, next_g);
+                             kvm, wsb, L, s, h_ready, next_g, &fold_in, fold && !last ? &fold_out : nullptr);
         else
             st = run_block(c, model->layers[l], rope_table, t_max_table, h_max_len, cur, nxt, B, 1, 0, lens,
-                           caches[l].k, caches[l].v, kvm, wsb, L, s, nullptr, nullptr, h_ready, next_g);
+                           caches[l].k, caches[l].v, kvm, wsb, L, s, nullptr, nullptr, h_ready, next_g, &fold_in,
+                           fold && !last ? &fold_out : nullptr);
         if (st != TFB_OK) return st;
+        fold_in = fold_out;
         void *tmp = cur; cur = nxt; nxt = tmp;
     }
     // Final norm and untied LM head ([TIR] How it works step 4), fp32 logits.

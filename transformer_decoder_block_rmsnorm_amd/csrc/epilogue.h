@@ -29,7 +29,52 @@ struct EpiParams {
     KvMap kvm;               // cache row addressing (contiguous or paged)
     int rope_rows;           // rows of the RoPE table (device positions are clamped to it)
     int vec8;                // set by the GEMM launcher: 8-column groups may use 16-byte accesses
+    // RESID on the large-M bf16 GEMM, with the next RMSNorm folded in (nu
+    // non-null): besides y, write nu[m, c] = bf16(y[m, c] * ng[c]) and, per
+    // row and column tile of the launch, the sum of y^2 over the tile's
+    // columns to nss[m * nss_n + tile] (y as stored: rounded to bf16 unless
+    // out_f32).  The GEMM that takes nu as its A operand applies the row
+    // scale 1 / sqrt(sum / N + eps) to its products.
+    const bf16_t *ng;
+    bf16_t *nu;
+    int64_t ldu;
+    float *nss;
+    int nss_n;
 };
+
+// Eight consecutive bf16 values -> one 16-byte store.
+// Output stores of the epilogues take the nontemporal policy: a round of
+// GEMM tiles writes about an L2's worth of output per XCD, which would
+// otherwise push out the operand panels the next tiles read (the long-context
+// step ran ~0.35% faster this way; decode unchanged).
+__device__ __forceinline__ void store_bf16x8(bf16_t *dst, const float (&v)[8]) {
+    u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(w, (u32x4 *)dst);
+}
+// y as the RESID epilogue stored it: fp32, or rounded to the storage type.
+__device__ __forceinline__ float as_stored(const EpiParams &p, float y) {
+    return p.out_f32 ? y : bf16_lo(pack_bf16x2(y, 0.0f));
+}
+
+// The folded norm's part of one 8-column group of row m: nu = bf16(y * g)
+// (gains g of the group's columns, already widened) and the group's sum of
+// y^2, returned.  Groups are whole inside the output here (the launcher
+// folds the norm only when every group is).
+__device__ __forceinline__ float epi_norm8(const EpiParams &p, int m, int c, const float (&y)[8],
+                                           const float (&g)[8]) {
+    if (m >= p.M) return 0.0f;
+    float u[8], ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        u[k] = y[k] * g[k];
+        ss += y[k] * y[k];
+    }
+    // plain stores: the next GEMM reads these rows right away, many times
+    // over, and they should stay in the caches for it
+    *(u32x4 *)(p.nu + (int64_t)m * p.ldu + c) =
+        u32x4{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]), pack_bf16x2(u[6], u[7])};
+    return ss;
+}
 
 // Position of output row m (token t of sequence b).
 __device__ __forceinline__ void qkv_row(const EpiParams &p, int m, int &b, int &t, int &ps) {
@@ -99,15 +144,6 @@ __device__ __forceinline__ void epi_store_pair(const EpiParams &p, int m, int c,
     }
 }
 
-// Eight consecutive bf16 values -> one 16-byte store.
-// Output stores of the epilogues take the nontemporal policy: a round of
-// GEMM tiles writes about an L2's worth of output per XCD, which would
-// otherwise push out the operand panels the next tiles read (the long-context
-// step ran ~0.35% faster this way; decode unchanged).
-__device__ __forceinline__ void store_bf16x8(bf16_t *dst, const float (&v)[8]) {
-    u32x4 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-    __builtin_nontemporal_store(w, (u32x4 *)dst);
-}
 __device__ __forceinline__ void load_bf16x8(const bf16_t *src, float (&v)[8]) {
     const u32x4 w = *(const u32x4 *)src;
 #pragma unroll
@@ -123,8 +159,11 @@ __device__ __forceinline__ void load_bf16x8(const bf16_t *src, float (&v)[8]) {
 // group that is not whole inside the output, or a launch without vec8, goes
 // through the pairwise path, which checks each column.  KIND == EPI_SWIGLU
 // takes the finished SiLU(gate) * up values.
+// y (RESID with a folded norm, p.nu): receives the values as stored; only the
+// 16-byte path fills it (the launcher folds a norm only where every group
+// takes that path).
 template <int KIND>
-__device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, const float (&v)[8]) {
+__device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, const float (&v)[8], float (&y)[8]) {
     if (!p.vec8 || c + 8 > p.N) {
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
@@ -153,6 +192,9 @@ __device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, con
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) r[k] += v[k];
+        if (p.nu)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) y[k] = as_stored(p, r[k]);
         if (p.out_f32) {
             float *o = (float *)p.out + io;
             __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, (f32x4 *)o);
@@ -198,6 +240,12 @@ __device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, con
             store_bf16x8(dst + kv_row(p.kvm, b, p.Hkv, g, ps) * p.dh + e, w);
         }
     }
+}
+
+template <int KIND>
+__device__ __forceinline__ void epi_store8(const EpiParams &p, int m, int c, const float (&v)[8]) {
+    float y[8];
+    epi_store8<KIND>(p, m, c, v, y);
 }
 
 // What the epilogue of one 8-column group reads from memory besides the
@@ -271,7 +319,7 @@ __device__ __forceinline__ void epi_load8_lane(const EpiParams &p, const EpiLane
 
 template <int KIND>
 __device__ __forceinline__ void epi_store8_lane(const EpiParams &p, const EpiLane &L, const float (&v)[8],
-                                                const EpiPre &pre) {
+                                                const EpiPre &pre, float (&y)[8]) {
     if constexpr (KIND == EPI_SWIGLU) {
         store_bf16x8((bf16_t *)p.out + (int64_t)L.m * p.ldo + L.c, v);
     } else if constexpr (KIND == EPI_RESID) {
@@ -290,6 +338,9 @@ __device__ __forceinline__ void epi_store8_lane(const EpiParams &p, const EpiLan
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) r[k] += v[k];
+        if (p.nu)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) y[k] = as_stored(p, r[k]);
         if (p.out_f32) {
             float *o = (float *)p.out + io;
             __builtin_nontemporal_store(f32x4{r[0], r[1], r[2], r[3]}, (f32x4 *)o);
@@ -331,6 +382,13 @@ template <typename T>
 __device__ __forceinline__ void epi_store_swiglu(const EpiParams &p, int m, int c, float gate, float up) {
     if (m >= p.M || c >= p.N) return;
     Elem<T>::store((T *)p.out, (int64_t)m * p.ldo + c, silu_f(gate) * up);
+}
+
+template <int KIND>
+__device__ __forceinline__ void epi_store8_lane(const EpiParams &p, const EpiLane &L, const float (&v)[8],
+                                                const EpiPre &pre) {
+    float y[8];
+    epi_store8_lane<KIND>(p, L, v, pre, y);
 }
 
 }  // namespace tfb

@@ -48,7 +48,15 @@ struct GemmArgs {
     // them in a fixed order and applies the epilogue
     int full_tiles, splits;
     float *part;        // [tiles - full_tiles][splits][BM][BN]
+    // A folded RMSNorm (rss non-null): the A rows are bf16(x * gain), and
+    // rss [M][rss_n] holds partial sums of x^2 over column tiles of x, added
+    // here in order; the products of row m are scaled by
+    // 1 / sqrt(sum / rss_d + rss_eps) before the epilogue.
+    const float *rss;
+    int rss_n, rss_d;
+    float rss_eps;
 };
+
 
 // Workgroups are dealt to the 8 XCDs round robin.  xcd_remap gives each XCD a
 // contiguous run of n consecutive logical indices (n a multiple of 8), so the
@@ -97,7 +105,12 @@ __device__ __forceinline__ void wg_work(const GemmArgs &g, int bid, int &tile, i
 // makes every wave's slots visible.  The MFMAs of one 16-wide k half run
 // while the fragments of the next half are read from LDS.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int SRC, int EPI>
+// NORM: a folded RMSNorm.  0 none; NORM_SCALE: A holds bf16(x * gain) and
+// g.rss the row sums (the row scale is applied to the products); NORM_FOLD
+// (RESID): the epilogue folds the next norm (ep.nu).  Separate instances, so
+// the plain kernels carry none of the extra registers.
+enum NormKind { NORM_NONE = 0, NORM_SCALE = 1, NORM_FOLD = 2 };
+template <int BM, int BN, int WM, int WN, int SRC, int EPI, int NORM>
 __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, EpiParams ep) {
     constexpr int NW = WM * WN, NT = NW * 64;
     constexpr int BKD = 32, NST = 4;  // ring stages of BKD k each
@@ -151,10 +164,16 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
             int sidx = 0, c2 = cglob;
             if (c2 >= g.w_cols[0]) { c2 -= g.w_cols[0]; sidx = 1; if (c2 >= g.w_cols[1]) { c2 -= g.w_cols[1]; sidx = 2; } }
             if (sidx == 2 && c2 >= g.w_cols[2]) c2 = g.w_cols[2] - 8;  // ragged tail: a valid, unused column
-            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = c2;
+            // selects rather than an index into the argument arrays, which
+            // the compiler would load per lane from memory
+            base = (const bf16_t *)(sidx == 0 ? g.w[0] : (sidx == 1 ? g.w[1] : g.w[2]));
+            ld = sidx == 0 ? g.w_cols[0] : (sidx == 1 ? g.w_cols[1] : g.w_cols[2]);
+            col = c2;
         } else {
             const int sidx = (cglob >> 5) & 1;
-            base = (const bf16_t *)g.w[sidx]; ld = g.w_cols[sidx]; col = 32 * (cglob >> 6) + (cglob & 31);
+            base = (const bf16_t *)(sidx ? g.w[1] : g.w[0]);
+            ld = sidx ? g.w_cols[1] : g.w_cols[0];
+            col = 32 * (cglob >> 6) + (cglob & 31);
         }
         if (col >= ld) col = ld - 8;  // ragged tail: a valid column whose outputs are never stored
         b_ld[j] = ld;
@@ -247,6 +266,36 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     // barrier.  Stage s lives in ring slot s % NST; all NST slots are filled
     // ahead, and a slot is refilled right after the barrier that follows the
     // last read of its stage.
+    // Folded norm: the partial sums of the tile's rows are one contiguous
+    // block of BM * rss_n floats; thread t loads half of row t / 2 (the
+    // halves of a row sit in adjacent lanes), with 16-byte loads when the
+    // halves are whole 16-byte groups, so the loads coalesce.  They are
+    // issued right before the operand stream starts (the empty asm keeps
+    // them after the setup above) and added after the main loop, whose last
+    // wait has drained every load.  Indexes are clamped into the row, so the
+    // loads are unconditional and issue together.
+    constexpr int RS_MAX = kRowSsMaxParts / 2;
+    static_assert(NT == 2 * BM, "two threads per tile row");
+    __shared__ float rs_scale[BM];
+    const int rs_row = tid >> 1, rs_half = tid & 1;
+    f32x4 rsv[RS_MAX / 4];
+    int rs_cnt = 0;
+    asm volatile("" ::: "memory");
+    if constexpr (NORM == NORM_SCALE) {
+        const int per = (g.rss_n + 1) / 2, j0 = rs_half * per;
+        rs_cnt = min(per, g.rss_n - j0);
+        const float *row = g.rss + (int64_t)min(m0 + rs_row, g.M - 1) * g.rss_n;
+        if (g.rss_n % 8 == 0) {
+#pragma unroll
+            for (int q = 0; q < RS_MAX / 4; ++q)
+                rsv[q] = *(const f32x4 *)(row + j0 + min(4 * q, per - 4));
+        } else {
+#pragma unroll
+            for (int q = 0; q < RS_MAX / 4; ++q)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) rsv[q][k] = row[min(j0 + 4 * q + k, g.rss_n - 1)];
+        }
+    }
 #pragma unroll
     for (int st = 0; st < NST; ++st)
         if (st < KT) issue(st, st);
@@ -284,7 +333,36 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     first_product(fa1, fb1);
     other_products(fa1, fb1);
     wait_vmcnt<0>();
+    if constexpr (NORM == NORM_SCALE) {
+        // each half in order, then the two halves (adjacent lanes); 1/rms of
+        // the row by the same expression as a standalone RMSNorm
+        // (the empty asm keeps the additions here, after the loop, rather
+        // than next to the loads, where they would wait for each load)
+        float part = 0.0f;
+#pragma unroll
+        for (int q = 0; q < RS_MAX / 4; ++q) {
+            asm volatile("" : "+v"(rsv[q]));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) part += 4 * q + k < rs_cnt ? rsv[q][k] : 0.0f;
+        }
+        const float other = __shfl_xor(part, 1);
+        const float sum = rs_half ? other + part : part + other;
+        if (!rs_half) rs_scale[rs_row] = 1.0f / sqrtf(sum / (float)g.rss_d + g.rss_eps);
+    }
     __syncthreads();  // every wave is done with the ring before it is reused for staging
+    if constexpr (NORM == NORM_SCALE) {
+        // every product of a row is scaled by its 1/rms
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 sv = *(const f32x4 *)(rs_scale + wm * WTM + i * 32 + 8 * q4 + 4 * lh);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j][4 * q4 + k] *= sv[k];
+            }
+    }
 
     // Epilogue, one 32-row slab of the wave tile at a time: the accumulators
     // go through LDS (row stride SW floats) so that each lane then holds 8
@@ -314,6 +392,23 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     // SwiGLU epilogue reads nothing and stays on the general path, which
     // measured slightly faster for it.
     const bool whole = EPI != EPI_SWIGLU && split < 0 && ep.vec8 && m0 + BM <= ep.M && n0 + BN <= ep.N;
+    // A folded RMSNorm of the output (RESID with ep.nu): each group's sum of
+    // y^2 is added over the lanes of its row (a fixed butterfly), each wave
+    // leaves its rows' sums in LDS past the staging area, and after the
+    // epilogue the WN sums of a row are added in wave order.  A lane's
+    // columns are the same in every group, so it widens its gains once.
+    const bool fold = NORM == NORM_FOLD && split < 0;
+    static_assert((NW * 32 * SW + WN * BM) * 4 <= NST * STAGE * 2, "row sums fit past the staging area");
+    float *ssl = (float *)lds + NW * 32 * SW;  // [WN][BM]
+    float gn[8];
+    if constexpr (NORM == NORM_FOLD)
+        if (fold) load_bf16x8(ep.ng + c0 + 8 * (lane % SEGS), gn);
+    auto fold_group = [&](int row_local, int m, int c, const float (&y)[8]) {
+        float ss = epi_norm8(ep, m, c, y, gn);
+#pragma unroll
+        for (int o = SEGS / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if (lane % SEGS == 0) ssl[wn * BM + row_local] = ss;
+    };
     if (whole) {
         EpiLane L;
         const int rbase = m0 + wm * WTM + lane / SEGS;  // the lane's first row; rows step by 64 / SEGS
@@ -346,54 +441,75 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
                 float v8[8];
                 read8(stage + rl * SW + 8 * sg, sg, v8);
                 epi_lane_seek<EPI>(ep, rbase + i * 32 + r * RSTEP, L);
-                epi_store8_lane<EPI>(ep, L, v8, pre[r]);
+                if constexpr (EPI == EPI_RESID) {
+                    float y8[8];
+                    epi_store8_lane<EPI>(ep, L, v8, pre[r], y8);
+                    if (fold) fold_group(wm * WTM + i * 32 + rl, L.m, L.c, y8);
+                } else {
+                    epi_store8_lane<EPI>(ep, L, v8, pre[r]);
+                }
             }
             if (i + 1 < TM)
 #pragma unroll
                 for (int r = 0; r < NG; ++r) pre[r] = nxt[r];
             __builtin_amdgcn_wave_barrier();
         }
-        return;
+    } else {
+        // Edge tiles and split-K partials: each group checks its own bounds.
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int row0 = m0 + wm * WTM + i * 32;
+            if (split >= 0 || EPI != EPI_SWIGLU) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * SW + j * 32 + lr] = acc[i][j][v];
+            } else {
+#pragma unroll
+                for (int jp = 0; jp < TN / 2; ++jp)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * SW + jp * 32 + lr] =
+                            silu_f(acc[i][2 * jp][v]) * acc[i][2 * jp + 1][v];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (split >= 0) {
+                // split tail: raw fp32 partial of this k range, tile-local layout
+                float *dst = g.part + ((int64_t)(tile - g.full_tiles) * g.splits + split) * (BM * BN) +
+                             (wm * WTM + i * 32) * BN + wn * WTN;
+#pragma unroll
+                for (int r = 0; r < 32 * WTN / 4 / 64; ++r) {
+                    const int p = r * 64 + lane, rl = p / (WTN / 4), c4 = p % (WTN / 4);
+                    *(f32x4 *)(dst + rl * BN + 4 * c4) = *(const f32x4 *)(stage + rl * SW + 4 * c4);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < NG; ++r) {
+                    const int p = r * 64 + lane, rl = p / SEGS, sg = p % SEGS;
+                    float v8[8];
+                    read8(stage + rl * SW + 8 * sg, sg, v8);
+                    if constexpr (EPI == EPI_RESID) {
+                        float y8[8];
+                        epi_store8<EPI>(ep, row0 + rl, c0 + 8 * sg, v8, y8);
+                        if (fold) fold_group(wm * WTM + i * 32 + rl, row0 + rl, c0 + 8 * sg, y8);
+                    } else {
+                        epi_store8<EPI>(ep, row0 + rl, c0 + 8 * sg, v8);
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
     }
-    // Edge tiles and split-K partials: each group checks its own bounds.
+    if (fold) {
+        __syncthreads();
+        for (int row = tid; row < BM; row += NT) {
+            float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row0 = m0 + wm * WTM + i * 32;
-        if (split >= 0 || EPI != EPI_SWIGLU) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * SW + j * 32 + lr] = acc[i][j][v];
-        } else {
-#pragma unroll
-            for (int jp = 0; jp < TN / 2; ++jp)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    stage[(8 * (v >> 2) + 4 * lh + (v & 3)) * SW + jp * 32 + lr] =
-                        silu_f(acc[i][2 * jp][v]) * acc[i][2 * jp + 1][v];
+            for (int w = 0; w < WN; ++w) sum += ssl[w * BM + row];
+            if (m0 + row < ep.M) ep.nss[(int64_t)(m0 + row) * ep.nss_n + tn] = sum;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (split >= 0) {
-            // split tail: raw fp32 partial of this k range, tile-local layout
-            float *dst = g.part + ((int64_t)(tile - g.full_tiles) * g.splits + split) * (BM * BN) +
-                         (wm * WTM + i * 32) * BN + wn * WTN;
-#pragma unroll
-            for (int r = 0; r < 32 * WTN / 4 / 64; ++r) {
-                const int p = r * 64 + lane, rl = p / (WTN / 4), c4 = p % (WTN / 4);
-                *(f32x4 *)(dst + rl * BN + 4 * c4) = *(const f32x4 *)(stage + rl * SW + 4 * c4);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < NG; ++r) {
-                const int p = r * 64 + lane, rl = p / SEGS, sg = p % SEGS;
-                float v8[8];
-                read8(stage + rl * SW + 8 * sg, sg, v8);
-                epi_store8<EPI>(ep, row0 + rl, c0 + 8 * sg, v8);
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -510,6 +626,21 @@ __global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiPa
         for (int k = 0; k < 4; ++k) epi_store_swiglu<bf16_t>(ep, m, lc + k, v[k], u[k]);
     } else {
         const float v8[8] = {v[0], v[1], v[2], v[3], u[0], u[1], u[2], u[3]};
+        if constexpr (EPI == EPI_RESID) {
+            if (ep.nu) {
+                // folded norm: the BN / 8 threads of a row are consecutive
+                // lanes; their sums of y^2 are added by a fixed butterfly
+                const int c = tn * BN + col;
+                float y8[8], gn[8];
+                epi_store8<EPI>(ep, m, c, v8, y8);
+                load_bf16x8(ep.ng + c, gn);
+                float ss = epi_norm8(ep, m, c, y8, gn);
+#pragma unroll
+                for (int o = BN / 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+                if (col == 0 && m < ep.M) ep.nss[(int64_t)m * ep.nss_n + tn] = ss;
+                return;
+            }
+        }
         epi_store8<EPI>(ep, m, tn * BN + col, v8);
     }
 }
@@ -534,10 +665,15 @@ static SplitPlan plan_split(int tiles, int k_steps, int cus, int tile_elems) {
 }
 
 template <int BM, int BN, int WM, int WN, int SRC, int EPI>
-static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, void *part, size_t part_bytes, hipStream_t s) {
+static hipError_t launch_dma(GemmArgs g, EpiParams ep, void *part, size_t part_bytes, hipStream_t s) {
     g.tiles_m = (g.M + BM - 1) / BM;
     g.tiles_n = (g.N + BN - 1) / BN;
     g.group_m = 8;
+    if (ep.nu) {  // a folded norm: one partial sum of squares per row and column tile
+        if (EPI != EPI_RESID || !ep.vec8 || ep.N % 8 || g.tiles_n > kRowSsMaxParts) return hipErrorInvalidValue;
+        ep.nss_n = g.tiles_n;
+    }
+    if (g.rss && (g.rss_n < 1 || g.rss_n > kRowSsMaxParts)) return hipErrorInvalidValue;
     const int tiles = g.tiles_m * g.tiles_n;
     SplitPlan sp = plan_split(tiles, g.K / 32, device_cus(), BM * BN);
     if (!part || sp.part_bytes > part_bytes) sp = SplitPlan{tiles, 1, 0};
@@ -545,8 +681,25 @@ static hipError_t launch_dma(GemmArgs g, const EpiParams &ep, void *part, size_t
     g.splits = sp.splits;
     g.part = (float *)part;
     const int blocks = sp.full_tiles + (tiles - sp.full_tiles) * sp.splits;
-    hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI>), dim3(blocks), dim3(WM * WN * 64), 0, s,
-                       g, ep);
+    if constexpr (EPI == EPI_RESID) {
+        if (ep.nu)
+            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI, NORM_FOLD>), dim3(blocks),
+                               dim3(WM * WN * 64), 0, s, g, ep);
+        else
+            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI, NORM_NONE>), dim3(blocks),
+                               dim3(WM * WN * 64), 0, s, g, ep);
+    } else if constexpr (EPI == EPI_SWIGLU || EPI == EPI_QKV) {
+        if (g.rss)
+            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI, NORM_SCALE>), dim3(blocks),
+                               dim3(WM * WN * 64), 0, s, g, ep);
+        else
+            hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI, NORM_NONE>), dim3(blocks),
+                               dim3(WM * WN * 64), 0, s, g, ep);
+    } else {
+        if (g.rss) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_bf16_dma_kernel<BM, BN, WM, WN, SRC, EPI, NORM_NONE>), dim3(blocks),
+                           dim3(WM * WN * 64), 0, s, g, ep);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || sp.splits == 1) return e;
     dim3 fg((BM * BN / (EPI == EPI_SWIGLU ? 4 : 8) + 255) / 256, tiles - sp.full_tiles);
@@ -584,6 +737,13 @@ static TilePlan plan_tiles(int M, int N_virtual, int K) {
     return c128 < c256 ? T_256x128 : T_256;
 }
 
+int gemm_fold_parts(int M, int N, int K) {
+    if (M <= kSkinnyMaxM || N % 8) return 0;
+    const int bn = plan_tiles(M, N, K) == T_256 ? 256 : 128;
+    const int parts = (N + bn - 1) / bn;
+    return parts <= kRowSsMaxParts ? parts : 0;
+}
+
 size_t gemm_split_bytes(int M, int N_virtual, int K) {
     if (M <= kSkinnyMaxM || plan_tiles(M, N_virtual, K) != T_256) return 0;
     const int tiles = ((M + 255) / 256) * ((N_virtual + 255) / 256);
@@ -609,7 +769,23 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s) {
     g.M = c.M;
     g.K = c.K;
     for (int i = 0; i < 3; ++i) { g.w[i] = c.w[i]; g.w_cols[i] = c.w_cols[i]; }
+    g.rss = c.row_ss;
+    g.rss_n = c.row_ss_n;
+    g.rss_d = c.K;
+    g.rss_eps = c.row_ss_eps;
     EpiParams ep = c.ep;
+    ep.ng = nullptr;
+    ep.nu = nullptr;
+    ep.nss = nullptr;
+    if (c.norm_ss) {  // fold the next RMSNorm (large-M path only)
+        if (c.dtype != TFB_BF16 || c.M <= kSkinnyMaxM || c.epi != EPI_RESID || !c.norm_g || !c.norm_out)
+            return hipErrorInvalidValue;
+        ep.ng = (const bf16_t *)c.norm_g;
+        ep.nu = (bf16_t *)c.norm_out;
+        ep.ldu = c.ep.N;
+        ep.nss = c.norm_ss;
+    }
+    if (c.row_ss && (c.dtype != TFB_BF16 || c.M <= kSkinnyMaxM)) return hipErrorInvalidValue;
     // 16-byte epilogue accesses need every 8-column group to start 16-byte
     // aligned: leading dimensions in elements, and whole groups inside one head
     switch (c.epi) {

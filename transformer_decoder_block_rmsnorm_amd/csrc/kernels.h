@@ -46,6 +46,18 @@ struct GemmCall {
     // EPI_RESID on the skinny path only: the activations A are the decode
     // attention's chunk partials (see skinny_takes_attn_chunks); A is unused
     const AttnChunks *attn_chunks;
+    // EPI_RESID on the large-M bf16 path (M > kSkinnyMaxM): fold the next
+    // RMSNorm (gain norm_g).  The epilogue writes bf16(y * norm_g) to
+    // norm_out [M, N] and gemm_fold_parts(M, N, K) partial sums of y^2 per
+    // row to norm_ss [M][parts]; the GEMM that reads norm_out passes them
+    // as row_ss.
+    float *norm_ss;
+    // Large-M bf16 path: A holds bf16(x * gain) of a folded RMSNorm, row_ss
+    // [M][row_ss_n] the partial sums of x^2 over the K columns; the products
+    // of each row are scaled by 1 / sqrt(sum / K + row_ss_eps).
+    const float *row_ss;
+    int row_ss_n;
+    float row_ss_eps;
 };
 constexpr int kSkinnyNormMaxN = 8192;
 // Compute units of the current device (queried once per device; 256 if the
@@ -55,6 +67,12 @@ hipError_t gemm_launch(const GemmCall &c, hipStream_t s);
 // Scratch the large-M bf16 GEMM uses for its split-K tail (0: none); with
 // less, it runs without splitting.  N_virtual: B columns (gate-up: 2 f).
 size_t gemm_split_bytes(int M, int N_virtual, int K);
+// Most partial sums of squares per row a folded norm may bring (two threads
+// of a GEMM workgroup load a row's partials, kRowSsMaxParts / 2 each).
+constexpr int kRowSsMaxParts = 32;
+// Partial sums of squares per row that a RESID GEMM of this shape writes when
+// it folds the next RMSNorm (0: it cannot fold one).
+int gemm_fold_parts(int M, int N, int K);
 // Skinny (M <= 64) weight-streaming GEMM with split-K partials in `part`.
 constexpr int kSkinnyMaxM = 64;
 hipError_t skinny_gemm_launch(const GemmCall &c, void *part, size_t part_bytes, hipStream_t s);
