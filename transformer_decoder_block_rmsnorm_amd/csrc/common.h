@@ -189,6 +189,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16_t *p) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// A wave-uniform value as a scalar register (read from the first lane).
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    return (const void *)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b));
+}
+
 // 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
 // Issued as inline assembly so that the compiler neither tracks the LDS write
 // nor inserts its own vmcnt waits; callers order it with wait_vmcnt and a

@@ -539,12 +539,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, EpiParams ep)
                 int gc = n0 + c, gk = k0 + kk;
                 float v = 0.0f;
                 if (gk < g.K) {
+                    // (selects rather than indexes into the argument arrays)
                     if (EPI == EPI_SWIGLU) {
-                        if (gc < g.w_cols[s]) v = ((const float *)g.w[s])[(int64_t)gk * g.w_cols[s] + gc];
+                        const int ldw = s ? g.w_cols[1] : g.w_cols[0];
+                        if (gc < ldw) v = ((const float *)(s ? g.w[1] : g.w[0]))[(int64_t)gk * ldw + gc];
                     } else {
                         int src = 0, cc = gc;
-                        while (src < 2 && g.w[src + 1] && cc >= g.w_cols[src]) { cc -= g.w_cols[src]; ++src; }
-                        if (cc < g.w_cols[src]) v = ((const float *)g.w[src])[(int64_t)gk * g.w_cols[src] + cc];
+                        if (g.w[1] && cc >= g.w_cols[0]) {
+                            cc -= g.w_cols[0];
+                            src = 1;
+                            if (g.w[2] && cc >= g.w_cols[1]) {
+                                cc -= g.w_cols[1];
+                                src = 2;
+                            }
+                        }
+                        const int ldw = src == 0 ? g.w_cols[0] : (src == 1 ? g.w_cols[1] : g.w_cols[2]);
+                        const float *wm = (const float *)(src == 0 ? g.w[0] : (src == 1 ? g.w[1] : g.w[2]));
+                        if (cc < ldw) v = wm[(int64_t)gk * ldw + cc];
                     }
                 }
                 Bs[s][kk][c] = v;

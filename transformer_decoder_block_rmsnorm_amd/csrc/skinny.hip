@@ -56,16 +56,31 @@ constexpr int kSkinnyXcMaxK = 512;
 // so one wave's two 16-column tiles hold the gate and the up value of the same
 // outputs.  Every matrix width is a multiple of 64, so an 8-column chunk never
 // straddles two matrices or groups.
+// The matrix is chosen among wave-uniform copies of the argument arrays
+// (readfirstlane): indexing the arrays with a per-lane value, or selecting
+// between their elements, makes the compiler load them per lane from the
+// argument memory and wait for those loads before the first weight DMA.
 __device__ __forceinline__ const bf16_t *b_column(const SkinnyArgs &a, int c, int &ld) {
+    const int wc0 = uniform_i32(a.w_cols[0]), wc1 = uniform_i32(a.w_cols[1]), wc2 = uniform_i32(a.w_cols[2]);
+    const bf16_t *w0 = (const bf16_t *)uniform_ptr(a.w[0]), *w1 = (const bf16_t *)uniform_ptr(a.w[1]),
+                 *w2 = (const bf16_t *)uniform_ptr(a.w[2]);
     int s = 0;
     if (a.src == 2) {
         s = (c >> 4) & 1;
         c = 16 * (c >> 5) + (c & 15);
     } else if (a.src != 0) {
-        while (s < 2 && a.w[s + 1] && c >= a.w_cols[s]) { c -= a.w_cols[s]; ++s; }
+        if (w1 && c >= wc0) {
+            c -= wc0;
+            s = 1;
+            if (w2 && c >= wc1) {
+                c -= wc1;
+                s = 2;
+            }
+        }
     }
-    ld = a.w_cols[s];
-    return a.w[s] + min(c, ld - 8);
+    ld = s == 0 ? wc0 : (s == 1 ? wc1 : wc2);
+    const bf16_t *base = s == 0 ? w0 : (s == 1 ? w1 : w2);
+    return base + min(c, ld - 8);
 }
 
 // 32-byte granule swizzle of a weight row in LDS: the four rows one 16-lane
