@@ -122,10 +122,12 @@ def block_inputs(cfg, B, T):
     return w32, w, x32, _dev_tensor(x32, xb)
 
 
-def time_prefill(cfg, steps, warmup):
+def time_prefill(cfg, steps, warmup, fold=0):
+    """fold: the config's fold_norms (RMSNorm2 folded into the Wo and gate-up
+    GEMMs); the folded leg is timed without the per-stage pass."""
     import torch
     import transformer_decoder_block_rmsnorm_amd as tfb
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     B, T = cfg.B, cfg.T
     w32, w, x32, x = block_inputs(cfg, B, T)
     rope = tfb.rope_table_init(tc, cfg.t_max)
@@ -153,6 +155,9 @@ def time_prefill(cfg, steps, warmup):
     tfb.profile_enable(False)
     ms = e0.elapsed_time(e1) / steps
     dominant = tfb.profile_read()
+    if fold:
+        flops = prefill_flops(B, T, cfg.d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff)
+        return dict(ms=ms, flops=flops, dominant=dominant)
     # the same K steps with every launch bracketed: per-stage breakdown (the
     # event pairs add gaps between launches, so this pass is not the headline)
     tfb.profile_stages(None)
@@ -247,11 +252,13 @@ def time_model(cfg, decode_steps, reps):
     """The 32-layer model: prefill of the prompts (logits of the last rows,
     greedy next token), then decode_steps greedy steps with the growing cache.
     Weights are drawn N(0, 0.02) on the GPU (torch generator, seeded); the
-    gains are 1."""
+    gains are 1.  The prefill is also timed with fold_norms (the RMSNorms
+    that follow a GEMM folded into the GEMMs around them)."""
     import torch
     import transformer_decoder_block_rmsnorm_amd as tfb
     from synth.inputs import weight_shapes
     tc = tfb.Config.of(cfg)
+    tc_fold = tfb.Config.of(cfg, 1)
     B, T, L, V, d = cfg.B, cfg.T, cfg.n_layers, cfg.vocab, cfg.d
     dh = d // cfg.n_heads
     g = torch.Generator(device="cuda")
@@ -267,6 +274,7 @@ def time_model(cfg, decode_steps, reps):
     embed, w_un = randn((V, d)), randn((d, V))
     g_final = torch.ones(d, dtype=torch.bfloat16, device="cuda")
     h = tfb.ModelHandle(tc, layers, embed, g_final, w_un)
+    h_fold = tfb.ModelHandle(tc_fold, layers, embed, g_final, w_un)
     caches = [(torch.zeros((B, cfg.n_kv_heads, cfg.t_max, dh), dtype=torch.bfloat16, device="cuda"),
                torch.zeros((B, cfg.n_kv_heads, cfg.t_max, dh), dtype=torch.bfloat16, device="cuda"))
               for _ in range(L)]
@@ -275,13 +283,15 @@ def time_model(cfg, decode_steps, reps):
     lens = torch.zeros(B, dtype=torch.int32, device="cuda")
     nxt = torch.empty((B, 1), dtype=torch.int32, device="cuda")
     ws_pre = tfb.workspace(tc, B, T, V)
+    ws_pre_fold = tfb.workspace(tc_fold, B, T, V)
     ws_dec = tfb.workspace(tc, B, 1, V)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def prefill():
+    def prefill(folded=False):
         lens.zero_()
-        tfb.model_forward(h, rope, ids, caches, lens, 0, last_only=True, next_ids=nxt.view(B), ws=ws_pre)
+        tfb.model_forward(h_fold if folded else h, rope, ids, caches, lens, 0, last_only=True, next_ids=nxt.view(B),
+                          ws=ws_pre_fold if folded else ws_pre)
 
     def decode():
         for s in range(decode_steps):
@@ -294,8 +304,15 @@ def time_model(cfg, decode_steps, reps):
         torch.cuda.synchronize()
         if time.time() - t0 >= MIN_WARM_SECONDS:
             break
-    pre_ms, dec_ms = [], []
+    pre_ms, dec_ms, fold_ms = [], [], []
     for _ in range(reps):
+        flush.fill_(1)
+        torch.cuda.synchronize()
+        e0.record()
+        prefill(True)
+        e1.record()
+        torch.cuda.synchronize()
+        fold_ms.append(e0.elapsed_time(e1))
         flush.fill_(1)
         torch.cuda.synchronize()
         e0.record()
@@ -317,6 +334,8 @@ def time_model(cfg, decode_steps, reps):
                         "token ids uniform in [0, V), then %d greedy decode steps" % decode_steps,
             "prefill_ms": round(pre, 3), "prefill_tflops": round(flops / (pre * 1e-3) / 1e12, 2),
             "prefill_mfma_frac": round(flops / (pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "prefill_folded_norms_ms": round(min(fold_ms), 3),
+            "prefill_folded_norms_tflops": round(flops / (min(fold_ms) * 1e-3) / 1e12, 2),
             "decode_ms_per_step": round(step_ms, 4), "decode_tok_per_s": round(B / (step_ms * 1e-3), 1),
             "decode_hbm_frac": round((wbytes + kv / decode_steps) / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "decode_bytes_per_step": int(wbytes + kv / decode_steps), "reps": reps,
@@ -460,12 +479,23 @@ def main():
         "prefill_stage_ms": long_summary["stage_ms"],
         "attention_tflops": long_summary["attention_tflops"],
     }
+    def folded(cfg):
+        """The same block step with fold_norms: RMSNorm2 folded into the Wo
+        epilogue and the gate-up GEMM (not the headline: it moves where the
+        GEMM operand is rounded to bf16)."""
+        f = time_prefill(cfg, args.steps, args.warmup, fold=1)
+        gms, gcalls = f["dominant"]["gateup_gemm"]
+        return {"ms_per_step": round(f["ms"], 4), "tflops": round(f["flops"] / (f["ms"] * 1e-3) / 1e12, 2),
+                "gateup_launch_ms": round(gms / gcalls, 4)}
+
+    result["prefill_folded_norms"] = {"long_context": folded(C3)}
     if not args.no_7b:
         pre7 = time_prefill(C2, args.steps, args.warmup)
         _, roof7, sum7 = prefill_summary(C2, pre7, "Llama-2-7B-shaped block prefill: d=4096 H=Hkv=32 dh=128 "
                                                    "f=11008 B=1 T=2048, KV cache written")
         sum7["gateup_roofline"] = roof7
         result["prefill_7b"] = sum7
+        result["prefill_folded_norms"]["7b"] = folded(C2)
     if not args.no_decode:
         dec = time_decode(C4, args.steps, args.warmup)
         ams, acalls = dec["dominant"]["attention"]

@@ -61,6 +61,14 @@ def test_workspace_bytes():
         else:
             assert tfb.workspace_bytes(cc, 1, 1) == 0
     assert tfb.workspace_bytes(c, 0, 1) == 0 and tfb.workspace_bytes(c, 1, 0) == 0
+    # fold_norms adds room for the row sums of squares (at most 32 per row)
+    # only where it folds: bf16 calls of more than 64 rows
+    f = _cfg(fold_norms=1)
+    assert tfb.workspace_bytes(f, 2, 256) >= n2 + 2 * 256 * 32 * 4
+    assert tfb.workspace_bytes(f, 64, 1) == tfb.workspace_bytes(c, 64, 1)
+    f32, f32f = _cfg(d=64, n_heads=4, n_kv_heads=2, d_ff=192, dtype="f32"), _cfg(
+        d=64, n_heads=4, n_kv_heads=2, d_ff=192, dtype="f32", fold_norms=1)
+    assert tfb.workspace_bytes(f32f, 2, 256) == tfb.workspace_bytes(f32, 2, 256)
 
 
 def _weights(addr=FAKE):
