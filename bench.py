@@ -203,21 +203,30 @@ def time_decode(cfg, steps, warmup):
         tfb.block_decode(tc, w, rope, x, out, (kc, vc), pos, int(lens.max()), ws=ws)
 
     warm_up(step, warmup)
-    tfb.profile_read()
-    tfb.profile_stages(["attention", "attention_combine"])
+    # timed steps, nothing bracketed inside them (an event pair around a
+    # short kernel adds several microseconds to a 0.26 ms step)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     total = 0.0
     for _ in range(steps):
         flush.fill_(1)  # evict the caches between steps; not timed
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        tfb.profile_enable(True)
         e0.record()
         step()
         e1.record()
         torch.cuda.synchronize()
-        tfb.profile_enable(False)
         total += e0.elapsed_time(e1)
     ms = total / steps
+    # the same steps with the attention kernel and its merge bracketed by
+    # HIP events on their launch stream (the roofline entry)
+    tfb.profile_read()
+    tfb.profile_stages(["attention", "attention_combine"])
+    for _ in range(steps):
+        flush.fill_(1)
+        torch.cuda.synchronize()
+        tfb.profile_enable(True)
+        step()
+        torch.cuda.synchronize()
+        tfb.profile_enable(False)
     dominant = tfb.profile_read()
     tfb.profile_stages(None)
     tfb.profile_enable(True)
@@ -248,12 +257,12 @@ def decode_gemm_rates(cfg, stages):
     return out
 
 
-def time_model(cfg, decode_steps, reps):
+def time_model(cfg, decode_steps, reps, fold=True):
     """The 32-layer model: prefill of the prompts (logits of the last rows,
     greedy next token), then decode_steps greedy steps with the growing cache.
     Weights are drawn N(0, 0.02) on the GPU (torch generator, seeded); the
-    gains are 1.  The prefill is also timed with fold_norms (the RMSNorms
-    that follow a GEMM folded into the GEMMs around them)."""
+    gains are 1.  With fold, the prefill is also timed with fold_norms (the
+    RMSNorms that follow a GEMM folded into the GEMMs around them)."""
     import torch
     import transformer_decoder_block_rmsnorm_amd as tfb
     from synth.inputs import weight_shapes
@@ -306,13 +315,14 @@ def time_model(cfg, decode_steps, reps):
             break
     pre_ms, dec_ms, fold_ms = [], [], []
     for _ in range(reps):
-        flush.fill_(1)
-        torch.cuda.synchronize()
-        e0.record()
-        prefill(True)
-        e1.record()
-        torch.cuda.synchronize()
-        fold_ms.append(e0.elapsed_time(e1))
+        if fold:
+            flush.fill_(1)
+            torch.cuda.synchronize()
+            e0.record()
+            prefill(True)
+            e1.record()
+            torch.cuda.synchronize()
+            fold_ms.append(e0.elapsed_time(e1))
         flush.fill_(1)
         torch.cuda.synchronize()
         e0.record()
@@ -330,12 +340,15 @@ def time_model(cfg, decode_steps, reps):
     wbytes = 2 * (L * block_matrix_params(d, cfg.n_heads, cfg.n_kv_heads, cfg.d_ff) + d * V)
     kv = sum(L * decode_attention_bytes([T + s] * B, cfg.n_kv_heads, dh) for s in range(decode_steps))
     step_ms = dec / decode_steps
+    folded = {}
+    if fold:
+        folded = {"prefill_folded_norms_ms": round(min(fold_ms), 3),
+                  "prefill_folded_norms_tflops": round(flops / (min(fold_ms) * 1e-3) / 1e12, 2)}
     return {"workload": "32-layer GQA model: d=4096 H=32 Hkv=8 f=14336 V=32000 untied, B=4, prompt T=1024 "
                         "token ids uniform in [0, V), then %d greedy decode steps" % decode_steps,
             "prefill_ms": round(pre, 3), "prefill_tflops": round(flops / (pre * 1e-3) / 1e12, 2),
             "prefill_mfma_frac": round(flops / (pre * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "prefill_folded_norms_ms": round(min(fold_ms), 3),
-            "prefill_folded_norms_tflops": round(flops / (min(fold_ms) * 1e-3) / 1e12, 2),
+            **folded,
             "decode_ms_per_step": round(step_ms, 4), "decode_tok_per_s": round(B / (step_ms * 1e-3), 1),
             "decode_hbm_frac": round((wbytes + kv / decode_steps) / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "decode_bytes_per_step": int(wbytes + kv / decode_steps), "reps": reps,
@@ -410,6 +423,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the GQA decode step (for counter runs); prints the decode fields alone")
     ap.add_argument("--no-model", action="store_true")
+    ap.add_argument("--no-fold", action="store_true", help="skip the folded-norm legs (profiling runs)")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--min-warm", type=float, default=1.0,
@@ -488,14 +502,16 @@ def main():
         return {"ms_per_step": round(f["ms"], 4), "tflops": round(f["flops"] / (f["ms"] * 1e-3) / 1e12, 2),
                 "gateup_launch_ms": round(gms / gcalls, 4)}
 
-    result["prefill_folded_norms"] = {"long_context": folded(C3)}
+    if not args.no_fold:
+        result["prefill_folded_norms"] = {"long_context": folded(C3)}
     if not args.no_7b:
         pre7 = time_prefill(C2, args.steps, args.warmup)
         _, roof7, sum7 = prefill_summary(C2, pre7, "Llama-2-7B-shaped block prefill: d=4096 H=Hkv=32 dh=128 "
                                                    "f=11008 B=1 T=2048, KV cache written")
         sum7["gateup_roofline"] = roof7
         result["prefill_7b"] = sum7
-        result["prefill_folded_norms"]["7b"] = folded(C2)
+        if not args.no_fold:
+            result["prefill_folded_norms"]["7b"] = folded(C2)
     if not args.no_decode:
         dec = time_decode(C4, args.steps, args.warmup)
         ams, acalls = dec["dominant"]["attention"]
@@ -521,7 +537,7 @@ def main():
             "gemm_hbm": decode_gemm_rates(C4, dec["stages"]),
         }
     if not args.no_model:
-        result["model"] = time_model(C5, C5.decode_steps, max(1, args.model_reps))
+        result["model"] = time_model(C5, C5.decode_steps, max(1, args.model_reps), fold=not args.no_fold)
         result["tiny"] = time_tiny(C1, 21)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(C3, pre["w32"], pre["x32"], args.cpu_rows)

@@ -438,14 +438,16 @@ def test_decode_batch_sizes(oracle, B, d, H, Hkv, f):
                 cache_rows(inter["v_pre"], Hkv)[:, :, 0])
 
 
-@pytest.mark.parametrize("dtype,chunks", [("f32", [5, 7, 4]), ("bf16", [100, 37, 129, 1]), ("bf16", [64, 64, 64])])
-def test_chunked_prefill_matches_full_prefill(oracle, dtype, chunks):
+@pytest.mark.parametrize("dtype,chunks,fold", [("f32", [5, 7, 4], 0), ("bf16", [100, 37, 129, 1], 0),
+                                              ("bf16", [64, 64, 64], 0), ("bf16", [100, 37, 129, 1], 1)])
+def test_chunked_prefill_matches_full_prefill(oracle, dtype, chunks, fold):
     """Prefill in chunks at start positions 0, c0, c0+c1, ... into one cache
-    (the causal diagonal shifts by the start position)."""
+    (the causal diagonal shifts by the start position); fold: the config's
+    fold_norms (chunks of more than 64 rows fold RMSNorm2)."""
     torch = _torch()
     d, f = (64, 192) if dtype == "f32" else (512, 1024)
     cfg = small_cfg(d=d, H=4, Hkv=2, f=f, dtype=dtype, number=97)
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     w32, w = dev_weights(cfg)
     T = sum(chunks)
     x32, x = dev_x(cfg, 2, T)
@@ -453,7 +455,7 @@ def test_chunked_prefill_matches_full_prefill(oracle, dtype, chunks):
     rope = tfb.rope_table_init(tc, t_max)
     kc, vc = new_cache(cfg, 2, t_max)
     outs, s0 = [], 0
-    print("case: chunked prefill", dtype, chunks, flush=True)
+    print("case: chunked prefill", dtype, chunks, "fold_norms=%d" % fold, flush=True)
     for c in chunks:
         o = torch.empty((2, c, cfg.d), dtype=x.dtype, device="cuda")
         tfb.block_prefill(tc, w, rope, x[:, s0:s0 + c].contiguous(), o, start_pos=s0, cache=(kc, vc))
@@ -625,15 +627,17 @@ def test_varlen_prefill_matches_per_sequence(oracle, dtype, d, H, Hkv, W, fold):
 
 # ---- paged KV cache (tirogla "Transformer block", Implementation notes: a
 # cache allocated in fixed-size blocks per sequence)
-@pytest.mark.parametrize("dtype,bs,W", [("bf16", 16, 0), ("bf16", 64, 0), ("bf16", 256, 40), ("f32", 8, 0)])
-def test_paged_cache_matches_contiguous_bitwise(oracle, dtype, bs, W):
+@pytest.mark.parametrize("dtype,bs,W,fold", [("bf16", 16, 0, 0), ("bf16", 64, 0, 0), ("bf16", 256, 40, 0),
+                                              ("f32", 8, 0, 0), ("bf16", 64, 0, 1)])
+def test_paged_cache_matches_contiguous_bitwise(oracle, dtype, bs, W, fold):
     """Prefill in two chunks, then decode steps, through a block table that
     scatters each sequence over a shuffled pool: outputs and cached rows must
-    equal the contiguous cache's bit for bit (only the addressing differs)."""
+    equal the contiguous cache's bit for bit (only the addressing differs;
+    fold: both with the config's fold_norms)."""
     torch = _torch()
     d, H, Hkv = (64, 4, 2) if dtype == "f32" else (256, 4, 2)
     cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=2 * d, dtype=dtype, number=130, window=W)
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     w32, w = dev_weights(cfg)
     B, T1, T2, steps = 2, 100, 50, 3
     T = T1 + T2 + steps
@@ -649,7 +653,7 @@ def test_paged_cache_matches_contiguous_bitwise(oracle, dtype, bs, W):
     vp = kp.clone()
     kc, vc = new_cache(cfg, B, t_max)
     rope = tfb.rope_table_init(tc, t_max)
-    print("case: paged", dtype, bs, W, flush=True)
+    print("case: paged", dtype, bs, W, "fold_norms=%d" % fold, flush=True)
     outs_c, outs_p = [], []
     for s0, n in ((0, T1), (T1, T2)):
         xi = x[:, s0:s0 + n].contiguous()
