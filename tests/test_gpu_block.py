@@ -106,6 +106,9 @@ def test_bf16_block_prefill_then_decode(oracle, shape):
     dict(d=512, H=4, Hkv=2, f=1024, B=2, T0=300, steps=2),    # 128x128 tiles, ragged last row tile
     dict(d=768, H=6, Hkv=2, f=2048, B=1, T0=2048, steps=1),   # gate-up on 256x128 tiles (W1|W3 pairs)
     dict(d=1024, H=8, Hkv=2, f=4096, B=1, T0=4096, steps=1),  # gate-up on 256x256 tiles
+    # d = 320 is not a multiple of the 128-column tiles: the last column
+    # tile of Wo (and of the gate-up's K range) ends past the row
+    dict(d=320, H=5, Hkv=1, f=640, B=1, T0=300, steps=1),
 ])
 def test_bf16_folded_norms_prefill_then_decode(oracle, shape):
     """fold_norms: RMSNorm2 folded into the Wo epilogue and the gate-up GEMM

@@ -42,6 +42,8 @@ def model_inputs(cfg, L, V):
     # RMSNorms folded into the GEMMs around them (prefill: 80 and 210 rows)
     ("bf16", 512, 4, 2, 1024, 2, 1024, 2, 40, 3, 1),
     ("bf16", 256, 2, 1, 512, 3, 512, 3, 70, 2, 1),
+    # widths that end inside a column tile (W2 folds the next RMSNorm1 there)
+    ("bf16", 320, 5, 1, 640, 2, 512, 2, 50, 2, 1),
 ])
 def test_model_prefill_then_greedy_decode(oracle, dtype, d, H, Hkv, f, L, V, B, T, steps, fold):
     import torch

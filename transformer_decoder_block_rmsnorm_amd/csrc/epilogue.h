@@ -58,11 +58,12 @@ __device__ __forceinline__ float as_stored(const EpiParams &p, float y) {
 
 // The folded norm's part of one 8-column group of row m: nu = bf16(y * g)
 // (gains g of the group's columns, already widened) and the group's sum of
-// y^2, returned.  Groups are whole inside the output here (the launcher
-// folds the norm only when every group is).
+// y^2, returned.  A group lies wholly inside the row or wholly past its end
+// (N is a multiple of 8, checked by the launcher); rows past M and groups
+// past N contribute nothing and write nothing.
 __device__ __forceinline__ float epi_norm8(const EpiParams &p, int m, int c, const float (&y)[8],
                                            const float (&g)[8]) {
-    if (m >= p.M) return 0.0f;
+    if (m >= p.M || c >= p.N) return 0.0f;
     float u[8], ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {

@@ -400,9 +400,9 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     const bool fold = NORM == NORM_FOLD && split < 0;
     static_assert((NW * 32 * SW + WN * BM) * 4 <= NST * STAGE * 2, "row sums fit past the staging area");
     float *ssl = (float *)lds + NW * 32 * SW;  // [WN][BM]
-    float gn[8];
+    float gn[8] = {};
     if constexpr (NORM == NORM_FOLD)
-        if (fold) load_bf16x8(ep.ng + c0 + 8 * (lane % SEGS), gn);
+        if (fold && c0 + 8 * (lane % SEGS) < ep.N) load_bf16x8(ep.ng + c0 + 8 * (lane % SEGS), gn);  // in the row
     auto fold_group = [&](int row_local, int m, int c, const float (&y)[8]) {
         float ss = epi_norm8(ep, m, c, y, gn);
 #pragma unroll
@@ -642,9 +642,9 @@ __global__ __launch_bounds__(256) void gemm_split_fixup_kernel(GemmArgs g, EpiPa
                 // folded norm: the BN / 8 threads of a row are consecutive
                 // lanes; their sums of y^2 are added by a fixed butterfly
                 const int c = tn * BN + col;
-                float y8[8], gn[8];
+                float y8[8], gn[8] = {};
                 epi_store8<EPI>(ep, m, c, v8, y8);
-                load_bf16x8(ep.ng + c, gn);
+                if (c < ep.N) load_bf16x8(ep.ng + c, gn);  // a group past the row's end reads no gains
                 float ss = epi_norm8(ep, m, c, y8, gn);
 #pragma unroll
                 for (int o = BN / 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
