@@ -57,7 +57,6 @@ struct GemmArgs {
     float rss_eps;
 };
 
-
 // Workgroups are dealt to the 8 XCDs round robin.  xcd_remap gives each XCD a
 // contiguous run of n consecutive logical indices (n a multiple of 8), so the
 // tiles resident on one XCD share A and B panels in that XCD's L2.
@@ -260,12 +259,6 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     };
     auto slot = [&](int kt) { return (const bf16_t *)(lds + (kt % NST) * STAGE); };
 
-    // Software pipeline at half-stage granularity: the LDS reads of the next
-    // k half are in flight while the MFMAs of the current one run, so LDS and
-    // matrix cores work at the same time instead of in turn after each
-    // barrier.  Stage s lives in ring slot s % NST; all NST slots are filled
-    // ahead, and a slot is refilled right after the barrier that follows the
-    // last read of its stage.
     // Folded norm: the partial sums of the tile's rows are one contiguous
     // block of BM * rss_n floats; thread t loads half of row t / 2 (the
     // halves of a row sit in adjacent lanes), with 16-byte loads when the
@@ -280,8 +273,8 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
     const int rs_row = tid >> 1, rs_half = tid & 1;
     f32x4 rsv[RS_MAX / 4];
     int rs_cnt = 0;
-    asm volatile("" ::: "memory");
     if constexpr (NORM == NORM_SCALE) {
+        asm volatile("" ::: "memory");
         const int per = (g.rss_n + 1) / 2, j0 = rs_half * per;
         rs_cnt = min(per, g.rss_n - j0);
         const float *row = g.rss + (int64_t)min(m0 + rs_row, g.M - 1) * g.rss_n;
@@ -296,6 +289,12 @@ __global__ __launch_bounds__(WM *WN * 64) void gemm_bf16_dma_kernel(GemmArgs g, 
                 for (int k = 0; k < 4; ++k) rsv[q][k] = row[min(j0 + 4 * q + k, g.rss_n - 1)];
         }
     }
+    // Software pipeline at half-stage granularity: the LDS reads of the next
+    // k half are in flight while the MFMAs of the current one run, so LDS and
+    // matrix cores work at the same time instead of in turn after each
+    // barrier.  Stage s lives in ring slot s % NST; all NST slots are filled
+    // ahead, and a slot is refilled right after the barrier that follows the
+    // last read of its stage.
 #pragma unroll
     for (int st = 0; st < NST; ++st)
         if (st < KT) issue(st, st);
