@@ -402,6 +402,8 @@ def test_decode_long_cache_chunks(oracle, lens, d, H, Hkv):
     (64, 1024, 8, 8, 2048),    # the full 64 rows, 128-column weight blocks split along k
     (80, 512, 4, 2, 1024),     # more rows than a weight stream takes: the tiled GEMMs, one ragged 128-row tile
     (130, 256, 2, 1, 512),     # two row tiles, the second holding 2 rows; dh = 128, MQA
+    (24, 2048, 16, 2, 1024),   # 8 query heads per KV head at dh = 128
+    (100, 2048, 16, 2, 1024),  # the same heads through the tiled GEMMs, with fold_norms
 ])
 def test_decode_batch_sizes(oracle, B, d, H, Hkv, f):
     """Decode of B sequences at spread positions: up to 64 rows the
@@ -412,7 +414,7 @@ def test_decode_batch_sizes(oracle, B, d, H, Hkv, f):
     import synth
     from tests.gpu_util import to_dev
     cfg = small_cfg(d=d, H=H, Hkv=Hkv, f=f, dtype="bf16", base=500000.0, number=93)
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, 1 if B == 100 else 0)
     dh = d // H
     lens = [int(v) for v in synth.integers(cfg.seed, 13, (B,), 1, 200)]
     t_max = max(lens) + 4
