@@ -723,14 +723,15 @@ static hipError_t launch_dma(GemmArgs g, EpiParams ep, void *part, size_t part_b
 //             moves 1.5x the operand bytes per flop;
 //  T_128:     128x128 on 4 waves, when fewer than half the compute units
 //             would get a 256x256 tile.
-// Between the first two: with K <= 4096, 256x128 whenever 256x256 tiles leave
-// a partial last round and 256x128 tiles fill whole rounds (measured on
-// MI355X: the 7B Wo 81 vs 94 us, the fused QKV 221 vs 228 us; the split
-// tail's fix-up pass is costly behind a heavy epilogue).  Longer K: a cost
-// model in units of one 256x256 k step, with constants measured on the 7B
-// block (K = 11008): a 256x128 k step costs 0.63 units plus 7 units of
+// Between the first two, when 256x256 tiles leave a partial last round: a
+// cost model in units of one 256x256 k step, with constants measured on the
+// 7B block (K = 11008): a 256x128 k step costs 0.63 units plus 7 units of
 // epilogue per round, and the split tail costs 0.77 units per MB of fp32
-// partials written and re-read.
+// partials written and re-read.  (It picks 256x128 for the 7B Wo, one round
+// of 256x128 tiles, and a split tail for the 7B and the 32-layer model's
+// fused QKV; measured on MI355X in one process, the 7B block step took 0.919
+// ms that way against 0.944 ms with the QKV on three rounds of 256x128
+// tiles, and the model's QKV 215 against 231 us.)
 enum TilePlan { T_256 = 0, T_256x128 = 1, T_128 = 2 };
 static TilePlan plan_tiles(int M, int N_virtual, int K) {
     const int cus = device_cus();
@@ -738,7 +739,6 @@ static TilePlan plan_tiles(int M, int N_virtual, int K) {
     const int t256 = tm * ((N_virtual + 255) / 256), t128 = tm * ((N_virtual + 127) / 128);
     if (t256 * 2 < cus) return T_128;
     if (t256 % cus == 0) return T_256;
-    if (K <= 4096 && t128 % cus == 0) return T_256x128;
     const SplitPlan sp = plan_split(t256, kt, cus, 256 * 256);
     double c256 = (double)(t256 / cus) * kt;
     if (sp.splits > 1) c256 += (double)kt / sp.splits + 0.77 * sp.part_bytes / (1 << 20);
