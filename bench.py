@@ -283,7 +283,7 @@ def time_model(cfg, decode_steps, reps, fold=True):
     embed, w_un = randn((V, d)), randn((d, V))
     g_final = torch.ones(d, dtype=torch.bfloat16, device="cuda")
     h = tfb.ModelHandle(tc, layers, embed, g_final, w_un)
-    h_fold = tfb.ModelHandle(tc_fold, layers, embed, g_final, w_un)
+    h_fold = tfb.ModelHandle(tc_fold, layers, embed, g_final, w_un) if fold else None
     caches = [(torch.zeros((B, cfg.n_kv_heads, cfg.t_max, dh), dtype=torch.bfloat16, device="cuda"),
                torch.zeros((B, cfg.n_kv_heads, cfg.t_max, dh), dtype=torch.bfloat16, device="cuda"))
               for _ in range(L)]
@@ -292,7 +292,7 @@ def time_model(cfg, decode_steps, reps, fold=True):
     lens = torch.zeros(B, dtype=torch.int32, device="cuda")
     nxt = torch.empty((B, 1), dtype=torch.int32, device="cuda")
     ws_pre = tfb.workspace(tc, B, T, V)
-    ws_pre_fold = tfb.workspace(tc_fold, B, T, V)
+    ws_pre_fold = tfb.workspace(tc_fold, B, T, V) if fold else None
     ws_dec = tfb.workspace(tc, B, 1, V)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
