@@ -785,9 +785,12 @@ def test_paged_ring_window_cache_matches_uncapped_bitwise(bs):
     assert np.isnan(widen_cache(kp)[free]).all()
 
 
-def test_model_with_ring_window_caches_matches_uncapped_bitwise():
+@pytest.mark.parametrize("fold", [0, 1])
+def test_model_with_ring_window_caches_matches_uncapped_bitwise(fold):
     """The model (prefill, then greedy decode far past the window) on bounded
-    window caches of W rows gives the logits and tokens of uncapped caches."""
+    window caches of W rows gives the logits and tokens of uncapped caches
+    (fold: both with fold_norms; the 100-row prefill folds its norms and
+    works in the ring's staging copy)."""
     import torch
     import synth
     from synth.configs import tensor_id
@@ -795,11 +798,11 @@ def test_model_with_ring_window_caches_matches_uncapped_bitwise():
     cfg = small_cfg(d=512, H=4, Hkv=2, f=1024, dtype="bf16", number=152, window=32)
     L, V, B, T, steps = 2, 1024, 2, 50, 80
     _, (ld, ed, gd, ud) = model_inputs(cfg, L, V)
-    tc = tfb.Config.of(cfg)
+    tc = tfb.Config.of(cfg, fold)
     h = tfb.ModelHandle(tc, ld, ed, gd, ud)
     rope = tfb.rope_table_init(tc, T + steps)
     ids = torch.from_numpy(synth.integers(cfg.seed, tensor_id("ids"), (B, T), 0, V - 1)).cuda()
-    print("case: model ring caches", flush=True)
+    print("case: model ring caches, fold_norms=%d" % fold, flush=True)
     res = []
     for ring, rows in ((True, 32), (False, T + steps)):
         caches = [(torch.full((B, 2, rows, 128), float("nan"), dtype=torch.bfloat16, device="cuda"),
