@@ -409,7 +409,14 @@ __global__ __launch_bounds__(NGRP * 256, 3 - NGRP) void flash_prefill_kernel(Fla
         }
         const bool cur = it >= w_lo && it < w_hi, nxt = it + 1 >= w_lo && it + 1 < w_hi;
         if (nxt) scores((s + 1) & 1, Sn);
+        // With two workgroups per CU, a wave in its softmax competes with
+        // waves issuing the next tile's products; a raised wave priority over
+        // the softmax (and the P.V products interleaved with it) took 1.7%
+        // off the long-context attention.  Around the score products instead
+        // it cost 4%; the single-workgroup layout (NGRP = 2) gained nothing.
+        if constexpr (NGRP == 1) __builtin_amdgcn_s_setprio(1);
         if (cur) softmax_tail(s & 1, Sc, softmax_head(it, Sc));
+        if constexpr (NGRP == 1) __builtin_amdgcn_s_setprio(0);
     };
     for (int s = 0; s < n_lo; s += 2) {
         step(s, S0, S1);
